@@ -1,0 +1,311 @@
+/*
+ * SLQ CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct reference for what the SLQ hot path
+ * computes.  Only the test suite, the smoke check and the bench's CPU-baseline
+ * leg may load this library; the product path never does.  It shares no
+ * source, header, table or helper with the HIP library.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp (IEEE fp32 on SSE,
+ * no contraction, round-to-nearest-even), see oracle/build.py.
+ *
+ * Sources (page title -> section):
+ *  [SLQ-gist]   "Statistically-Lossless Quantization of Large Language Models"
+ *               (gist.science technical summary): Methodology 1 (centering
+ *               inefficiency gamma = 2M/R, the gamma-squared variance law),
+ *               Methodology 2 (EAR as the summed min of the two next-token
+ *               distributions, averaged over positions), Methodology 3
+ *               (asymmetric integer group quantization, group size 128).
+ *  [SLQ-readme] "SLQ" code README: Pipeline paragraph (asymmetric INT, g128,
+ *               bit-widths 2..8), Usage 4 (weights packed to their per-layer
+ *               bit-widths on load), Evaluation (EAR and KL of a model against
+ *               its base).
+ *  [SLQ-blog-en] "SLQ: Bridging the Gap ..." : The Motivation (next-token
+ *               probability distribution), The Math of Asymmetry.
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function (readings R1..R12 in the design notes).
+ *
+ * Parity pins: every function here is pinned by tests/test_oracle_*.py
+ * against closed forms, brute force, worked values from the pages and
+ * invariants; none is "parity unpinned".
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#include "oracle.h"
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Round-to-nearest-even, then clamp to [0, maxq], all in fp32 (R4/R5). */
+static float clamp_code(float v, int maxq) {
+  if (v < 0.0f) return 0.0f;
+  if (v > (float)maxq) return (float)maxq;
+  return v;
+}
+
+/*
+ * Asymmetric integer group quantization ([SLQ-gist] Methodology 3;
+ * [SLQ-readme] Pipeline).  For each row n and each group g of `group`
+ * consecutive inputs k:
+ *   lo = min(0, min w), hi = max(0, max w)                (R1: 0 in range)
+ *   s  = fl32(fl32(hi - lo) / (2^b - 1))                  (R3: fp32 divide)
+ *   if s == 0 (all-zero group): s = 1, z = 0              (R2)
+ *   z  = clamp(rint(fl32(-lo / s)), 0, 2^b - 1)           (R4)
+ *   q  = clamp(rint(fl32(w / s)) + z, 0, 2^b - 1)         (R5)
+ * Symmetric grid (comparison only, [SLQ-gist] Methodology 1):
+ *   M = max |w|, s = fl32(2M / (2^b - 1)), z = 2^(b-1)    (R6)
+ */
+void oracle_quantize(const float *W, int64_t n, int64_t k, int bits, int group,
+                     int symmetric, uint8_t *q, float *scales, uint8_t *zeros) {
+  const int maxq = (1 << bits) - 1;
+  const int64_t G = k / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t g = 0; g < G; ++g) {
+      const float *w = W + r * k + g * group;
+      float s;
+      int z;
+      if (!symmetric) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int i = 0; i < group; ++i) {
+          if (w[i] < lo) lo = w[i];
+          if (w[i] > hi) hi = w[i];
+        }
+        float range = hi - lo;
+        s = range / (float)maxq;
+        if (s == 0.0f) {
+          s = 1.0f;
+          z = 0;
+        } else {
+          float zf = rintf((-lo) / s);
+          z = (int)clamp_code(zf, maxq);
+        }
+      } else {
+        float m = 0.0f;
+        for (int i = 0; i < group; ++i) {
+          float a = fabsf(w[i]);
+          if (a > m) m = a;
+        }
+        float two_m = 2.0f * m;
+        s = two_m / (float)maxq;
+        if (s == 0.0f) s = 1.0f;
+        z = 1 << (bits - 1);
+      }
+      scales[r * G + g] = s;
+      zeros[r * G + g] = (uint8_t)z;
+      for (int i = 0; i < group; ++i) {
+        float t = rintf(w[i] / s);
+        float v = clamp_code(t + (float)z, maxq);
+        q[r * k + g * group + i] = (uint8_t)(int)v;
+      }
+    }
+  }
+}
+
+/*
+ * Dense bit-packing ([SLQ-readme] Usage 4: weights packed to their per-layer
+ * bit-width).  R7: each row is one little-endian bitstream with no padding:
+ * code j of the row occupies bits [j*b, j*b + b) of the integer
+ * sum_i word_i * 2^(32 i).  A row of k codes fills k*b/32 words.
+ */
+void oracle_pack(const uint8_t *q, int64_t n, int64_t k, int bits, uint32_t *words) {
+  const int64_t wpr = k * bits / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    uint32_t *out = words + r * wpr;
+    for (int64_t i = 0; i < wpr; ++i) out[i] = 0u;
+    for (int64_t j = 0; j < k; ++j) {
+      uint32_t code = q[r * k + j];
+      for (int t = 0; t < bits; ++t) {
+        int64_t bit = j * bits + t;
+        if ((code >> t) & 1u) out[bit / 32] |= (1u << (bit % 32));
+      }
+    }
+  }
+}
+
+void oracle_unpack(const uint32_t *words, int64_t n, int64_t k, int bits, uint8_t *q) {
+  const int64_t wpr = k * bits / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    const uint32_t *in = words + r * wpr;
+    for (int64_t j = 0; j < k; ++j) {
+      uint32_t code = 0;
+      for (int t = 0; t < bits; ++t) {
+        int64_t bit = j * bits + t;
+        code |= ((in[bit / 32] >> (bit % 32)) & 1u) << t;
+      }
+      q[r * k + j] = (uint8_t)code;
+    }
+  }
+}
+
+/* Reconstruction w_hat = fl32((q - z) * s) of every element. */
+void oracle_dequantize(const uint8_t *q, const float *scales, const uint8_t *zeros,
+                       int64_t n, int64_t k, int group, float *w_hat) {
+  const int64_t G = k / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t j = 0; j < k; ++j) {
+      int64_t g = j / group;
+      float d = (float)((int)q[r * k + j] - (int)zeros[r * G + g]);
+      w_hat[r * k + j] = d * scales[r * G + g];
+    }
+  }
+}
+
+static double bf16_to_double(uint16_t h) {
+  uint32_t u = ((uint32_t)h) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/*
+ * Weight-only matmul y = x . W_hat^T ([SLQ-gist] Methodology 3 and Inference
+ * Speedup: weights quantized, activations kept in 16-bit).  x is bf16 [m][k],
+ * W_hat fp32 [n][k]; y and the error bound sum |x| |w_hat| are fp64 [m][n].
+ */
+void oracle_gemm(const uint16_t *x, int64_t m, int64_t k, const float *w_hat, int64_t n,
+                 double *y, double *bound) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t c = 0; c < n; ++c) {
+      double acc = 0.0, b = 0.0;
+      for (int64_t j = 0; j < k; ++j) {
+        double xv = bf16_to_double(x[i * k + j]);
+        double wv = (double)w_hat[c * k + j];
+        acc += xv * wv;
+        b += fabs(xv) * fabs(wv);
+      }
+      y[i * n + c] = acc;
+      bound[i * n + c] = b;
+    }
+  }
+}
+
+/* The same products for an explicit list of (row of x, row of W_hat) pairs. */
+void oracle_gemm_pairs(const uint16_t *x, int64_t k, const float *w_hat_rows,
+                       const int64_t *xi, const int64_t *wi, int64_t npairs,
+                       double *y, double *bound) {
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < npairs; ++p) {
+    const uint16_t *xr = x + xi[p] * k;
+    const float *wr = w_hat_rows + wi[p] * k;
+    double acc = 0.0, b = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      double xv = bf16_to_double(xr[j]);
+      double wv = (double)wr[j];
+      acc += xv * wv;
+      b += fabs(xv) * fabs(wv);
+    }
+    y[p] = acc;
+    bound[p] = b;
+  }
+}
+
+/*
+ * Log-normalizer of a row of logits ([SLQ-blog-en] The Motivation: the
+ * next-token distribution is the softmax of the logits, temperature 1):
+ *   A = max_v a_v + log sum_v exp(a_v - max), in fp64.
+ */
+static double row_lse(const float *a, int64_t vocab) {
+  double m = -INFINITY;
+  for (int64_t v = 0; v < vocab; ++v)
+    if ((double)a[v] > m) m = (double)a[v];
+  double z = 0.0;
+  for (int64_t v = 0; v < vocab; ++v) z += exp((double)a[v] - m);
+  return m + log(z);
+}
+
+void oracle_row_lse(const float *a, int64_t rows, int64_t vocab, double *lse) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) lse[r] = row_lse(a + r * vocab, vocab);
+}
+
+/*
+ * Fidelity of a quantized model's next-token distribution q against the
+ * reference p, per row (position):
+ *   EAR_r = sum_v min(p_v, q_v)  ([SLQ-gist] Methodology 2, full vocabulary
+ *                                 per the spec reading R9)
+ *   KL_r  = sum_v p_v (log p_v - log q_v), natural log, KL(p || q)  (R10)
+ * and their arithmetic means over rows (the 1/N average over positions).
+ * p = softmax(a) is the reference, q = softmax(b) the quantized model.
+ */
+void oracle_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab,
+                   double *ear, double *kl, double *means) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float *ar = a + r * vocab;
+    const float *br = b + r * vocab;
+    double A = row_lse(ar, vocab);
+    double B = row_lse(br, vocab);
+    double e = 0.0, d = 0.0;
+    for (int64_t v = 0; v < vocab; ++v) {
+      double lp = (double)ar[v] - A;
+      double lq = (double)br[v] - B;
+      double p = exp(lp);
+      double q = exp(lq);
+      e += (p < q) ? p : q;
+      d += p * (lp - lq);
+    }
+    ear[r] = e;
+    kl[r] = d;
+  }
+  double se = 0.0, sk = 0.0;
+  for (int64_t r = 0; r < rows; ++r) {
+    se += ear[r];
+    sk += kl[r];
+  }
+  means[0] = rows > 0 ? se / (double)rows : 0.0;
+  means[1] = rows > 0 ? sk / (double)rows : 0.0;
+}
+
+/*
+ * Quantization noise of one grid over a layer, for the gamma-squared law
+ * ([SLQ-gist] Methodology 1): out[0] = sum (w - w_hat)^2, out[1] = sum_g s_g^2,
+ * both fp64.  Rounding noise per element scales with s^2, so the ratio of
+ * out[1] between the symmetric and asymmetric grids is the predicted noise
+ * ratio (R11) and the ratio of out[0] is the measured one.
+ */
+void oracle_quant_error(const float *W, const float *w_hat, const float *scales,
+                        int64_t n, int64_t k, int group, double *out) {
+  const int64_t G = k / group;
+  double sse = 0.0, s2 = 0.0;
+#pragma omp parallel for schedule(static) reduction(+ : sse, s2)
+  for (int64_t r = 0; r < n; ++r) {
+    double rs = 0.0, rq = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      double e = (double)W[r * k + j] - (double)w_hat[r * k + j];
+      rs += e * e;
+    }
+    for (int64_t g = 0; g < G; ++g) {
+      double s = (double)scales[r * G + g];
+      rq += s * s;
+    }
+    sse += rs;
+    s2 += rq;
+  }
+  out[0] = sse;
+  out[1] = s2;
+}
+
+/*
+ * Storage cost in bits per parameter of a g-group format with `meta_bits` of
+ * scale + zero point per group ([SLQ-readme] Search: the bit-width map adds
+ * 0.156 bits per parameter at every width; Evaluation: Uniform-4 is 4.16 bpp).
+ */
+double oracle_bits_per_param(int bits, int meta_bits, int group) {
+  return (double)bits + (double)meta_bits / (double)group;
+}

@@ -1,0 +1,115 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each case plants one mistake into a copy of oracle/oracle.c (a dropped term,
+a wrong sign, a wrong index, a transposed operand, the wrong rounding or
+reduction), builds it into a temporary library, points the oracle module at
+it and runs every pin.  At least one pin must fail for every mutant; the real
+oracle must pass them all.
+"""
+import inspect
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import (test_oracle_fidelity, test_oracle_gamma, test_oracle_gemm,
+                   test_oracle_pack, test_oracle_quant)
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+HDR_DIR = os.path.dirname(SRC)
+
+MUTANTS = {
+    "code_drops_zero_point": ("float v = clamp_code(t + (float)z, maxq);", "float v = clamp_code(t, maxq);"),
+    "zero_point_sign": ("rintf((-lo) / s)", "rintf(lo / s)"),
+    "codes_floor_not_rint": ("float t = rintf(w[i] / s);", "float t = floorf(w[i] / s);"),
+    "codes_half_away_from_zero": ("float t = rintf(w[i] / s);", "float t = roundf(w[i] / s);"),
+    "range_excludes_zero": ("float lo = 0.0f, hi = 0.0f;", "float lo = w[0], hi = w[0];"),
+    "levels_off_by_one": ("s = range / (float)maxq;", "s = range / (float)(maxq + 1);"),
+    "symmetric_center": ("z = 1 << (bits - 1);", "z = (1 << (bits - 1)) - 1;"),
+    "pack_bit_order_in_code": ("int64_t bit = j * bits + t;\n        if ((code",
+                               "int64_t bit = j * bits + (bits - 1 - t);\n        if ((code"),
+    "pack_bit_order_in_word": ("out[bit / 32] |= (1u << (bit % 32));", "out[bit / 32] |= (1u << (31 - bit % 32));"),
+    "dequant_group_index": ("int64_t g = j / group;", "int64_t g = j % G;"),
+    "dequant_drops_zero": ("float d = (float)((int)q[r * k + j] - (int)zeros[r * G + g]);",
+                           "float d = (float)((int)q[r * k + j]);"),
+    "gemm_transposed_weight": ("double wv = (double)w_hat[c * k + j];", "double wv = (double)w_hat[j * n + c];"),
+    "gemm_bound_without_abs": ("b += fabs(xv) * fabs(wv);\n      }\n      y[i",
+                               "b += xv * wv;\n      }\n      y[i"),
+    "lse_drops_max": ("return m + log(z);", "return log(z);"),
+    "ear_max_not_min": ("e += (p < q) ? p : q;", "e += (p > q) ? p : q;"),
+    "kl_reversed": ("d += p * (lp - lq);", "d += q * (lq - lp);"),
+    "kl_wrong_normalizer_sign": ("double lq = (double)br[v] - B;", "double lq = (double)br[v] + B;"),
+    "mean_over_rows_minus_one": ("means[0] = rows > 0 ? se / (double)rows : 0.0;",
+                                 "means[0] = rows > 1 ? se / (double)(rows - 1) : 0.0;"),
+    "sse_not_squared": ("rs += e * e;", "rs += fabs(e);"),
+    "bpp_meta_per_group": ("(double)meta_bits / (double)group", "(double)meta_bits / (double)(2 * group)"),
+}
+
+
+def _pin_calls():
+    """Every pin with every parameter value, as zero-argument callables."""
+    calls = []
+    for mod in (test_oracle_quant, test_oracle_pack, test_oracle_gemm,
+                test_oracle_fidelity, test_oracle_gamma):
+        for name, fn in inspect.getmembers(mod, inspect.isfunction):
+            if not name.startswith("test_") or fn.__module__ != mod.__name__:
+                continue
+            params = inspect.signature(fn).parameters
+            grids = [{}]
+            for mark in getattr(fn, "pytestmark", []):
+                if mark.name == "parametrize":
+                    argname, values = mark.args[0], mark.args[1]
+                    grids = [dict(g, **{argname: v}) for g in grids for v in values]
+            for g in grids:
+                kwargs = dict(g)
+                if "orc" in params:
+                    kwargs["orc"] = oracle
+                calls.append((f"{mod.__name__}.{name}{g or ''}", fn, kwargs))
+    return calls
+
+
+def _failures(calls):
+    failed = []
+    for label, fn, kwargs in calls:
+        try:
+            fn(**kwargs)
+        except Exception:   # AssertionError or a crash-free numerical error
+            failed.append(label)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def calls():
+    return _pin_calls()
+
+
+def _build(src_text, tmp):
+    c = os.path.join(tmp, "oracle.c")
+    with open(c, "w") as f:
+        f.write(src_text)
+    so = os.path.join(tmp, "libmut.so")
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+                    "-fopenmp", "-I", HDR_DIR, "-shared", c, "-o", so, "-lm"], check=True)
+    return oracle.load(so)
+
+
+def test_real_oracle_passes_all_pins(calls):
+    assert len(calls) > 50
+    assert _failures(calls) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, calls):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor not unique: {name}"
+    with tempfile.TemporaryDirectory() as tmp:
+        L = _build(text.replace(old, new), tmp)
+        prev = oracle.use(L)
+        try:
+            failed = _failures(calls)
+        finally:
+            oracle.use(prev)
+    assert failed, f"no pin catches mutant {name}"
