@@ -1,0 +1,185 @@
+/*
+ * slq.h -- C ABI of libslq.so, the MI355X (gfx950) hot path of SLQ
+ * (Statistically-Lossless Quantization): asymmetric INT2..INT8 group-128
+ * weight quantization with dense bit-packing, the weight-only dequantize
+ * matmul (W{2..8}A16) that serves a layer-wise mixed-bit-width model, and
+ * the EAR / KL fidelity reductions used to judge it.
+ *
+ * Sources (page title -> section):
+ *   gist.science, "Statistically-Lossless Quantization of Large Language
+ *     Models": Methodology 1 (centering inefficiency gamma = 2M/R and the
+ *     gamma-squared variance law), Methodology 2 (EAR), Methodology 3
+ *     (asymmetric integer group quantization, group size 128; served by
+ *     weight-only mixed-precision kernels), Inference Speedup.
+ *   "SLQ" GitHub README: Pipeline (asymmetric INT, g128, bit-widths 2..8),
+ *     Usage 4 (weights packed to their per-layer bit-width on load),
+ *     Evaluation (EAR and KL of a model against its base).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer (hipMalloc / torch CUDA memory)
+ *     owned by the caller; the library never allocates, frees or retains it.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; results are visible after the
+ *     stream is synchronized.  Device faults surface at that synchronization.
+ *   - Arguments are validated on the host before any HIP call.  On any
+ *     status other than SLQ_OK nothing was enqueued and outputs are untouched.
+ *   - Sizes may be zero (then the call is a no-op returning SLQ_OK).
+ *   - Calls on different streams are independent and thread-safe; calls that
+ *     share a workspace buffer must be ordered by the caller.
+ *   - Non-finite weights or logits are a precondition violation (results are
+ *     unspecified, never an error code).
+ */
+#ifndef SLQ_H
+#define SLQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLQ_OK = 0,
+  SLQ_EINVAL = 1,   /* bad size, bit-width, pointer, alignment or aliasing   */
+  SLQ_ENOTSUP = 2,  /* valid request the library does not implement (g!=128) */
+  SLQ_EHIP = 3      /* the HIP runtime reported an error at launch            */
+} slq_status;
+
+typedef enum {
+  SLQ_ASYM = 0,     /* asymmetric grid: scale and zero point per group       */
+  SLQ_SYM = 1       /* symmetric grid (comparison only): center 2^(b-1)      */
+} slq_grid;
+
+typedef void *slq_stream; /* a hipStream_t */
+
+/*
+ * A quantized weight W[n][k] (n outputs, k inputs, k contiguous) in groups of
+ * `group` consecutive inputs along k.  G = k / group groups per row.
+ *   codes  : uint32 [n][k*bits/32].  Each row is one little-endian bitstream:
+ *            code j of the row occupies bits [j*bits, j*bits+bits) of the
+ *            integer sum_i codes[row][i] * 2^(32 i); group g starts at word
+ *            4*bits*g.  For bits = 4 this is 8 codes per word, nibble j = code
+ *            j; 3/5/6/7-bit codes straddle word boundaries with no padding.
+ *   scales : fp32 [n][G], > 0.
+ *   zeros  : uint8 [n][G], in [0, 2^bits - 1].
+ * Reconstruction: w_hat[n][k] = fl32((q[n][k] - zeros[n][g]) * scales[n][g]).
+ * Storage: bits + 40/group bits per parameter (fp32 scale + u8 zero point).
+ */
+typedef struct {
+  int32_t bits;   /* 2..8                                   */
+  int32_t group;  /* 128                                    */
+  int64_t n;      /* rows (outputs)                         */
+  int64_t k;      /* columns (inputs), a multiple of group  */
+  uint32_t *codes;
+  float *scales;
+  uint8_t *zeros;
+} slq_packed;
+
+/* Bytes of the codes array: n*k*bits/8 (0 on invalid arguments). */
+size_t slq_codes_bytes(int64_t n, int64_t k, int bits);
+
+/*
+ * Group quantization and dense packing of an fp32 weight (gist.science
+ * summary, Methodology 3: asymmetric integer group quantization with group
+ * size 128; README, Pipeline: bit-widths 2..8; README, Usage 4: packing to
+ * the per-layer bit-width).  Per row n and group g, with maxq = 2^bits - 1:
+ *   SLQ_ASYM: lo = min(0, min w), hi = max(0, max w);
+ *             s = fl32(fl32(hi - lo) / maxq); if s == 0 then s = 1, z = 0;
+ *             else z = clamp(rint(fl32(-lo / s)), 0, maxq).
+ *   SLQ_SYM : M = max |w|, s = fl32(2M / maxq) (1 if zero), z = 2^(bits-1)
+ *             (the comparison grid of Methodology 1).
+ *   q = clamp(rint(fl32(w / s)) + z, 0, maxq); rint rounds half to even and
+ *   every fp32 operation is IEEE correctly rounded, so the result is exact
+ *   and reproducible bit for bit.
+ * In : W fp32 [n][k] (device, 16-byte aligned), n >= 0, k % group == 0,
+ *      bits in 2..8, group == 128 (else SLQ_ENOTSUP).
+ * Out: out->codes/scales/zeros must point to caller-owned device buffers of
+ *      slq_codes_bytes(n,k,bits), 4*n*(k/group) and n*(k/group) bytes, codes
+ *      16-byte aligned, none overlapping W.  The call fills out->bits, group,
+ *      n and k and writes the three arrays.
+ */
+slq_status slq_quantize_pack(const float *W, int64_t n, int64_t k, int bits, int group,
+                             slq_grid grid, slq_packed *out, slq_stream stream);
+
+/*
+ * Reconstruction w_hat[n][k] = fl32((q - z) * s) into W_deq (fp32 [n][k],
+ * device, not overlapping the packed arrays).
+ */
+slq_status slq_dequantize(const slq_packed *w, float *W_deq, slq_stream stream);
+
+/* Workspace bytes slq_dequant_gemm needs for this (m, w); may be 0. */
+size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w);
+
+/*
+ * Weight-only dequantize matmul y[m][n] = sum_k x[m][k] * w_hat[n][k]
+ * (gist.science summary, Methodology 3 and Inference Speedup: 16-bit
+ * activations against the packed low-bit weights of each layer).
+ * In : x bf16 bit patterns [m][k] (device, 16-byte aligned), w a packed
+ *      weight from slq_quantize_pack (any bits 2..8), m >= 0.
+ * Out: y fp32 [m][n] (device, 16-byte aligned, not overlapping inputs).
+ * workspace: device buffer of slq_gemm_workspace_bytes(m, w) bytes, 256-byte
+ *      aligned, ZERO-FILLED before its first use.  Its first 64 KiB hold
+ *      split-K tickets that every completed call leaves at zero, so one buffer
+ *      (of the largest size needed) serves any sequence of calls on one
+ *      stream; calls that overlap in time must not share it.  May be NULL when
+ *      the size is 0.
+ * Accumulation is fp32.  m <= 64 runs the decode kernel (exact integer
+ * (q - z), per-group scale in fp32); m > 64 runs the prefill kernel (w_hat
+ * rounded to bf16 tiles in LDS, bf16 MFMA).  Both stay within
+ * |y - y_exact| <= 1e-2 * sum_k |x||w_hat|.
+ */
+slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t m,
+                            float *y, void *workspace, slq_stream stream);
+
+/* Workspace bytes slq_ear_kl / slq_row_lse need for (rows, vocab). */
+size_t slq_ear_kl_workspace_bytes(int64_t rows, int64_t vocab);
+
+/*
+ * Row log-normalizer lse[r] = max_v a[r][v] + log sum_v exp(a[r][v] - max),
+ * fp64 out (the softmax at temperature 1 that defines the next-token
+ * distribution; SLQ blog, The Motivation).
+ * In : a fp32 [rows][vocab] (device, 16-byte aligned).  Out: lse fp64 [rows].
+ * workspace: slq_ear_kl_workspace_bytes(rows, vocab) bytes, 256-byte aligned.
+ */
+slq_status slq_row_lse(const float *logits, int64_t rows, int64_t vocab, double *lse,
+                       void *workspace, slq_stream stream);
+
+/*
+ * Fidelity of a quantized model's next-token distributions q = softmax(b)
+ * against the reference p = softmax(a), per row (position):
+ *   EAR_r = sum_v min(p_v, q_v)    (gist.science summary, Methodology 2; over
+ *                                   the full vocabulary)
+ *   KL_r  = sum_v p_v log(p_v / q_v), natural log (README, Evaluation)
+ * and means[0] = mean_r EAR_r, means[1] = mean_r KL_r.
+ * In : logits_p (reference), logits_q: fp32 [rows][vocab] (device, 16-byte
+ *      aligned).  Out: ear_rows, kl_rows fp32 [rows]; means fp64 [2].
+ * workspace: slq_ear_kl_workspace_bytes(rows, vocab) bytes, 256-byte aligned.
+ * Reductions are deterministic (fixed order): repeated calls are bit-equal.
+ */
+slq_status slq_ear_kl(const float *logits_p, const float *logits_q, int64_t rows, int64_t vocab,
+                      float *ear_rows, float *kl_rows, double *means, void *workspace,
+                      slq_stream stream);
+
+/* Workspace bytes slq_quant_error needs for w. */
+size_t slq_quant_error_workspace_bytes(const slq_packed *w);
+
+/*
+ * Quantization noise of a grid over a layer, for the gamma-squared law
+ * (gist.science summary, Methodology 1): out[0] = sum (w - w_hat)^2,
+ * out[1] = sum_g s_g^2, fp64, deterministic order.  The symmetric/asymmetric
+ * ratio of out[0] is the measured noise-variance ratio, that of out[1] the
+ * predicted one (rounding noise is s^2/12 per element).
+ * In : W fp32 [n][k] (the quantized source), w packed from W.
+ * Out: out fp64 [2] (device).
+ */
+slq_status slq_quant_error(const float *W, const slq_packed *w, double *out, void *workspace,
+                           slq_stream stream);
+
+/* Static description of a status code. */
+const char *slq_strerror(slq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLQ_H */

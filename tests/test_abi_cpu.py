@@ -1,0 +1,127 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/slq.h declares, and rejects invalid requests before any HIP call.
+
+Pointers here are fake device addresses; validation never dereferences them
+and an invalid request returns before the HIP runtime is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_mixed_amd as slq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "slq.h")
+
+A = 0x10000000          # fake, 256-byte aligned "device" addresses far apart
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(slq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = slq.lib()
+    names = declared_functions()
+    assert len(names) == 11
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def packed(bits=4, group=128, n=64, k=256, codes=B, scales=C, zeros=D):
+    return slq.SlqPacked(bits, group, n, k, codes, scales, zeros)
+
+
+def call_qp(W=A, n=64, k=256, bits=4, group=128, grid=0, out=None):
+    out = out if out is not None else packed(0, 0, 0, 0)
+    st = slq.lib().slq_quantize_pack(W, n, k, bits, group, grid, ctypes.byref(out), None)
+    return st, out
+
+
+def test_quantize_pack_validation():
+    assert call_qp(bits=1)[0] == slq.SLQ_EINVAL
+    assert call_qp(bits=9)[0] == slq.SLQ_EINVAL
+    assert call_qp(group=64)[0] == slq.SLQ_ENOTSUP
+    assert call_qp(group=0)[0] == slq.SLQ_EINVAL
+    assert call_qp(k=200)[0] == slq.SLQ_EINVAL
+    assert call_qp(n=-1)[0] == slq.SLQ_EINVAL
+    assert call_qp(grid=7)[0] == slq.SLQ_EINVAL
+    assert call_qp(W=None)[0] == slq.SLQ_EINVAL
+    assert call_qp(W=A + 4)[0] == slq.SLQ_EINVAL                      # misaligned
+    assert slq.lib().slq_quantize_pack(A, 4, 128, 4, 128, 0, None, None) == slq.SLQ_EINVAL
+    # outputs overlapping the input or each other
+    st, _ = call_qp(out=packed(codes=A + 4096, scales=C, zeros=D))
+    assert st == slq.SLQ_EINVAL
+    st, _ = call_qp(out=packed(codes=B, scales=B + 64, zeros=D))
+    assert st == slq.SLQ_EINVAL
+    # the descriptor is untouched on error
+    out = packed(bits=0, group=0, n=0, k=0)
+    st, out = call_qp(bits=9, out=out)
+    assert st == slq.SLQ_EINVAL and out.bits == 0 and out.n == 0
+    # empty input: valid no-op that fills the descriptor, no HIP call
+    out = packed(bits=0, group=0, n=0, k=0)
+    st, out = call_qp(n=0, out=out)
+    assert st == slq.SLQ_OK and (out.bits, out.group, out.n, out.k) == (4, 128, 0, 256)
+
+
+def test_dequant_gemm_validation():
+    L = slq.lib()
+    w = packed()
+    y = E
+    assert L.slq_dequant_gemm(A, ctypes.byref(packed(bits=9)), 1, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(packed(group=32)), 1, y, None, None) == slq.SLQ_ENOTSUP
+    assert L.slq_dequant_gemm(A, ctypes.byref(packed(k=100)), 1, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(packed(codes=0)), 1, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(packed(codes=B + 4)), 1, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(w), -1, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(None, ctypes.byref(w), 1, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, None, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, A, None, None) == slq.SLQ_EINVAL  # y aliases x
+    assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, B, None, None) == slq.SLQ_EINVAL  # y aliases codes
+    assert L.slq_dequant_gemm(A, None, 1, y, None, None) == slq.SLQ_EINVAL
+    # split-K workspace required when the plan uses one
+    big = packed(n=4096, k=4096)
+    assert L.slq_gemm_workspace_bytes(1, ctypes.byref(big)) > 0
+    assert L.slq_dequant_gemm(A, ctypes.byref(big), 1, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(big), 1, y, E + 0x100000 + 8, None) == slq.SLQ_EINVAL
+    # m == 0: valid no-op
+    assert L.slq_dequant_gemm(None, ctypes.byref(w), 0, None, None, None) == slq.SLQ_OK
+
+
+def test_fidelity_and_error_validation():
+    L = slq.lib()
+    assert L.slq_ear_kl(A, B, 4, 0, C, C + 64, D, E, None) == slq.SLQ_EINVAL       # empty vocab
+    assert L.slq_ear_kl(A, B, -1, 10, C, C + 64, D, E, None) == slq.SLQ_EINVAL
+    assert L.slq_ear_kl(A, B, 4, 10, C, C, D, E, None) == slq.SLQ_EINVAL           # ear == kl
+    assert L.slq_ear_kl(A, B, 4, 10, C, C + 64, D, None, None) == slq.SLQ_EINVAL   # no workspace
+    assert L.slq_ear_kl(A + 4, B, 4, 12, C, C + 64, D, E, None) == slq.SLQ_EINVAL  # misaligned
+    assert L.slq_ear_kl(A, B, 0, 10, None, None, None, None, None) == slq.SLQ_OK
+    assert L.slq_row_lse(A, 4, 0, C, E, None) == slq.SLQ_EINVAL
+    assert L.slq_row_lse(A, 4, 10, A, E, None) == slq.SLQ_EINVAL                   # lse aliases input
+    assert L.slq_quant_error(A, ctypes.byref(packed(bits=1)), C, E, None) == slq.SLQ_EINVAL
+    assert L.slq_quant_error(A, ctypes.byref(packed()), None, E, None) == slq.SLQ_EINVAL
+    assert L.slq_quant_error(A, ctypes.byref(packed()), C, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequantize(ctypes.byref(packed()), None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequantize(ctypes.byref(packed()), B, None) == slq.SLQ_EINVAL     # aliases codes
+
+
+def test_sizes_and_strings():
+    L = slq.lib()
+    for b in range(2, 9):
+        assert L.slq_codes_bytes(4096, 4096, b) == 4096 * 4096 * b // 8
+    assert L.slq_codes_bytes(3, 256, 3) == 3 * 256 * 3 // 8
+    assert L.slq_codes_bytes(3, 256, 9) == 0
+    assert L.slq_gemm_workspace_bytes(1, ctypes.byref(packed(n=1, k=128))) == 0
+    assert L.slq_ear_kl_workspace_bytes(512, 151936) > 0
+    assert L.slq_quant_error_workspace_bytes(ctypes.byref(packed())) > 0
+    for s in range(4):
+        assert L.slq_strerror(s)
+    assert L.slq_strerror(0) == b"ok"

@@ -1,0 +1,190 @@
+"""GPU parity of the weight-only dequantize matmul (decode m <= 64 and prefill
+m > 64) against the oracle's fp64 product, within
+|y - y_ref| <= 1e-2 * sum_k |x| |w_hat| per output, plus exact pins."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import slq_synth as S
+import weight_only_mixed_amd as slq
+from tests.gpu_util import (DEV, assert_gemm_close, gpu, oracle_sampled, sample_pairs, say,
+                            x_gpu)
+
+pytestmark = pytest.mark.gpu
+
+BITS = [2, 3, 4, 5, 6, 7, 8]
+
+
+def run(W, bits, x_bits):
+    pw = slq.slq_quantize_pack(gpu(W), bits)
+    y = slq.slq_dequant_gemm(x_gpu(x_bits), pw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), pw
+
+
+def full_ref(W, bits, x_bits):
+    q, s, z = oracle.quantize(W, bits)
+    wh = oracle.dequantize(q, s, z)
+    y, b = oracle.gemm(x_bits, wh)
+    return y, b, wh
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_decode_small_shapes(bits):
+    for (n, k) in [(1, 128), (50, 384), (300, 1024), (1000, 4096)]:
+        W = S.skewed_weights(n, k, 10 * bits + n, row_offset_std=0.005)
+        for m in (1, 3, 8, 16, 17, 32, 64):
+            say(f"decode bits={bits} m={m} n={n} k={k}")
+            x = S.activations_bf16(m, k, m + n + bits)
+            y, _ = run(W, bits, x)
+            yr, br, _ = full_ref(W, bits, x)
+            assert_gemm_close(y, yr, br, what=f"b{bits} m{m} {n}x{k}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_prefill_small_shapes(bits):
+    for (m, n, k) in [(65, 70, 256), (129, 300, 640), (256, 128, 1024)]:
+        say(f"prefill bits={bits} m={m} n={n} k={k}")
+        W = S.skewed_weights(n, k, 7 * bits + n, row_offset_std=0.005)
+        x = S.activations_bf16(m, k, m + bits)
+        y, _ = run(W, bits, x)
+        yr, br, _ = full_ref(W, bits, x)
+        assert_gemm_close(y, yr, br, what=f"b{bits} m{m} {n}x{k}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_exact_pins(bits):
+    """One-hot activations give w_hat exactly (decode path); zero rows give 0;
+    identical activation rows give identical outputs."""
+    n, k = 40, 512
+    W = S.skewed_weights(n, k, 5 + bits)
+    W[7] = 0.0
+    q, s, z = oracle.quantize(W, bits)
+    wh = oracle.dequantize(q, s, z)
+    pw = slq.slq_quantize_pack(gpu(W), bits)
+    for k0 in (0, 1, 127, 128, 300, 511):
+        for m in (1, 16, 64):
+            xb = np.zeros((m, k), np.uint16)
+            xb[:, k0] = 0x3F80                     # bf16 1.0
+            y = slq.slq_dequant_gemm(x_gpu(xb), pw).cpu().numpy()
+            assert np.array_equal(y, np.broadcast_to(wh[:, k0], (m, n))), (bits, k0, m)
+    for m in (1, 5, 33, 64, 100):
+        xb = S.activations_bf16(m, k, 9)
+        xb[m // 2] = xb[0]
+        y = slq.slq_dequant_gemm(x_gpu(xb), pw).cpu().numpy()
+        assert (y[:, 7] == 0).all()
+        assert np.array_equal(y[0], y[m // 2])
+    # prefill one-hot: within bf16 rounding of w_hat
+    xb = np.zeros((96, k), np.uint16)
+    xb[:, 300] = 0x3F80
+    y = slq.slq_dequant_gemm(x_gpu(xb), pw).cpu().numpy()
+    assert np.all(np.abs(y - wh[:, 300]) <= np.abs(wh[:, 300]) * 2 ** -8)
+
+
+def test_decode_deterministic_and_workspace_reset():
+    n, k = 4096, 4096
+    W = S.skewed_weights(n, k, 1)
+    pw = slq.slq_quantize_pack(gpu(W), 4)
+    x = x_gpu(S.activations_bf16(16, k, 2))
+    nb = slq.gemm_workspace_bytes(16, pw)
+    assert nb > 0
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    y1 = slq.slq_dequant_gemm(x, pw, ws=ws).clone()
+    y2 = slq.slq_dequant_gemm(x, pw, ws=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    # tickets (first 64 KiB of the workspace) are back to zero
+    assert int(ws[:65536].sum()) == 0
+    # a smaller plan after a larger one reuses the buffer: tickets still valid
+    W2 = S.skewed_weights(14336, 4096, 3)
+    pw2 = slq.slq_quantize_pack(gpu(W2), 3)
+    assert slq.gemm_workspace_bytes(1, pw2) <= nb
+    xs = S.activations_bf16(1, 4096, 4)
+    y3 = slq.slq_dequant_gemm(x_gpu(xs), pw2, ws=ws).cpu().numpy()
+    mi, ni = sample_pairs(1, 14336, 2048, seed=5)
+    yr, br = oracle_sampled(W2, 3, xs, mi, ni)
+    assert_gemm_close(y3[mi, ni], yr, br, what="reused workspace")
+    assert int(ws[:65536].sum()) == 0
+
+
+def test_single_layer_decode_workload():
+    """M=1, 4096x4096, asymmetric INT4 g128: every output against the oracle."""
+    W = S.skewed_weights(4096, 4096, S.seed_for(1))
+    x = S.activations_bf16(1, 4096, S.seed_for(1) + 1)
+    y, _ = run(W, 4, x)
+    yr, br, _ = full_ref(W, 4, x)
+    r = assert_gemm_close(y, yr, br, what="single layer")
+    say(f"single-layer decode max err/bound = {r:.3e}")
+
+
+def test_decode_sweep_workload_sampled():
+    """Llama-3-8B projections x bits {3,4,8} x M {1,8,16} at full size, in the
+    launch configuration the bench times; 4096 sampled outputs per point."""
+    shapes = {"q": (4096, 4096), "kv": (1024, 4096), "gateup": (14336, 4096), "down": (4096, 14336)}
+    worst = 0.0
+    for i, (name, (n, k)) in enumerate(shapes.items()):
+        W = S.skewed_weights(n, k, S.seed_for(2, 0, i), row_offset_std=0.005)
+        Wd = gpu(W)
+        for bits in (3, 4, 8):
+            pw = slq.slq_quantize_pack(Wd, bits)
+            for m in (1, 8, 16):
+                say(f"sweep {name} {n}x{k} bits={bits} m={m}")
+                x = S.activations_bf16(m, k, S.seed_for(2, m, i))
+                y = slq.slq_dequant_gemm(x_gpu(x), pw).cpu().numpy()
+                mi, ni = sample_pairs(m, n, 4096, seed=i * 100 + bits * 10 + m)
+                yr, br = oracle_sampled(W, bits, x, mi, ni)
+                worst = max(worst, assert_gemm_close(y[mi, ni], yr, br, what=f"{name} b{bits} m{m}"))
+    say(f"sweep worst err/bound = {worst:.3e}")
+
+
+def test_mixed_stack_workload_sampled():
+    """32 layers x 7 projections of Llama-3-8B shape with the seeded per-layer
+    bit map (k/v 7-8, q/o 5-6, MLP 3-4), M in {1, 32, 64}: the bench's recipe
+    (one layer of fp32 weights quantized at every layer's widths), sampled
+    outputs of all 224 matmuls."""
+    bmap = S.mixed_bit_map()
+    Ws = {p: S.skewed_weights(*S.LLAMA3_8B_PROJ[p], S.seed_for(3, 0, j), row_offset_std=0.005)
+          for j, p in enumerate(S.PROJ_ORDER)}
+    Wd = {p: gpu(w) for p, w in Ws.items()}
+    xs = {m: {k: S.activations_bf16(m, k, S.seed_for(3, m, k % 97)) for k in (4096, 14336)}
+          for m in (1, 32, 64)}
+    xd = {m: {k: x_gpu(v) for k, v in d.items()} for m, d in xs.items()}
+    refcache = {}
+    for layer in range(32):
+        say(f"stack layer {layer}: {bmap[layer]}")
+        for j, p in enumerate(S.PROJ_ORDER):
+            b = bmap[layer][p]
+            n, k = S.LLAMA3_8B_PROJ[p]
+            pw = slq.slq_quantize_pack(Wd[p], b)
+            for m in (1, 32, 64):
+                y = slq.slq_dequant_gemm(xd[m][k], pw).cpu().numpy()
+                mi, ni = sample_pairs(m, n, 256, seed=layer * 1000 + j * 10 + m)
+                key = (p, b, m, layer)
+                yr, br = oracle_sampled(Ws[p], b, xs[m][k], mi, ni)
+                assert_gemm_close(y[mi, ni], yr, br, what=f"L{layer} {p} b{b} m{m}")
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bits", [4, 6])
+def test_prefill_workload_sampled(bits):
+    """M=4096 on Llama-3.3-70B projection shapes, 4096 sampled outputs each."""
+    x = S.activations_bf16(4096, 8192, S.seed_for(4) + bits)
+    x28 = None
+    for i, name in enumerate(("q", "k", "gate", "down")):
+        n, k = S.LLAMA33_70B_PROJ[name]
+        say(f"prefill {name} {n}x{k} bits={bits}")
+        W = S.skewed_weights(n, k, S.seed_for(4, 0, i), row_offset_std=0.005)
+        if k == 8192:
+            xb = x
+        else:
+            x28 = x28 if x28 is not None else S.activations_bf16(4096, k, S.seed_for(4) + 10 + bits)
+            xb = x28
+        pw = slq.slq_quantize_pack(gpu(W), bits)
+        y = slq.slq_dequant_gemm(x_gpu(xb), pw)
+        mi, ni = sample_pairs(4096, n, 4096, seed=bits * 10 + i)
+        ys = y[torch.from_numpy(mi).to(DEV), torch.from_numpy(ni).to(DEV)].cpu().numpy()
+        yr, br = oracle_sampled(W, bits, xb, mi, ni)
+        assert_gemm_close(ys, yr, br, what=f"prefill {name} b{bits}")
+        del y, pw, W
+        torch.cuda.empty_cache()

@@ -1,0 +1,208 @@
+"""Python binding of libslq (SLQ hot path on MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI in include/slq.h: every computation runs
+in the HIP kernels of libslq.so.  torch provides device memory and the current
+stream.  There is no fallback: if the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libslq.so")
+
+SLQ_OK, SLQ_EINVAL, SLQ_ENOTSUP, SLQ_EHIP = 0, 1, 2, 3
+SLQ_ASYM, SLQ_SYM = 0, 1
+GROUP = 128
+
+
+class SlqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().slq_strerror(status).decode()} (status {status})")
+
+
+class SlqPacked(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p)]
+
+
+_LIB = None
+_i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_pp = ctypes.POINTER(SlqPacked)
+
+
+def lib():
+    """Load libslq.so (built in-tree by weight_only_mixed_amd/build.py)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with weight_only_mixed_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        L.slq_codes_bytes.argtypes = [_i64, _i64, _int]
+        L.slq_codes_bytes.restype = _sz
+        L.slq_quantize_pack.argtypes = [_vp, _i64, _i64, _int, _int, _int, _pp, _vp]
+        L.slq_dequantize.argtypes = [_pp, _vp, _vp]
+        L.slq_gemm_workspace_bytes.argtypes = [_i64, _pp]
+        L.slq_gemm_workspace_bytes.restype = _sz
+        L.slq_dequant_gemm.argtypes = [_vp, _pp, _i64, _vp, _vp, _vp]
+        L.slq_ear_kl_workspace_bytes.argtypes = [_i64, _i64]
+        L.slq_ear_kl_workspace_bytes.restype = _sz
+        L.slq_row_lse.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+        L.slq_ear_kl.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+        L.slq_quant_error_workspace_bytes.argtypes = [_pp]
+        L.slq_quant_error_workspace_bytes.restype = _sz
+        L.slq_quant_error.argtypes = [_vp, _pp, _vp, _vp, _vp]
+        L.slq_strerror.argtypes = [_int]
+        L.slq_strerror.restype = ctypes.c_char_p
+        for f in ("slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm", "slq_row_lse",
+                  "slq_ear_kl", "slq_quant_error"):
+            getattr(L, f).restype = _int
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str):
+    if status != SLQ_OK:
+        raise SlqError(status, what)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class PackedWeight:
+    """A packed weight: codes uint32 [n][k*bits/32], scales fp32 [n][G], zeros uint8 [n][G]."""
+    bits: int
+    n: int
+    k: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+    zeros: torch.Tensor
+    group: int = GROUP
+
+    def c(self) -> SlqPacked:
+        return SlqPacked(self.bits, self.group, self.n, self.k, _ptr(self.codes),
+                         _ptr(self.scales), _ptr(self.zeros))
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.numel() * 4 + self.scales.numel() * 4 + self.zeros.numel()
+
+
+def alloc_packed(n: int, k: int, bits: int, device, group: int = GROUP) -> PackedWeight:
+    G = k // group
+    return PackedWeight(bits, n, k,
+                        torch.empty((n, k * bits // 32), dtype=torch.int32, device=device),
+                        torch.empty((n, G), dtype=torch.float32, device=device),
+                        torch.empty((n, G), dtype=torch.uint8, device=device), group)
+
+
+def slq_quantize_pack(W: torch.Tensor, bits: int, group: int = GROUP, grid: int = SLQ_ASYM,
+                      out: PackedWeight | None = None) -> PackedWeight:
+    """Quantize fp32 W[n][k] to `bits` (asymmetric by default) and pack it."""
+    assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous()
+    n, k = W.shape
+    pw = out if out is not None else alloc_packed(n, k, bits, W.device, group)
+    desc = pw.c()
+    _check(lib().slq_quantize_pack(_ptr(W), n, k, bits, group, grid, ctypes.byref(desc),
+                                   _stream(W)), "slq_quantize_pack")
+    return pw
+
+
+def slq_dequantize(pw: PackedWeight, out: torch.Tensor | None = None) -> torch.Tensor:
+    out = out if out is not None else torch.empty((pw.n, pw.k), dtype=torch.float32,
+                                                  device=pw.codes.device)
+    desc = pw.c()
+    _check(lib().slq_dequantize(ctypes.byref(desc), _ptr(out), _stream(out)), "slq_dequantize")
+    return out
+
+
+_WS: dict = {}
+
+
+def workspace(nbytes: int, device, tag: str = "gemm") -> torch.Tensor | None:
+    """A zero-filled workspace cached per (tag, device, stream); grown on demand.
+
+    The library leaves a gemm workspace zero-filled after every completed call,
+    so one buffer serves all calls issued on the same stream."""
+    if nbytes == 0:
+        return None
+    dev = torch.device(device)
+    key = (tag, dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=dev)
+        _WS[key] = buf
+    return buf
+
+
+def gemm_workspace_bytes(m: int, pw: PackedWeight) -> int:
+    desc = pw.c()
+    return lib().slq_gemm_workspace_bytes(m, ctypes.byref(desc))
+
+
+def slq_dequant_gemm(x: torch.Tensor, pw: PackedWeight, y: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None) -> torch.Tensor:
+    """y[m][n] = x[m][k] . w_hat[n][k]^T with bf16 x, fp32 y."""
+    assert x.dtype in (torch.bfloat16, torch.int16, torch.uint16) and x.is_cuda
+    assert x.is_contiguous() and x.shape[-1] == pw.k
+    m = x.numel() // pw.k if pw.k else x.shape[0]
+    y = y if y is not None else torch.empty((m, pw.n), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(gemm_workspace_bytes(m, pw), x.device)
+    desc = pw.c()
+    _check(lib().slq_dequant_gemm(_ptr(x), ctypes.byref(desc), m, _ptr(y), _ptr(ws), _stream(x)),
+           "slq_dequant_gemm")
+    return y
+
+
+def slq_row_lse(logits: torch.Tensor) -> torch.Tensor:
+    assert logits.dtype == torch.float32 and logits.is_cuda and logits.is_contiguous()
+    rows, vocab = logits.shape
+    lse = torch.empty(rows, dtype=torch.float64, device=logits.device)
+    ws = workspace(lib().slq_ear_kl_workspace_bytes(rows, vocab), logits.device, "fidelity")
+    _check(lib().slq_row_lse(_ptr(logits), rows, vocab, _ptr(lse), _ptr(ws), _stream(logits)),
+           "slq_row_lse")
+    return lse
+
+
+def slq_ear_kl(logits_p: torch.Tensor, logits_q: torch.Tensor):
+    """Per-row EAR and KL(p||q) (fp32) and their means (fp64 [2]) on the device."""
+    assert logits_p.shape == logits_q.shape and logits_p.dtype == torch.float32
+    assert logits_p.is_contiguous() and logits_q.is_contiguous()
+    rows, vocab = logits_p.shape
+    dev = logits_p.device
+    ear = torch.empty(rows, dtype=torch.float32, device=dev)
+    kl = torch.empty(rows, dtype=torch.float32, device=dev)
+    means = torch.empty(2, dtype=torch.float64, device=dev)
+    ws = workspace(lib().slq_ear_kl_workspace_bytes(rows, vocab), dev, "fidelity")
+    _check(lib().slq_ear_kl(_ptr(logits_p), _ptr(logits_q), rows, vocab, _ptr(ear), _ptr(kl),
+                            _ptr(means), _ptr(ws), _stream(logits_p)), "slq_ear_kl")
+    return ear, kl, means
+
+
+def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
+    """fp64 [2] on the device: (sum (w - w_hat)^2, sum_g s_g^2)."""
+    desc = pw.c()
+    out = torch.empty(2, dtype=torch.float64, device=W.device)
+    ws = workspace(lib().slq_quant_error_workspace_bytes(ctypes.byref(desc)), W.device, "qerr")
+    _check(lib().slq_quant_error(_ptr(W), ctypes.byref(desc), _ptr(out), _ptr(ws), _stream(W)),
+           "slq_quant_error")
+    return out
+
+
+__all__ = ["lib", "SlqError", "SlqPacked", "PackedWeight", "alloc_packed", "workspace",
+           "gemm_workspace_bytes", "slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm",
+           "slq_row_lse", "slq_ear_kl", "slq_quant_error", "SLQ_ASYM", "SLQ_SYM", "GROUP"]

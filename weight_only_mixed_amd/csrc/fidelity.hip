@@ -1,0 +1,320 @@
+// Fidelity reductions over next-token logits for gfx950: row log-normalizer,
+// EAR (sum of min(p, q)) and KL(p || q).
+//
+// Sources: gist.science summary "Statistically-Lossless Quantization of Large
+// Language Models", Methodology 2 (EAR: summed min of the reference and
+// quantized next-token distributions, averaged over positions); SLQ README,
+// Evaluation (EAR and KL of a model against its base); SLQ blog, The
+// Motivation (the next-token distribution is the softmax of the logits).
+//
+// Each row (a position) is cut into C chunks so that rows * C workgroups fill
+// the chip.  Pass 1 streams a and b once per chunk and keeps, per thread, an
+// online (running max, sum of exp) pair for both rows plus
+//   U = sum_v exp(a_v - max_a) * (a_v - b_v),
+// which gives KL without a second pass: KL = U / Z_a - (A - B), where A and B
+// are the log-normalizers.  Chunk partials are combined per row in fp64 in a
+// fixed order.  Pass 2 needs A and B (min(p, q) is not decomposable before
+// normalization), re-reads the rows in reverse order so the most recently
+// streamed rows are still cached, and sums min(exp(a - A), exp(b - B)).
+// Every reduction has a fixed shape, so repeated calls are bit-identical.
+#include <algorithm>
+
+#include "launch.h"
+#include "slq_device.h"
+
+namespace slq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Fid {
+  int C;          // chunks per row
+  int64_t chunk;  // elements per chunk (multiple of 4)
+};
+
+Fid fid_plan(int64_t rows, int64_t vocab) {
+  Fid f;
+  int64_t c = (1024 + rows - 1) / rows;
+  const int64_t maxc = std::max<int64_t>(1, (vocab + 4095) / 4096);
+  c = std::min(std::max<int64_t>(c, 1), maxc);
+  int64_t chunk = (vocab + c - 1) / c;
+  chunk = (chunk + 3) & ~(int64_t)3;
+  f.C = (int)((vocab + chunk - 1) / chunk);
+  f.chunk = chunk;
+  return f;
+}
+
+// Workspace: stats [rows][C][5] | rowres [rows][4] | earpart [rows][C]  (doubles)
+size_t ws_doubles(int64_t rows, const Fid &f) {
+  return (size_t)rows * f.C * 5 + (size_t)rows * 4 + (size_t)rows * f.C;
+}
+
+__device__ __forceinline__ float fast_exp(float v) { return exp2f(v * kLog2e); }
+
+// (m, z, u) combine: z, u are sums of exp(. - m).
+struct MZ {
+  double m, z, u;
+};
+__device__ __forceinline__ MZ mz_combine(MZ p, MZ q) {
+  if (q.m == -INFINITY) return p;
+  if (p.m == -INFINITY) return q;
+  const double M = p.m > q.m ? p.m : q.m;
+  const double fp = exp(p.m - M), fq = exp(q.m - M);
+  return MZ{M, p.z * fp + q.z * fq, p.u * fp + q.u * fq};
+}
+__device__ __forceinline__ MZ mz_shfl(MZ v, int o) {
+  return MZ{__shfl_xor(v.m, o, kWave), __shfl_xor(v.z, o, kWave), __shfl_xor(v.u, o, kWave)};
+}
+__device__ MZ mz_block(MZ v, MZ *lds) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = mz_combine(v, mz_shfl(v, o));
+  const int wave = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[wave] = v;
+  __syncthreads();
+  MZ t = lds[0];
+  for (int i = 1; i < kThreads / kWave; ++i) t = mz_combine(t, lds[i]);
+  return t;
+}
+
+// Online update of (m, z, u) with 4 new values of a (u only when WITH_U).
+// The difference a - b enters u in fp64, where it is exact: with logits far
+// from zero an fp32 difference would lose more than the KL being measured.
+template <bool WITH_U>
+__device__ __forceinline__ void online4(float4 a, float4 b, float &m, double &z, double &u) {
+  const float mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
+  if (mx > m) {
+    const float f = fast_exp(m - mx);   // m = -inf gives 0
+    z *= (double)f;
+    if (WITH_U) u *= (double)f;
+    m = mx;
+  }
+  const float e0 = fast_exp(a.x - m), e1 = fast_exp(a.y - m), e2 = fast_exp(a.z - m),
+              e3 = fast_exp(a.w - m);
+  if (!WITH_U) {
+    z += (double)((e0 + e1) + (e2 + e3));
+  } else {
+    // U / Z is a p-weighted mean of a - b, which can be large next to the KL:
+    // both sums take exactly the same fp64 weights.
+    z += (double)e0;
+    z += (double)e1;
+    z += (double)e2;
+    z += (double)e3;
+    u = fma((double)e0, (double)a.x - (double)b.x, u);
+    u = fma((double)e1, (double)a.y - (double)b.y, u);
+    u = fma((double)e2, (double)a.z - (double)b.z, u);
+    u = fma((double)e3, (double)a.w - (double)b.w, u);
+  }
+}
+
+// Online update with one value (rows whose length is not a multiple of 4).
+template <bool WITH_U>
+__device__ __forceinline__ void online1(float a, float b, float &m, double &z, double &u) {
+  if (a > m) {
+    const float f = fast_exp(m - a);
+    z *= (double)f;
+    if (WITH_U) u *= (double)f;
+    m = a;
+  }
+  const float e = fast_exp(a - m);
+  z += (double)e;
+  if (WITH_U) u = fma((double)e, (double)a - (double)b, u);
+}
+
+// Pass 1: per (chunk, row) partial (m_a, Z_a, U, m_b, Z_b).
+template <bool WITH_B>
+__global__ __launch_bounds__(kThreads) void stats_kernel(const float *__restrict__ a,
+                                                         const float *__restrict__ b,
+                                                         int64_t vocab, Fid f,
+                                                         double *__restrict__ stats) {
+  __shared__ MZ lds[kThreads / kWave];
+  const int c = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int64_t beg = (int64_t)c * f.chunk;
+  const int64_t end = std::min<int64_t>(beg + f.chunk, vocab);
+  const float *ar = a + row * vocab;
+  const float *br = WITH_B ? b + row * vocab : nullptr;
+
+  float ma = -INFINITY, mb = -INFINITY;
+  double za = 0.0, ua = 0.0, zb = 0.0, ub = 0.0;
+  const bool vec = ((vocab & 3) == 0);
+  if (vec) {
+    const float4 *a4 = reinterpret_cast<const float4 *>(ar);
+    const float4 *b4 = WITH_B ? reinterpret_cast<const float4 *>(br) : nullptr;
+    for (int64_t i = beg / 4 + threadIdx.x; i < end / 4; i += kThreads) {
+      const float4 va = a4[i];
+      if (WITH_B) {
+        const float4 vb = b4[i];
+        online4<true>(va, vb, ma, za, ua);
+        online4<false>(vb, vb, mb, zb, ub);
+      } else {
+        online4<false>(va, va, ma, za, ua);
+      }
+    }
+  } else {
+    for (int64_t i = beg + threadIdx.x; i < end; i += kThreads) {
+      const float va = ar[i];
+      const float vb = WITH_B ? br[i] : 0.f;
+      online1<WITH_B>(va, vb, ma, za, ua);
+      if (WITH_B) online1<false>(vb, vb, mb, zb, ub);
+    }
+  }
+  const MZ ra = mz_block(MZ{(double)ma, za, ua}, lds);
+  MZ rb{0.0, 0.0, 0.0};
+  if (WITH_B) rb = mz_block(MZ{(double)mb, zb, 0.0}, lds);
+  if (threadIdx.x == 0) {
+    double *o = stats + (row * f.C + c) * 5;
+    o[0] = ra.m;
+    o[1] = ra.z;
+    o[2] = ra.u;
+    o[3] = rb.m;
+    o[4] = rb.z;
+  }
+}
+
+// Per row: combine chunk partials in chunk order -> A, B, KL.
+template <bool WITH_B>
+__global__ __launch_bounds__(kThreads) void rows_kernel(const double *__restrict__ stats, int64_t rows,
+                                                        Fid f, double *__restrict__ rowres,
+                                                        double *__restrict__ lse_out,
+                                                        float *__restrict__ kl_rows) {
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= rows) return;
+  MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
+  for (int c = 0; c < f.C; ++c) {
+    const double *s = stats + (r * f.C + c) * 5;
+    ta = mz_combine(ta, MZ{s[0], s[1], s[2]});
+    if (WITH_B) tb = mz_combine(tb, MZ{s[3], s[4], 0.0});
+  }
+  const double A = ta.m + log(ta.z);
+  if (!WITH_B) {
+    lse_out[r] = A;
+    return;
+  }
+  const double B = tb.m + log(tb.z);
+  const double kl = ta.u / ta.z - (A - B);
+  rowres[r * 4 + 0] = A;
+  rowres[r * 4 + 1] = B;
+  rowres[r * 4 + 2] = kl;
+  kl_rows[r] = (float)kl;
+}
+
+__device__ __forceinline__ double block_sum_f64(double v, double *lds) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  const int wave = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kThreads / kWave; ++i) t += lds[i];
+  return t;
+}
+
+// Pass 2: per (chunk, row) partial of sum min(exp(a - A), exp(b - B)).
+__global__ __launch_bounds__(kThreads) void ear_kernel(const float *__restrict__ a,
+                                                       const float *__restrict__ b, int64_t rows,
+                                                       int64_t vocab, Fid f,
+                                                       const double *__restrict__ rowres,
+                                                       double *__restrict__ earpart) {
+  __shared__ double lds[kThreads / kWave];
+  const int c = blockIdx.x;
+  const int64_t row = rows - 1 - blockIdx.y;   // reverse of pass 1's order
+  const int64_t beg = (int64_t)c * f.chunk;
+  const int64_t end = std::min<int64_t>(beg + f.chunk, vocab);
+  // a - A is formed as (a - A_hi) - A_lo with A = A_hi + A_lo split into two
+  // floats: the first subtraction is exact wherever p is not negligible, so
+  // the exponent keeps full fp32 accuracy even for logits far from zero.
+  const double Ad = rowres[row * 4 + 0], Bd = rowres[row * 4 + 1];
+  const float Ahi = (float)Ad, Alo = (float)(Ad - (double)Ahi);
+  const float Bhi = (float)Bd, Blo = (float)(Bd - (double)Bhi);
+  const float *ar = a + row * vocab;
+  const float *br = b + row * vocab;
+  double acc = 0.0;
+  if ((vocab & 3) == 0) {
+    const float4 *a4 = reinterpret_cast<const float4 *>(ar);
+    const float4 *b4 = reinterpret_cast<const float4 *>(br);
+    for (int64_t i = beg / 4 + threadIdx.x; i < end / 4; i += kThreads) {
+      const float4 va = a4[i], vb = b4[i];
+      const float p0 = fast_exp((va.x - Ahi) - Alo), q0 = fast_exp((vb.x - Bhi) - Blo);
+      const float p1 = fast_exp((va.y - Ahi) - Alo), q1 = fast_exp((vb.y - Bhi) - Blo);
+      const float p2 = fast_exp((va.z - Ahi) - Alo), q2 = fast_exp((vb.z - Bhi) - Blo);
+      const float p3 = fast_exp((va.w - Ahi) - Alo), q3 = fast_exp((vb.w - Bhi) - Blo);
+      acc += (double)((fminf(p0, q0) + fminf(p1, q1)) + (fminf(p2, q2) + fminf(p3, q3)));
+    }
+  } else {
+    for (int64_t i = beg + threadIdx.x; i < end; i += kThreads) {
+      const float p = fast_exp((ar[i] - Ahi) - Alo), q = fast_exp((br[i] - Bhi) - Blo);
+      acc += (double)fminf(p, q);
+    }
+  }
+  const double t = block_sum_f64(acc, lds);
+  if (threadIdx.x == 0) earpart[row * f.C + c] = t;
+}
+
+// Per row EAR, then the two means; one workgroup, fixed order.
+__global__ __launch_bounds__(kThreads) void final_kernel(const double *__restrict__ earpart,
+                                                         const double *__restrict__ rowres,
+                                                         int64_t rows, Fid f,
+                                                         float *__restrict__ ear_rows,
+                                                         double *__restrict__ means) {
+  __shared__ double lds[kThreads / kWave];
+  double se = 0.0, sk = 0.0;
+  for (int64_t r = threadIdx.x; r < rows; r += kThreads) {
+    double e = 0.0;
+    for (int c = 0; c < f.C; ++c) e += earpart[r * f.C + c];
+    ear_rows[r] = (float)e;
+    se += e;
+    sk += rowres[r * 4 + 2];
+  }
+  const double te = block_sum_f64(se, lds);
+  const double tk = block_sum_f64(sk, lds);
+  if (threadIdx.x == 0) {
+    means[0] = rows > 0 ? te / (double)rows : 0.0;
+    means[1] = rows > 0 ? tk / (double)rows : 0.0;
+  }
+}
+
+}  // namespace
+
+size_t fidelity_workspace(int64_t rows, int64_t vocab) {
+  if (rows <= 0 || vocab <= 0) return 0;
+  return ws_doubles(rows, fid_plan(rows, vocab)) * sizeof(double);
+}
+
+hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *lse, void *ws,
+                          hipStream_t s) {
+  const Fid f = fid_plan(rows, vocab);
+  double *stats = static_cast<double *>(ws);
+  hipLaunchKernelGGL((stats_kernel<false>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a,
+                     nullptr, vocab, f, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, stats, rows, f, nullptr, lse, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab, float *ear,
+                         float *kl, double *means, void *ws, hipStream_t s) {
+  const Fid f = fid_plan(rows, vocab);
+  double *stats = static_cast<double *>(ws);
+  double *rowres = stats + (size_t)rows * f.C * 5;
+  double *earpart = rowres + (size_t)rows * 4;
+  hipLaunchKernelGGL((stats_kernel<true>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
+                     vocab, f, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rows_kernel<true>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, stats, rows, f, rowres, nullptr, kl);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(ear_kernel, dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b, rows,
+                     vocab, f, rowres, earpart);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(final_kernel, dim3(1), dim3(kThreads), 0, s, earpart, rowres, rows, f, ear,
+                     means);
+  return hipGetLastError();
+}
+
+}  // namespace slq

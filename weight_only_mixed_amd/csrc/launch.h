@@ -1,0 +1,44 @@
+// Internal launchers behind the C ABI (host code; arguments already validated).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace slq {
+
+// quantize.hip
+hipError_t launch_quantize_pack(const float *W, int64_t n, int64_t k, int bits, bool symmetric,
+                                uint32_t *codes, float *scales, uint8_t *zeros, hipStream_t s);
+hipError_t launch_dequantize(const uint32_t *codes, const float *scales, const uint8_t *zeros,
+                             int64_t n, int64_t k, int bits, float *out, hipStream_t s);
+size_t quant_error_workspace(int64_t n, int64_t k);
+hipError_t launch_quant_error(const float *W, const uint32_t *codes, const float *scales,
+                              const uint8_t *zeros, int64_t n, int64_t k, int bits, double *out,
+                              void *ws, hipStream_t s);
+
+// gemv.hip (decode, m <= 64)
+struct GemvPlan {
+  int mt;          // 16-row tiles of x
+  int nblocks;     // workgroups along n (64 rows each)
+  int ksplits;     // workgroups along k
+  size_t ws_bytes; // partial sums + counters
+};
+GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);
+hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const float *scales,
+                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, int bits, float *y,
+                       void *ws, const GemvPlan &plan, hipStream_t s);
+
+// gemm.hip (prefill, m > 64)
+size_t gemm_workspace(int64_t m, int64_t n, int64_t k, int bits);
+hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const float *scales,
+                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, int bits, float *y,
+                       void *ws, hipStream_t s);
+
+// fidelity.hip
+size_t fidelity_workspace(int64_t rows, int64_t vocab);
+hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *lse, void *ws,
+                          hipStream_t s);
+hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab, float *ear,
+                         float *kl, double *means, void *ws, hipStream_t s);
+
+}  // namespace slq

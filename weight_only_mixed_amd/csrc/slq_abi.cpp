@@ -1,0 +1,231 @@
+// C ABI of libslq: argument validation on the host, then the HIP launchers.
+// Every check runs before the first HIP call, so an invalid request returns
+// SLQ_EINVAL / SLQ_ENOTSUP with nothing enqueued and outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/slq.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kGroupSize = 128;                 // group size the kernels are built for
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // kernels index rows/cols with int
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+slq_status from_hip(hipError_t e) { return e == hipSuccess ? SLQ_OK : SLQ_EHIP; }
+
+bool dims_ok(int64_t n, int64_t k) {
+  return n >= 0 && k >= 0 && n < kMaxDim && k < kMaxDim && (n == 0 || k <= ((int64_t)1 << 50) / n);
+}
+
+struct PackedSizes {
+  size_t codes, scales, zeros;
+};
+
+PackedSizes sizes_of(int64_t n, int64_t k, int bits, int group) {
+  PackedSizes s;
+  s.codes = (size_t)(n * k / 8 * bits);
+  s.scales = (size_t)(n * (k / group)) * sizeof(float);
+  s.zeros = (size_t)(n * (k / group));
+  return s;
+}
+
+// Shape, bit-width, group, pointers and alignment of a packed weight.
+slq_status check_packed(const slq_packed *w, PackedSizes *sz) {
+  if (!w) return SLQ_EINVAL;
+  if (w->bits < 2 || w->bits > 8) return SLQ_EINVAL;
+  if (w->group <= 0) return SLQ_EINVAL;
+  if (w->group != kGroupSize) return SLQ_ENOTSUP;
+  if (!dims_ok(w->n, w->k) || w->k % w->group != 0) return SLQ_EINVAL;
+  *sz = sizes_of(w->n, w->k, w->bits, w->group);
+  if (w->n * w->k > 0) {
+    if (!w->codes || !w->scales || !w->zeros) return SLQ_EINVAL;
+    if (!aligned(w->codes, 16) || !aligned(w->scales, 4)) return SLQ_EINVAL;
+    if (overlap(w->codes, sz->codes, w->scales, sz->scales) ||
+        overlap(w->codes, sz->codes, w->zeros, sz->zeros) ||
+        overlap(w->scales, sz->scales, w->zeros, sz->zeros))
+      return SLQ_EINVAL;
+  }
+  return SLQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t slq_codes_bytes(int64_t n, int64_t k, int bits) {
+  if (bits < 2 || bits > 8 || !dims_ok(n, k) || k % 32 != 0) return 0;
+  return (size_t)(n * k / 8 * bits);
+}
+
+slq_status slq_quantize_pack(const float *W, int64_t n, int64_t k, int bits, int group,
+                             slq_grid grid, slq_packed *out, slq_stream stream) {
+  if (!out) return SLQ_EINVAL;
+  if (bits < 2 || bits > 8) return SLQ_EINVAL;
+  if (group <= 0) return SLQ_EINVAL;
+  if (group != kGroupSize) return SLQ_ENOTSUP;
+  if (grid != SLQ_ASYM && grid != SLQ_SYM) return SLQ_EINVAL;
+  if (!dims_ok(n, k) || k % group != 0) return SLQ_EINVAL;
+  const PackedSizes sz = sizes_of(n, k, bits, group);
+  if (n * k > 0) {
+    if (!W || !out->codes || !out->scales || !out->zeros) return SLQ_EINVAL;
+    if (!aligned(W, 16) || !aligned(out->codes, 16) || !aligned(out->scales, 4)) return SLQ_EINVAL;
+    const size_t wb = (size_t)(n * k) * sizeof(float);
+    if (overlap(W, wb, out->codes, sz.codes) || overlap(W, wb, out->scales, sz.scales) ||
+        overlap(W, wb, out->zeros, sz.zeros) || overlap(out->codes, sz.codes, out->scales, sz.scales) ||
+        overlap(out->codes, sz.codes, out->zeros, sz.zeros) ||
+        overlap(out->scales, sz.scales, out->zeros, sz.zeros))
+      return SLQ_EINVAL;
+  }
+  out->bits = bits;
+  out->group = group;
+  out->n = n;
+  out->k = k;
+  if (n * k == 0) return SLQ_OK;
+  return from_hip(slq::launch_quantize_pack(W, n, k, bits, grid == SLQ_SYM, out->codes,
+                                            out->scales, out->zeros,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+slq_status slq_dequantize(const slq_packed *w, float *W_deq, slq_stream stream) {
+  PackedSizes sz;
+  slq_status st = check_packed(w, &sz);
+  if (st != SLQ_OK) return st;
+  if (w->n * w->k == 0) return SLQ_OK;
+  const size_t ob = (size_t)(w->n * w->k) * sizeof(float);
+  if (!W_deq || !aligned(W_deq, 16)) return SLQ_EINVAL;
+  if (overlap(W_deq, ob, w->codes, sz.codes) || overlap(W_deq, ob, w->scales, sz.scales) ||
+      overlap(W_deq, ob, w->zeros, sz.zeros))
+    return SLQ_EINVAL;
+  return from_hip(slq::launch_dequantize(w->codes, w->scales, w->zeros, w->n, w->k, w->bits,
+                                         W_deq, static_cast<hipStream_t>(stream)));
+}
+
+size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w) {
+  PackedSizes sz;
+  if (m < 0 || m >= kMaxDim || check_packed(w, &sz) != SLQ_OK) return 0;
+  if (m == 0 || w->n == 0) return 0;
+  if (m <= 64) return slq::gemv_plan(m, w->n, w->k, w->bits).ws_bytes;
+  return slq::gemm_workspace(m, w->n, w->k, w->bits);
+}
+
+slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t m, float *y,
+                            void *workspace, slq_stream stream) {
+  PackedSizes sz;
+  slq_status st = check_packed(w, &sz);
+  if (st != SLQ_OK) return st;
+  if (m < 0 || m >= kMaxDim) return SLQ_EINVAL;
+  if (m == 0 || w->n == 0) return SLQ_OK;
+  const size_t xb = (size_t)(m * w->k) * 2, yb = (size_t)(m * w->n) * sizeof(float);
+  if (!y || !aligned(y, 16)) return SLQ_EINVAL;
+  if (xb > 0 && (!x_bf16 || !aligned(x_bf16, 16))) return SLQ_EINVAL;
+  const size_t wsb = slq_gemm_workspace_bytes(m, w);
+  if (wsb > 0 && (!workspace || !aligned(workspace, 256))) return SLQ_EINVAL;
+  if (overlap(y, yb, x_bf16, xb) || overlap(y, yb, w->codes, sz.codes) ||
+      overlap(y, yb, w->scales, sz.scales) || overlap(y, yb, w->zeros, sz.zeros) ||
+      overlap(y, yb, workspace, wsb) || overlap(workspace, wsb, x_bf16, xb) ||
+      overlap(workspace, wsb, w->codes, sz.codes) ||
+      overlap(workspace, wsb, w->scales, sz.scales) || overlap(workspace, wsb, w->zeros, sz.zeros))
+    return SLQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m <= 64) {
+    const slq::GemvPlan plan = slq::gemv_plan(m, w->n, w->k, w->bits);
+    return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros, m, w->n, w->k,
+                                     w->bits, y, workspace, plan, s));
+  }
+  return from_hip(slq::launch_gemm(x_bf16, w->codes, w->scales, w->zeros, m, w->n, w->k, w->bits,
+                                   y, workspace, s));
+}
+
+size_t slq_ear_kl_workspace_bytes(int64_t rows, int64_t vocab) {
+  if (rows < 0 || vocab < 0 || rows >= kMaxDim || vocab >= kMaxDim) return 0;
+  return slq::fidelity_workspace(rows, vocab);
+}
+
+slq_status slq_row_lse(const float *logits, int64_t rows, int64_t vocab, double *lse,
+                       void *workspace, slq_stream stream) {
+  if (rows < 0 || vocab < 0 || rows >= kMaxDim || vocab >= kMaxDim) return SLQ_EINVAL;
+  if (rows == 0) return SLQ_OK;
+  if (vocab == 0) return SLQ_EINVAL;   // softmax over an empty vocabulary is undefined
+  const size_t lb = (size_t)(rows * vocab) * sizeof(float);
+  const size_t wsb = slq_ear_kl_workspace_bytes(rows, vocab);
+  if (!logits || !lse || !workspace) return SLQ_EINVAL;
+  if (!aligned(logits, 16) || !aligned(lse, 8) || !aligned(workspace, 256)) return SLQ_EINVAL;
+  if (overlap(lse, rows * 8, logits, lb) || overlap(workspace, wsb, logits, lb) ||
+      overlap(workspace, wsb, lse, rows * 8))
+    return SLQ_EINVAL;
+  return from_hip(slq::launch_row_lse(logits, rows, vocab, lse, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+slq_status slq_ear_kl(const float *logits_p, const float *logits_q, int64_t rows, int64_t vocab,
+                      float *ear_rows, float *kl_rows, double *means, void *workspace,
+                      slq_stream stream) {
+  if (rows < 0 || vocab < 0 || rows >= kMaxDim || vocab >= kMaxDim) return SLQ_EINVAL;
+  if (rows == 0) return SLQ_OK;
+  if (vocab == 0) return SLQ_EINVAL;
+  const size_t lb = (size_t)(rows * vocab) * sizeof(float);
+  const size_t rb = (size_t)rows * sizeof(float);
+  const size_t wsb = slq_ear_kl_workspace_bytes(rows, vocab);
+  if (!logits_p || !logits_q || !ear_rows || !kl_rows || !means || !workspace) return SLQ_EINVAL;
+  if (!aligned(logits_p, 16) || !aligned(logits_q, 16) || !aligned(ear_rows, 4) ||
+      !aligned(kl_rows, 4) || !aligned(means, 8) || !aligned(workspace, 256))
+    return SLQ_EINVAL;
+  const void *outs[4] = {ear_rows, kl_rows, means, workspace};
+  const size_t outb[4] = {rb, rb, 2 * sizeof(double), wsb};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], logits_p, lb) || overlap(outs[i], outb[i], logits_q, lb))
+      return SLQ_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return SLQ_EINVAL;
+  }
+  return from_hip(slq::launch_ear_kl(logits_p, logits_q, rows, vocab, ear_rows, kl_rows, means,
+                                     workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t slq_quant_error_workspace_bytes(const slq_packed *w) {
+  PackedSizes sz;
+  if (check_packed(w, &sz) != SLQ_OK) return 0;
+  return slq::quant_error_workspace(w->n, w->k);
+}
+
+slq_status slq_quant_error(const float *W, const slq_packed *w, double *out, void *workspace,
+                           slq_stream stream) {
+  PackedSizes sz;
+  slq_status st = check_packed(w, &sz);
+  if (st != SLQ_OK) return st;
+  if (!out || !aligned(out, 8)) return SLQ_EINVAL;
+  const size_t wb = (size_t)(w->n * w->k) * sizeof(float);
+  const size_t wsb = slq_quant_error_workspace_bytes(w);
+  if (wb > 0 && (!W || !aligned(W, 16))) return SLQ_EINVAL;
+  if (wsb > 0 && (!workspace || !aligned(workspace, 256))) return SLQ_EINVAL;
+  if (overlap(out, 16, W, wb) || overlap(out, 16, workspace, wsb) ||
+      overlap(workspace, wsb, W, wb) || overlap(out, 16, w->codes, sz.codes) ||
+      overlap(out, 16, w->scales, sz.scales) || overlap(out, 16, w->zeros, sz.zeros) ||
+      overlap(workspace, wsb, w->codes, sz.codes) || overlap(workspace, wsb, w->scales, sz.scales) ||
+      overlap(workspace, wsb, w->zeros, sz.zeros))
+    return SLQ_EINVAL;
+  return from_hip(slq::launch_quant_error(W, w->codes, w->scales, w->zeros, w->n, w->k, w->bits,
+                                          out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+const char *slq_strerror(slq_status s) {
+  switch (s) {
+    case SLQ_OK: return "ok";
+    case SLQ_EINVAL: return "invalid argument (size, bit-width, pointer, alignment or aliasing)";
+    case SLQ_ENOTSUP: return "unsupported request (group size other than 128)";
+    case SLQ_EHIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"
