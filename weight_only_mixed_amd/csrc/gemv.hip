@@ -146,188 +146,251 @@ __device__ __forceinline__ uint32_t x_pair(const uint32_t (&X)[16], int j) {
   return perm(X[b / 2], X[a / 2], halves_sel(a % 2, b % 2));
 }
 
-template <int BITS, int MT, int NT>
+// Activation fragments for one 32-code chunk in pair order: 4 MFMA A operands
+// of 4 bf16 pairs each (16 words).
+template <int BITS>
+__device__ __forceinline__ void x_fragments(const uint32_t (&X)[16], uint32_t (&F)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) F[j] = x_pair<BITS>(X, j);
+}
+
+// Workgroup: 4 wavefronts on the same 16*NT rows, each taking a contiguous
+// quarter of the workgroup's k-block.  The activations of the k-block are
+// staged once in LDS, already permuted into MFMA fragment order.  Each wave
+// streams its groups in batches of B with the next batch's loads issued
+// before the current batch is consumed (two register buffers), so every lane
+// keeps up to 2*B*NT chunk loads in flight.  The four partial sums meet in
+// LDS; with several k-blocks the workgroup partials go to the workspace and
+// the last workgroup of each row block adds them in k-block order.
+template <int BITS, int NT, int B>
+struct Batch {
+  Chunk<BITS> c[B][NT];
+};
+
+template <int BITS, int MT, int NT, int B>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    int ksplits, float *__restrict__ y, float *__restrict__ partial,
+    int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
     unsigned *__restrict__ tickets) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int col = lane & 15, kq = lane >> 4;
   const int G = K / kGroup;
-  const int split = blockIdx.y;
-  const int g0 = (int)((int64_t)split * G / ksplits);
-  const int g1 = (int)((int64_t)(split + 1) * G / ksplits);
-  const int nbase = blockIdx.x * (kWaves * 16 * NT) + wave * (16 * NT);
-  const int64_t wpr = (int64_t)K * BITS / 32;   // words per row
+  const int kb = blockIdx.y;
+  const int gbase = kb * GW;
+  const int gcount = min(GW, G - gbase);        // groups in this k-block
+  const int xpitch = gcount * 64 + 4;           // words per activation row (+16 B vs bank conflicts)
+  const int n0 = blockIdx.x * 16 * NT;
+  const int64_t wpr = (int64_t)K * BITS / 32;
+
+  // ---- stage activations [M][gcount*128] into LDS in fragment order ----
+  for (int i = threadIdx.x; i < M * gcount * 4; i += kThreads) {
+    const int m = i / (gcount * 4), c = i % (gcount * 4);
+    const u32x4_t *src =
+        reinterpret_cast<const u32x4_t *>(x + (int64_t)m * K + (int64_t)gbase * kGroup + 32 * c);
+    uint32_t X[16], F[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4_t v = src[q];
+      X[4 * q + 0] = v[0];
+      X[4 * q + 1] = v[1];
+      X[4 * q + 2] = v[2];
+      X[4 * q + 3] = v[3];
+    }
+    x_fragments<BITS>(X, F);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(lds + m * xpitch + c * 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
+  }
+
+  // ---- stage the workgroup's scales and zero points [16*NT rows][gcount] ----
+  // The [n][G] layout makes each row's run contiguous; one coalesced pass
+  // replaces many scattered 4-byte and 1-byte loads per row and group.
+  float2 *meta = reinterpret_cast<float2 *>(lds + M * xpitch);
+  for (int i = threadIdx.x; i < 16 * NT * gcount; i += kThreads) {
+    const int r = i / gcount, gl = i % gcount;
+    const int n = min(n0 + r, N - 1);
+    const int64_t o = (int64_t)n * G + gbase + gl;
+    meta[i] = make_float2(scales[o], (float)zeros[o]);
+  }
+
+  // this wave's local group range [ga, gz)
+  const int per = (gcount + kWaves - 1) / kWaves;
+  const int ga = min(gcount, wave * per), gz = min(gcount, ga + per);
 
   const uint32_t *crow[NT];
-  const float *srow[NT];
-  const uint8_t *zrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int n = min(nbase + 16 * t + col, N - 1);   // rows past N are read, never stored
-    crow[t] = codes + (int64_t)n * wpr + kq * BITS;
-    srow[t] = scales + (int64_t)n * G;
-    zrow[t] = zeros + (int64_t)n * G;
+    const int n = min(n0 + 16 * t + col, N - 1);   // rows past N are read, never stored
+    crow[t] = codes + (int64_t)n * wpr + (int64_t)gbase * 4 * BITS + kq * BITS;
   }
-  const uint16_t *xrow[MT];
-  bool xvalid[MT];
+  // Loads are unconditional (group index clamped to the wave's last group) so
+  // that the two batch buffers stay in flight across the loop back-edge.
+  auto load = [&](Batch<BITS, NT, B> &bt, int g) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + col;
-    xvalid[mt] = m < M;
-    xrow[mt] = x + (int64_t)(xvalid[mt] ? m : 0) * K + kq * 32;
-  }
+    for (int j = 0; j < B; ++j) {
+      const int gg = min(g + j, gz - 1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) bt.c[j][t] = load_chunk<BITS>(crow[t] + (int64_t)gg * 4 * BITS);
+    }
+  };
 
+  const u32x4_t unit = (BITS == 8) ? u32x4_t{kOne2, kOne2, kOne2, kOne2}
+                                   : u32x4_t{kMagic2, kMagic2, kMagic2, kMagic2};
   f32x4_t acc[NT][MT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const u32x4_t unit = (BITS == 8) ? u32x4_t{kOne2, kOne2, kOne2, kOne2}
-                                   : u32x4_t{kMagic2, kMagic2, kMagic2, kMagic2};
-
-  struct Loads {
-    Chunk<BITS> c[NT];
-    float s[NT];
-    uint32_t z[NT];
-    uint32_t X[MT][16];
-  };
-  auto issue = [&](int g, Loads &L) {
+  auto compute = [&](const Batch<BITS, NT, B> &bt, int g) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      L.c[t] = load_chunk<BITS>(crow[t] + (int64_t)g * 4 * BITS);
-      L.s[t] = srow[t][g];
-      L.z[t] = zrow[t][g];
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (xvalid[mt]) {
-        const u32x4_t *px = reinterpret_cast<const u32x4_t *>(xrow[mt] + (int64_t)g * kGroup);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4_t v = px[i];
-          L.X[mt][4 * i + 0] = v[0];
-          L.X[mt][4 * i + 1] = v[1];
-          L.X[mt][4 * i + 2] = v[2];
-          L.X[mt][4 * i + 3] = v[3];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) L.X[mt][i] = 0u;
-      }
-    }
-  };
-
-  Loads cur, nxt;
-  if (g0 < g1) issue(g0, cur);
-  for (int g = g0; g < g1; ++g) {
-    if (g + 1 < g1) issue(g + 1, nxt);
-
-    u32x4_t A[MT][4];
-    f32x4_t S[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        A[mt][r] = u32x4_t{x_pair<BITS>(cur.X[mt], 4 * r + 0), x_pair<BITS>(cur.X[mt], 4 * r + 1),
-                           x_pair<BITS>(cur.X[mt], 4 * r + 2), x_pair<BITS>(cur.X[mt], 4 * r + 3)};
-      S[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[mt] = mfma16(A[mt][r], unit, S[mt]);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      uint32_t p[16];
-      unpack_pairs<BITS>(cur.c[t], p);
-      const float s = cur.s[t];
-      const float zf = (float)cur.z[t];
+    for (int j = 0; j < B; ++j) {
+      const int gl = g + j;
+      if (gl >= gz) break;
+      u32x4_t A[MT][4];
+      f32x4_t S[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4_t C = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int m = 16 * mt + col;
+        if (m < M) {
+          const u32x4_t *src =
+              reinterpret_cast<const u32x4_t *>(lds + m * xpitch + (gl * 4 + kq) * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          C = mfma16(A[mt][r], u32x4_t{p[4 * r], p[4 * r + 1], p[4 * r + 2], p[4 * r + 3]}, C);
+          for (int r = 0; r < 4; ++r) A[mt][r] = src[r];
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float tv;
-          if constexpr (BITS == 8) {
-            tv = fmaf(-zf, S[mt][v], C[v]);
-          } else {
-            tv = fmaf(-zf * 0.0078125f, S[mt][v], C[v] - S[mt][v]);
+          for (int r = 0; r < 4; ++r) A[mt][r] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        S[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[mt] = mfma16(A[mt][r], unit, S[mt]);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        uint32_t p[16];
+        unpack_pairs<BITS>(bt.c[j][t], p);
+        const float2 sz = meta[(16 * t + col) * gcount + gl];
+        const float s = sz.x;
+        const float zf = sz.y;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4_t C = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            C = mfma16(A[mt][r], u32x4_t{p[4 * r], p[4 * r + 1], p[4 * r + 2], p[4 * r + 3]}, C);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float tv;
+            if constexpr (BITS == 8) {
+              tv = fmaf(-zf, S[mt][v], C[v]);
+            } else {
+              tv = fmaf(-zf * 0.0078125f, S[mt][v], C[v] - S[mt][v]);
+            }
+            acc[t][mt][v] = fmaf(s, tv, acc[t][mt][v]);
           }
-          acc[t][mt][v] = fmaf(s, tv, acc[t][mt][v]);
         }
       }
     }
-    if (g + 1 < g1) cur = nxt;
-  }
+  };
 
-  // Lane holds y rows m = 16*mt + 4*kq + v, column n = nbase + 16*t + col.
-  if (ksplits == 1) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int n = nbase + 16 * t + col;
-      if (n >= N) continue;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = 16 * mt + 4 * kq + v;
-          if (m < M) y[(int64_t)m * N + n] = acc[t][mt][v];
-        }
+  // Ring of two batch buffers: both are filled before the staging barrier, and
+  // each is refilled (two batches ahead) as soon as it has been consumed.
+  Batch<BITS, NT, B> b0, b1;
+  if (ga < gz) {
+    load(b0, ga);
+    load(b1, ga + B);
+  }
+  __syncthreads();   // activations staged
+  if (ga < gz) {
+    for (int g = ga;;) {
+      compute(b0, g);
+      load(b0, g + 2 * B);
+      g += B;
+      if (g >= gz) break;
+      compute(b1, g);
+      load(b1, g + 2 * B);
+      g += B;
+      if (g >= gz) break;
     }
-    return;
   }
 
-  float *mypart = partial + (int64_t)split * M * N;
+  // ---- reduce the 4 waves' partials in LDS (reusing the activation area) ----
+  __syncthreads();
+  f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int n = nbase + 16 * t + col;
-    if (n >= N) continue;
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) red[((wave * NT + t) * MT + mt) * kWave + lane] = acc[t][mt];
+  __syncthreads();
+  // wave w sums the (t, mt) tiles with (t * MT + mt) % 4 == w, adding waves in order
+  for (int e = wave; e < NT * MT; e += kWaves) {
+    const int t = e / MT, mt = e % MT;
+    f32x4_t sum = red[(t * MT + mt) * kWave + lane];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 16 * mt + 4 * kq + v;
-        if (m < M) mypart[(int64_t)m * N + n] = acc[t][mt][v];
+    for (int w = 1; w < kWaves; ++w) sum += red[((w * NT + t) * MT + mt) * kWave + lane];
+    const int n = n0 + 16 * t + col;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * mt + 4 * kq + v;
+      if (m >= M || n >= N) continue;
+      if (ksplits == 1) {
+        y[(int64_t)m * N + n] = sum[v];
+      } else {
+        // device-scope store: coherent across XCDs without an L2 writeback
+        __hip_atomic_store(&partial[((int64_t)kb * M + m) * N + n], sum[v], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
+    }
   }
-  __threadfence();
+  if (ksplits == 1) return;
+  // every partial store has completed (device scope) before the ticket is taken
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   __shared__ unsigned last;
   if (threadIdx.x == 0) {
-    const unsigned ticket = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_ACQ_REL,
+    const unsigned ticket = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
     last = (ticket == (unsigned)ksplits - 1u);
   }
   __syncthreads();
   if (!last) return;
-  __threadfence();
-  const int rows = kWaves * 16 * NT;
-  const int n0 = blockIdx.x * rows;
+  const int rows = 16 * NT;
   for (int i = threadIdx.x; i < M * rows; i += kThreads) {
     const int m = i / rows, n = n0 + i % rows;
     if (n >= N) continue;
     float sum = 0.f;
-    for (int sp = 0; sp < ksplits; ++sp) sum += partial[((int64_t)sp * M + m) * N + n];
+    for (int sp = 0; sp < ksplits; ++sp)
+      sum += __hip_atomic_load(&partial[((int64_t)sp * M + m) * N + n], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     y[(int64_t)m * N + n] = sum;
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kNT = 2;   // 16-row tiles per wavefront
 // Split-K tickets live in a fixed area at the start of the workspace, so no
 // call's partial sums ever overlap another call's tickets; every completed
 // call leaves all tickets at zero.
 constexpr size_t kTicketBytes = 65536;
 constexpr int64_t kMaxTicketBlocks = kTicketBytes / sizeof(unsigned);
 
-template <int BITS, int MT>
+// LDS: the activation tile [m][groups*128] in fragment order, reused for the
+// cross-wave reduction.
+size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw) {
+  const size_t xs = (size_t)m * (gw * 64 + 4) * 4;
+  const size_t meta = (size_t)16 * nt * gw * 8;
+  const size_t red = (size_t)kWaves * nt * mt * kWave * 16;
+  return std::max(xs + meta, red) + 16;
+}
+constexpr size_t kLdsBudget = 65536;   // activation bytes per workgroup
+// Dynamic LDS ceiling per workgroup: activations (<= 64 KiB + pitch padding)
+// plus scales/zero points (<= 32 KiB), or the reduction area (<= 64 KiB).
+constexpr size_t kMaxDynLds = 128 * 1024;
+
+template <int BITS, int MT, int NT, int B>
 hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *scales,
                        const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                        const GemvPlan &plan, hipStream_t st) {
@@ -337,10 +400,33 @@ hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *sc
     tickets = static_cast<unsigned *>(ws);
     partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
   }
-  hipLaunchKernelGGL((gemv_kernel<BITS, MT, kNT>), dim3(plan.nblocks, plan.ksplits),
-                     dim3(kThreads), 0, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
-                     plan.ksplits, y, partial, tickets);
+  const size_t lds = gemv_lds_bytes(m, MT, NT, plan.gw);
+  if (lds > kMaxDynLds) return hipErrorInvalidValue;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+  if (attr != hipSuccess) {
+    (void)hipGetLastError();   // leave no sticky error behind for later calls
+    return attr;
+  }
+  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B>), dim3(plan.nblocks, plan.ksplits),
+                     dim3(kThreads), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
+                     plan.gw, plan.ksplits, y, partial, tickets);
   return hipGetLastError();
+}
+
+// Groups per load batch: NT * B = 4 chunk loads per batch per lane, two
+// batches in flight.
+template <int BITS, int MT>
+hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *scales,
+                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
+                      const GemvPlan &plan, hipStream_t st) {
+  switch (plan.nt) {
+    case 1: return gemv_launch<BITS, MT, 1, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 2: return gemv_launch<BITS, MT, 2, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 4: return gemv_launch<BITS, MT, 4, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int BITS>
@@ -348,10 +434,10 @@ hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const float *scal
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      const GemvPlan &plan, hipStream_t st) {
   switch (plan.mt) {
-    case 1: return gemv_launch<BITS, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 2: return gemv_launch<BITS, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 3: return gemv_launch<BITS, 3>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 4: return gemv_launch<BITS, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 1: return gemv_shape<BITS, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 2: return gemv_shape<BITS, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 3: return gemv_shape<BITS, 3>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 4: return gemv_shape<BITS, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -362,21 +448,31 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   (void)bits;
   GemvPlan p;
   p.mt = (int)((m + 15) / 16);
-  const int64_t rows = kWaves * 16 * kNT;
-  p.nblocks = (int)((n + rows - 1) / rows);
   const int64_t G = k / kGroup;
-  // Enough workgroups to cover 256 CUs about twice, at least 2 groups per
-  // split, and partial sums kept small next to the weight bytes.
-  int64_t ks = (512 + p.nblocks - 1) / p.nblocks;
-  ks = std::min<int64_t>(ks, std::max<int64_t>(1, G / 2));
-  ks = std::min<int64_t>(ks, 16);
-  if (p.nblocks > kMaxTicketBlocks) ks = 1;
-  p.ksplits = (int)std::max<int64_t>(1, ks);
-  if (p.ksplits > 1) {
-    p.ws_bytes = kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float);
-  } else {
-    p.ws_bytes = 0;
+  // Fewest k-blocks such that the activations of a k-block fit the LDS budget
+  // and about 256 workgroups (one per CU) exist; widest row tiles first (they
+  // amortize the activation staging).
+  const int64_t gw_max = std::max<int64_t>(1, (int64_t)kLdsBudget / (std::max<int64_t>(m, 1) * 256));
+  const int64_t ks_min = std::max<int64_t>(1, (G + gw_max - 1) / gw_max);
+  const int64_t target = 256;
+  p.nt = 1;
+  for (int nt : {4, 2, 1}) {
+    if (nt * p.mt > 8) continue;   // register budget
+    if (m <= 4 && nt > 1) continue;   // tiny activations: occupancy matters more
+    const int64_t nb = (n + 16 * nt - 1) / (16 * nt);
+    if (nb * ks_min >= target || nt == 1) {
+      p.nt = nt;
+      break;
+    }
   }
+  const int64_t nb = (n + 16 * p.nt - 1) / (16 * p.nt);
+  int64_t ks = std::max<int64_t>(ks_min, (target + nb - 1) / nb);
+  ks = std::min<int64_t>(ks, std::max<int64_t>(1, G));
+  p.gw = (int)std::max<int64_t>(1, (G + ks - 1) / ks);
+  p.ksplits = (int)std::max<int64_t>(1, (G + p.gw - 1) / p.gw);
+  p.nblocks = (int)nb;
+  if (p.nblocks > kMaxTicketBlocks && p.ksplits > 1) p.ksplits = 0;   // not supported
+  p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
   return p;
 }
 

@@ -19,9 +19,11 @@ hipError_t launch_quant_error(const float *W, const uint32_t *codes, const float
 // gemv.hip (decode, m <= 64)
 struct GemvPlan {
   int mt;          // 16-row tiles of x
-  int nblocks;     // workgroups along n (64 rows each)
-  int ksplits;     // workgroups along k
-  size_t ws_bytes; // partial sums + counters
+  int nt;          // 16-row weight tiles per workgroup
+  int gw;          // 128-groups per k-block (workgroup)
+  int nblocks;     // workgroups along n
+  int ksplits;     // workgroups along k (0: shape not supported)
+  size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);
 hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const float *scales,

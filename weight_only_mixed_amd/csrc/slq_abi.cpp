@@ -139,6 +139,7 @@ slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (m <= 64) {
     const slq::GemvPlan plan = slq::gemv_plan(m, w->n, w->k, w->bits);
+    if (plan.ksplits == 0) return SLQ_ENOTSUP;
     return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros, m, w->n, w->k,
                                      w->bits, y, workspace, plan, s));
   }
