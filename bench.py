@@ -52,6 +52,35 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "slq_device.h"):
+        with open(os.path.join(ROOT, "weight_only_mixed_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/gemv_traffic.txt), or None when it was taken for another kernel
+    or an older version of the decode kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemv_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel") != kernel or kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 class Timer:
     def __init__(self, torch):
         self.torch = torch
@@ -78,6 +107,9 @@ def main():
                     "quantize,gemm,stack,fidelity,gamma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slots", type=int, default=2)
+    ap.add_argument("--pmc", default=None, metavar="KERNEL",
+                    help="counter mode: 5 copies of 256 MiB (known bytes), then 10 passes over the "
+                         "sweep points that launch KERNEL; prints what ran and exits")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -128,6 +160,24 @@ def main():
     ws_bytes = max(slq.gemm_workspace_bytes(m, packs[0][pi]) for pi, (_, n, k, b, m) in enumerate(points))
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+    if args.pmc:
+        src = torch.empty(256 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        sel = [pi for pi, (_, n, k, b, m) in enumerate(points) if slq.kernel_name(m, packs[0][pi]) == args.pmc]
+        for _ in range(10):
+            for pi in sel:
+                name, n, k, bits, m = points[pi]
+                slq.slq_dequant_gemm(xs[(m, k)], packs[_ % R][pi], y=ys[pi], ws=ws)
+        torch.cuda.synchronize()
+        nb = [alg_bytes(points[pi][4], points[pi][1], points[pi][2], points[pi][3]) for pi in sel]
+        print(json.dumps({"pmc_kernel": args.pmc, "points": len(sel), "launches": 10 * len(sel),
+                          "alg_bytes_per_launch": sum(nb) // max(1, len(nb)),
+                          "copy_bytes_each": 2 * 256 * 2**20, "copies": 5,
+                          "source_digest": source_digest()}))
+        return
     log(f"bench: sweep ready in {time.time() - t0:.1f}s "
         f"({sum(p.nbytes for p in packs[0]) / 1e6:.0f} MB packed per slot, {R} slots)")
 
@@ -164,7 +214,7 @@ def main():
     value = sweep_bytes / (step_ms * 1e-3) / 1e9
     log(f"bench: sweep step {step_ms * 1e3:.1f} us, {value:.1f} GB/s packed weights")
 
-    # per-launch durations (HIP events around each launch, CPU kept ahead)
+    # per-point event pairs (include ~2-4 us of dispatch latency per launch)
     per_point_ms = [[] for _ in points]
     for rep in range(3):
         evs = []
@@ -185,35 +235,52 @@ def main():
     by_kernel = {}
     for pi, (name, n, k, bits, m) in enumerate(points):
         ms = float(np.median(per_point_ms[pi]))
-        mt = (m + 15) // 16
-        kname = f"slq::gemv_kernel<{bits}, {mt}, 2>"
-        d = by_kernel.setdefault(kname, {"ms": 0.0, "bytes": 0, "launches": 0, "wbytes": 0})
-        d["ms"] += ms
-        d["bytes"] += alg_bytes(m, n, k, bits)
-        d["wbytes"] += packed_bytes(n, k, bits)
-        d["launches"] += 1
-        point_rows.append({"shape": name, "n": n, "k": k, "bits": bits, "m": m,
-                           "us": round(ms * 1e3, 2),
-                           "GBps_packed": round(packed_bytes(n, k, bits) / (ms * 1e-3) / 1e9, 1)})
-    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
-    avg_us = dom["ms"] / dom["launches"] * 1e3
-    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        kname = slq.kernel_name(m, packs[0][pi])
+        d = by_kernel.setdefault(kname, {"pts": [], "event_ms": 0.0})
+        d["pts"].append(pi)
+        d["event_ms"] += ms
+        point_rows.append({"shape": name, "n": n, "k": k, "bits": bits, "m": m, "kernel": kname,
+                           "event_us": round(ms * 1e3, 2)})
+
+    # Average launch duration of one kernel instance: a HIP graph holding all of
+    # its sweep launches over every rotation slot (kernels run back to back, as
+    # in the step graph), events around 5 replays.
+    def instance_time(kname):
+        pts = by_kernel[kname]["pts"]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for r in range(R):
+                for pi in pts:
+                    name, n, k, bits, m = points[pi]
+                    slq.slq_dequant_gemm(xs[(m, k)], packs[r][pi], y=ys[pi], ws=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        with Timer(torch) as T:
+            for _ in range(5):
+                g.replay()
+        launches = 5 * R * len(pts)
+        nbytes = 5 * R * sum(alg_bytes(points[pi][4], points[pi][1], points[pi][2], points[pi][3]) for pi in pts)
+        return T.ms / launches, nbytes / launches
+
+    dom_name = max(by_kernel, key=lambda kn: by_kernel[kn]["event_ms"])
+    dom_ms, dom_bytes = instance_time(dom_name)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "avg_launch_us": round(avg_us, 2),
-                "alg_bytes_per_launch": dom["bytes"] // dom["launches"],
-                "launches": dom["launches"]}
-    kernel_sum_ms = sum(min(v) for v in per_point_ms)
+                "traffic": measured_traffic(dom_name), "avg_launch_us": round(dom_ms * 1e3, 3),
+                "alg_bytes_per_launch": int(dom_bytes),
+                "launches_per_replay": R * len(by_kernel[dom_name]["pts"]),
+                "timing": "HIP graph of this instance's sweep launches over all rotation slots, "
+                          "events around 5 replays"}
 
     rows = {"decode_sweep": {
         "GBps_packed_step": round(value, 1),
-        "GBps_packed_kernels": round(sweep_bytes / (sum(float(np.median(v)) for v in per_point_ms) * 1e-3) / 1e9, 1),
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "points": point_rows}}
 
     # free sweep copies beyond slot 0 before the other rows
     del graphs
-    packs = packs[:1]
+    packs = packs[:1]   # other rows need only one copy
     torch.cuda.empty_cache()
 
     # ---------------- quantize + pack ----------------
@@ -374,28 +441,32 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         log("bench: timing the CPU oracle on a sample of the sweep")
-        sample = [(name, n, k, bits, 1) for (name, n, k) in SWEEP_SHAPES for bits in SWEEP_BITS]
-        sample += [("q", 4096, 4096, bits, 16) for bits in SWEEP_BITS]
+        sample = list(points)          # the whole 36-point sweep, in bench order
         qcache = {}
         for (name, n, k, bits, m) in sample:
             if (name, bits) not in qcache:
                 q, s, z = oracle.quantize(W_host[name], bits)
                 qcache[(name, bits)] = (oracle.pack(q, bits), s, z)
-        tb, tt = 0, 0.0
-        for (name, n, k, bits, m) in sample:
-            words, s, z = qcache[(name, bits)]
-            x = S.activations_bf16(m, k, S.seed_for(2, m, k % 97))
-            t1 = time.perf_counter()
-            q = oracle.unpack(words, k, bits)
-            wh = oracle.dequantize(q, s, z)
-            oracle.gemm(x, wh)
-            tt += time.perf_counter() - t1
-            tb += packed_bytes(n, k, bits)
+        tb, tt, npts = 0, 0.0, 0
+        xcache = {}
+        while tt < 10.0 and npts < 3 * len(sample):   # whole passes until >= 10 s of CPU work
+            for (name, n, k, bits, m) in sample:
+                words, s, z = qcache[(name, bits)]
+                if (m, k) not in xcache:
+                    xcache[(m, k)] = S.activations_bf16(m, k, S.seed_for(2, m, k % 97))
+                x = xcache[(m, k)]
+                t1 = time.perf_counter()
+                q = oracle.unpack(words, k, bits)
+                wh = oracle.dequantize(q, s, z)
+                oracle.gemm(x, wh)
+                tt += time.perf_counter() - t1
+                tb += packed_bytes(n, k, bits)
+                npts += 1
         cpu = {"value": round(tb / tt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
                "kind": "oracle", "seconds": round(tt, 2),
-               "sample": "oracle unpack + dequantize + fp64 matmul on the 12 sweep shape x bits "
-                         "points at M=1 plus q 4096x4096 at M=16 for bits {3,4,8}; packed-weight "
-                         "bytes / wall time"}
+               "sample": f"oracle unpack + dequantize + fp64 matmul over {npts // len(sample)} "
+                         f"pass(es) of the full 36-point sweep (same shapes, bits and M as the "
+                         f"GPU step); packed-weight bytes / wall time"}
         log(f"bench: cpu oracle {cpu['value']} GB/s in {tt:.1f}s on {cpu['cores']} threads")
 
     line = {

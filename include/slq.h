@@ -132,6 +132,14 @@ size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w);
 slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t m,
                             float *y, void *workspace, slq_stream stream);
 
+/*
+ * Name of the kernel instance slq_dequant_gemm launches for (m, w), as the
+ * profiler reports it (e.g. "slq::gemv_kernel<4, 1, 1, 4>"), so tools can
+ * match per-kernel statistics to calls.  Static storage; "" on invalid
+ * arguments.
+ */
+const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w);
+
 /* Workspace bytes slq_ear_kl / slq_row_lse need for (rows, vocab). */
 size_t slq_ear_kl_workspace_bytes(int64_t rows, int64_t vocab);
 

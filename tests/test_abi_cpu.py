@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for name in names:
         assert hasattr(L, name), name
 
@@ -88,7 +88,7 @@ def test_dequant_gemm_validation():
     assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, B, None, None) == slq.SLQ_EINVAL  # y aliases codes
     assert L.slq_dequant_gemm(A, None, 1, y, None, None) == slq.SLQ_EINVAL
     # split-K workspace required when the plan uses one
-    big = packed(n=4096, k=4096)
+    big = packed(n=1024, k=4096)
     assert L.slq_gemm_workspace_bytes(1, ctypes.byref(big)) > 0
     assert L.slq_dequant_gemm(A, ctypes.byref(big), 1, y, None, None) == slq.SLQ_EINVAL
     assert L.slq_dequant_gemm(A, ctypes.byref(big), 1, y, E + 0x100000 + 8, None) == slq.SLQ_EINVAL
@@ -122,6 +122,10 @@ def test_sizes_and_strings():
     assert L.slq_gemm_workspace_bytes(1, ctypes.byref(packed(n=1, k=128))) == 0
     assert L.slq_ear_kl_workspace_bytes(512, 151936) > 0
     assert L.slq_quant_error_workspace_bytes(ctypes.byref(packed())) > 0
+    name = L.slq_dequant_gemm_kernel_name(1, ctypes.byref(packed(n=4096, k=4096)))
+    assert name.startswith(b"slq::gemv_kernel<4, 1,")
+    assert L.slq_dequant_gemm_kernel_name(100, ctypes.byref(packed())) == b"slq::gemm_kernel<4>"
+    assert L.slq_dequant_gemm_kernel_name(1, ctypes.byref(packed(bits=9))) == b""
     for s in range(4):
         assert L.slq_strerror(s)
     assert L.slq_strerror(0) == b"ok"

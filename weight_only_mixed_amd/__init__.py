@@ -59,6 +59,8 @@ def lib():
         L.slq_quant_error_workspace_bytes.argtypes = [_pp]
         L.slq_quant_error_workspace_bytes.restype = _sz
         L.slq_quant_error.argtypes = [_vp, _pp, _vp, _vp, _vp]
+        L.slq_dequant_gemm_kernel_name.argtypes = [_i64, _pp]
+        L.slq_dequant_gemm_kernel_name.restype = ctypes.c_char_p
         L.slq_strerror.argtypes = [_int]
         L.slq_strerror.restype = ctypes.c_char_p
         for f in ("slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm", "slq_row_lse",
@@ -153,6 +155,12 @@ def gemm_workspace_bytes(m: int, pw: PackedWeight) -> int:
     return lib().slq_gemm_workspace_bytes(m, ctypes.byref(desc))
 
 
+def kernel_name(m: int, pw: PackedWeight) -> str:
+    """Profiler name of the kernel slq_dequant_gemm launches for (m, pw)."""
+    desc = pw.c()
+    return lib().slq_dequant_gemm_kernel_name(m, ctypes.byref(desc)).decode()
+
+
 def slq_dequant_gemm(x: torch.Tensor, pw: PackedWeight, y: torch.Tensor | None = None,
                      ws: torch.Tensor | None = None) -> torch.Tensor:
     """y[m][n] = x[m][k] . w_hat[n][k]^T with bf16 x, fp32 y."""
@@ -204,5 +212,5 @@ def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
 
 
 __all__ = ["lib", "SlqError", "SlqPacked", "PackedWeight", "alloc_packed", "workspace",
-           "gemm_workspace_bytes", "slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm",
+           "gemm_workspace_bytes", "kernel_name", "slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm",
            "slq_row_lse", "slq_ear_kl", "slq_quant_error", "SLQ_ASYM", "SLQ_SYM", "GROUP"]

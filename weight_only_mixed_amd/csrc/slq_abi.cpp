@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
 
 #include "../../include/slq.h"
 #include "launch.h"
@@ -145,6 +146,20 @@ slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t
   }
   return from_hip(slq::launch_gemm(x_bf16, w->codes, w->scales, w->zeros, m, w->n, w->k, w->bits,
                                    y, workspace, s));
+}
+
+const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
+  static thread_local char buf[64];
+  PackedSizes sz;
+  buf[0] = '\0';
+  if (m <= 0 || m >= kMaxDim || check_packed(w, &sz) != SLQ_OK) return buf;
+  if (m <= 64) {
+    const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
+    snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d>", w->bits, p.mt, p.nt, 4 / p.nt);
+  } else {
+    snprintf(buf, sizeof buf, "slq::gemm_kernel<%d>", w->bits);
+  }
+  return buf;
 }
 
 size_t slq_ear_kl_workspace_bytes(int64_t rows, int64_t vocab) {
