@@ -21,15 +21,24 @@
 //    converted exactly (q <= 255 fits bf16's 8 significant bits) with no offset.
 //  * MACs run on bf16 MFMA 16x16x32 (x as the 16-row A operand, dequantized
 //    weights as B), fp32 accumulate, one chain of 4 MFMAs per group.
-//  * Offset and zero point are removed per group in fp32:
-//       t = (C - S) - z * S / 128,  S = MFMA chain of x against bf16 128.0
-//    S runs the exact instruction sequence C runs for an all-zero group, so
-//    C - S is exactly 0 there and (q - z) enters exactly; t is scaled by s
-//    with one fma into the fp32 accumulator.
-//  * Split-K across workgroups writes fp32 partials; the last workgroup of
-//    each row block (atomic ticket, agent-scope release/acquire) sums them in
-//    split order, so results are deterministic, and resets its ticket.
+//  * Offset and zero point, one m-tile (m <= 16): a second chain runs x
+//    against the bf16 pair the codes would unpack to if all were equal to z
+//    (128 + z, or z for 8 bits), so t = C - S' = x . (q - z) exactly for an
+//    all-zero group and for one-hot x; t is scaled by s with one fma.
+//    Several m-tiles share one chain of x against bf16 128.0 (or 1.0) per
+//    m-tile: t = (C - S) - z * S / 128 (or C - z * S).
+//  * x of the workgroup's k-block is staged once in LDS in fragment order.
+//    Scales and zero points are staged per wave (each wave reads only its own
+//    groups), issued together with the first two weight batches so their HBM
+//    round trip overlaps them, in a [group][row] layout whose 16-row reads are
+//    bank-conflict free.
+//  * Split-K across workgroups writes fp32 partials with device-coherent
+//    stores; the last workgroup of each row block (relaxed atomic ticket after
+//    the stores have completed) sums them in split order, so results are
+//    deterministic, and resets its ticket.
+
 #include <algorithm>
+#include <limits>
 
 #include "launch.h"
 #include "slq_device.h"
@@ -37,7 +46,10 @@
 namespace slq {
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef SLQ_GEMV_THREADS
+#define SLQ_GEMV_THREADS 256
+#endif
+constexpr int kThreads = SLQ_GEMV_THREADS;
 constexpr int kWaves = kThreads / kWave;
 constexpr uint32_t kMagic2 = 0x43004300u;   // bf16 pair (128.0, 128.0)
 constexpr uint32_t kOne2 = 0x3F803F80u;     // bf16 pair (1.0, 1.0)
@@ -89,19 +101,21 @@ __device__ __forceinline__ Chunk<BITS> load_chunk(const uint32_t *__restrict__ p
   return c;
 }
 
-// 32 codes -> 16 bf16 pairs in pair order (see pair_c0/pair_c1).
+// 32 codes -> 16 bf16 pairs in pair order (see pair_c0/pair_c1); `magic` is
+// kMagic2 held in a register.
 template <int BITS>
-__device__ __forceinline__ void unpack_pairs(const Chunk<BITS> &c, uint32_t (&p)[16]) {
+__device__ __forceinline__ void unpack_pairs(const Chunk<BITS> &c, uint32_t (&p)[16],
+                                             uint32_t magic) {
   if constexpr (BITS == 2) {
 #pragma unroll
     for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[8 * d + i] = ((c.w[d] >> (2 * i)) & 0x00030003u) | kMagic2;
+      for (int i = 0; i < 8; ++i) p[8 * d + i] = ((c.w[d] >> (2 * i)) & 0x00030003u) | magic;
   } else if constexpr (BITS == 4) {
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[4 * d + i] = ((c.w[d] >> (4 * i)) & 0x000F000Fu) | kMagic2;
+      for (int i = 0; i < 4; ++i) p[4 * d + i] = ((c.w[d] >> (4 * i)) & 0x000F000Fu) | magic;
   } else if constexpr (BITS == 8) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
@@ -125,14 +139,14 @@ __device__ __forceinline__ void unpack_pairs(const Chunk<BITS> &c, uint32_t (&p)
     for (int j = 0; j < 16; ++j) {
       const int bit = j * BITS, h = bit / 16, o = bit % 16;
       if (o + BITS <= 16) {
-        p[j] = ((W[h] >> o) & m2) | kMagic2;
+        p[j] = ((W[h] >> o) & m2) | magic;
       } else {
         const int d0 = bit / 32;
         const uint32_t lo = alignbit(c.w[d0 + 1], c.w[d0], bit % 32) & mb;
         const int hb = 16 * BITS + bit, d1 = hb / 32;
         const uint32_t nxt = (d1 + 1 < BITS) ? c.w[d1 + 1] : 0u;
         const uint32_t hi = alignbit(nxt, c.w[d1], hb % 32) & mb;
-        p[j] = (lo | (hi << 16)) | kMagic2;
+        p[j] = (lo | (hi << 16)) | magic;
       }
     }
   }
@@ -156,26 +170,56 @@ __device__ __forceinline__ void x_fragments(const uint32_t (&X)[16], uint32_t (&
 
 // Workgroup: 4 wavefronts on the same 16*NT rows, each taking a contiguous
 // quarter of the workgroup's k-block.  The activations of the k-block are
-// staged once in LDS, already permuted into MFMA fragment order.  Each wave
-// streams its groups in batches of B with the next batch's loads issued
-// before the current batch is consumed (two register buffers), so every lane
-// keeps up to 2*B*NT chunk loads in flight.  The four partial sums meet in
-// LDS; with several k-blocks the workgroup partials go to the workspace and
-// the last workgroup of each row block adds them in k-block order.
+// staged once in LDS, already permuted into MFMA fragment order, and so are
+// the rows' scales and zero points for the k-block.  Each wave streams its
+// groups in batches of B with the next batch's loads issued before the
+// current batch is consumed (two register buffers), so every lane keeps up to
+// 2*B*NT chunk loads in flight.  The first two batches are issued before the
+// metadata staging waits, so its HBM round trip overlaps theirs.  The four
+// partial sums meet in LDS; with several k-blocks the workgroup partials go to
+// the workspace and the last workgroup of each row block adds them in k-block
+// order.
 template <int BITS, int NT, int B>
 struct Batch {
   Chunk<BITS> c[B][NT];
 };
 
-template <int BITS, int MT, int NT, int B>
+// Zero-point operand for the single-m-tile kernels: the bf16 pair the codes
+// of a group with zero point z would unpack to when all are equal to z
+// (128 + z for the offset widths, z itself for 8 bits).  An MFMA chain of x
+// against it runs the same instructions as the code chain, so C - S' is
+// exactly 0 for an all-zero group and exactly x . (q - z) for one-hot x.
+template <int BITS>
+__device__ __forceinline__ uint32_t zero_pair(uint32_t z) {
+  if constexpr (BITS == 8) return (__float_as_uint((float)z) >> 16) * 0x10001u;
+  else return kMagic2 | (z * 0x10001u);
+}
+
+// What the metadata area holds next to each scale: the zero-point pair's bits
+// (single m-tile) or the zero point as a float.
+template <int BITS, bool ZS>
+__device__ __forceinline__ float meta_zero(uint32_t z) {
+  if constexpr (ZS) return __uint_as_float(zero_pair<BITS>(z));
+  else return (float)z;
+}
+
+// Metadata staging with MV: one float4 of scales and one u32 of zero points
+// (4 consecutive groups of a row) per lane and round; a wave stages its own
+// 16*NT rows x [ga, gz) groups.
+constexpr int kMetaRounds = 2;
+
+template <int BITS, int MT, int NT, int B, bool MV>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
     unsigned *__restrict__ tickets) {
+  // One m-tile: the zero point is folded into a per-row S' chain (see
+  // zero_pair); several m-tiles share one S chain per m-tile instead.
+  constexpr bool ZS = (MT == 1);
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 15, kq = lane >> 4;
   const int G = K / kGroup;
   const int kb = blockIdx.y;
@@ -185,7 +229,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const int n0 = blockIdx.x * 16 * NT;
   const int64_t wpr = (int64_t)K * BITS / 32;
 
+  // this wave's local group range [ga, gz): a balanced share of the k-block
+  // in units of 4 groups (MV) or single groups
+  const int gunit = MV ? 4 : 1;
+  const int units = gcount / gunit;
+  const int ga = (wave * units / kWaves) * gunit, gz = ((wave + 1) * units / kWaves) * gunit;
+
   // ---- stage activations [M][gcount*128] into LDS in fragment order ----
+  // (an L2-resident operand: the barrier after it is a short wait)
   for (int i = threadIdx.x; i < M * gcount * 4; i += kThreads) {
     const int m = i / (gcount * 4), c = i % (gcount * 4);
     const u32x4_t *src =
@@ -204,21 +255,37 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
   }
+  __syncthreads();   // activations staged
 
-  // ---- stage the workgroup's scales and zero points [16*NT rows][gcount] ----
-  // The [n][G] layout makes each row's run contiguous; one coalesced pass
-  // replaces many scattered 4-byte and 1-byte loads per row and group.
+  // ---- scales and zero points: meta[group][16*NT rows] (a tile's 16 rows of
+  // one group are 32 consecutive words: conflict-free), each wave stages its own
+  // groups [ga, gz), so no workgroup barrier waits on this HBM round trip ----
   float2 *meta = reinterpret_cast<float2 *>(lds + M * xpitch);
-  for (int i = threadIdx.x; i < 16 * NT * gcount; i += kThreads) {
-    const int r = i / gcount, gl = i % gcount;
-    const int n = min(n0 + r, N - 1);
-    const int64_t o = (int64_t)n * G + gbase + gl;
-    meta[i] = make_float2(scales[o], (float)zeros[o]);
+  const int mrows = 16 * NT;
+  float4 msv[kMetaRounds];
+  uint32_t mzv[kMetaRounds];
+  const int q4 = (gz - ga) / 4;                  // float4 units per row (MV)
+  const int munits = mrows * q4;                 // <= kWave * kMetaRounds (planned)
+  if constexpr (MV) {
+    if (munits > 0) {
+#pragma unroll
+      for (int r = 0; r < kMetaRounds; ++r) {
+        const int e = min(lane + r * kWave, munits - 1);
+        const int n = min(n0 + e / q4, N - 1);
+        const int64_t o = (int64_t)n * G + gbase + ga + 4 * (e % q4);
+        msv[r] = *reinterpret_cast<const float4 *>(scales + o);
+        mzv[r] = *reinterpret_cast<const uint32_t *>(zeros + o);
+      }
+    }
+  } else {
+    const int cnt = gz - ga;
+    for (int i = lane; i < mrows * cnt; i += kWave) {
+      const int n = min(n0 + i / cnt, N - 1);
+      const int gl = ga + i % cnt;
+      const int64_t o = (int64_t)n * G + gbase + gl;
+      meta[gl * mrows + i / cnt] = make_float2(scales[o], meta_zero<BITS, ZS>(zeros[o]));
+    }
   }
-
-  // this wave's local group range [ga, gz)
-  const int per = (gcount + kWaves - 1) / kWaves;
-  const int ga = min(gcount, wave * per), gz = min(gcount, ga + per);
 
   const uint32_t *crow[NT];
 #pragma unroll
@@ -237,8 +304,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
   };
 
-  const u32x4_t unit = (BITS == 8) ? u32x4_t{kOne2, kOne2, kOne2, kOne2}
-                                   : u32x4_t{kMagic2, kMagic2, kMagic2, kMagic2};
+  const uint32_t magic = in_vgpr(kMagic2);
+  const uint32_t unit1 = (BITS == 8) ? kOne2 : kMagic2;
+  const u32x4_t unit = u32x4_t{unit1, unit1, unit1, unit1};
   f32x4_t acc[NT][MT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -250,46 +318,56 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     for (int j = 0; j < B; ++j) {
       const int gl = g + j;
       if (gl >= gz) break;
+      // x fragments; rows past M repeat row M-1 and only feed unstored outputs
       u32x4_t A[MT][4];
-      f32x4_t S[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + col;
-        if (m < M) {
-          const u32x4_t *src =
-              reinterpret_cast<const u32x4_t *>(lds + m * xpitch + (gl * 4 + kq) * 16);
+        const int m = min(16 * mt + col, M - 1);
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds + m * xpitch + (gl * 4 + kq) * 16);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) A[mt][r] = src[r];
-        } else {
+        for (int r = 0; r < 4; ++r) A[mt][r] = src[r];
+      }
+      f32x4_t S[MT];
+      if constexpr (!ZS) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) A[mt][r] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int mt = 0; mt < MT; ++mt) {
+          S[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[mt] = mfma16(A[mt][r], unit, S[mt]);
         }
-        S[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[mt] = mfma16(A[mt][r], unit, S[mt]);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint32_t p[16];
-        unpack_pairs<BITS>(bt.c[j][t], p);
-        const float2 sz = meta[(16 * t + col) * gcount + gl];
+        unpack_pairs<BITS>(bt.c[j][t], p, magic);
+        const float2 sz = meta[gl * (16 * NT) + 16 * t + col];
         const float s = sz.x;
-        const float zf = sz.y;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           f32x4_t C = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             C = mfma16(A[mt][r], u32x4_t{p[4 * r], p[4 * r + 1], p[4 * r + 2], p[4 * r + 3]}, C);
+          if constexpr (ZS) {
+            const uint32_t zp = __float_as_uint(sz.y);
+            const u32x4_t zb = u32x4_t{zp, zp, zp, zp};
+            f32x4_t Z = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float tv;
-            if constexpr (BITS == 8) {
-              tv = fmaf(-zf, S[mt][v], C[v]);
-            } else {
-              tv = fmaf(-zf * 0.0078125f, S[mt][v], C[v] - S[mt][v]);
+            for (int r = 0; r < 4; ++r) Z = mfma16(A[mt][r], zb, Z);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][mt][v] = fmaf(s, C[v] - Z[v], acc[t][mt][v]);
+          } else {
+            const float zf = sz.y;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float tv;
+              if constexpr (BITS == 8) {
+                tv = fmaf(-zf, S[mt][v], C[v]);
+              } else {
+                tv = fmaf(-zf * 0.0078125f, S[mt][v], C[v] - S[mt][v]);
+              }
+              acc[t][mt][v] = fmaf(s, tv, acc[t][mt][v]);
             }
-            acc[t][mt][v] = fmaf(s, tv, acc[t][mt][v]);
           }
         }
       }
@@ -303,7 +381,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     load(b0, ga);
     load(b1, ga + B);
   }
-  __syncthreads();   // activations staged
+  if constexpr (MV) {
+#pragma unroll
+    for (int r = 0; r < kMetaRounds; ++r) {
+      const int e = lane + r * kWave;
+      if (e < munits) {
+        const int base = (ga + 4 * (e % q4)) * mrows + e / q4;
+        meta[base + 0 * mrows] = make_float2(msv[r].x, meta_zero<BITS, ZS>(mzv[r] & 0xFFu));
+        meta[base + 1 * mrows] = make_float2(msv[r].y, meta_zero<BITS, ZS>((mzv[r] >> 8) & 0xFFu));
+        meta[base + 2 * mrows] = make_float2(msv[r].z, meta_zero<BITS, ZS>((mzv[r] >> 16) & 0xFFu));
+        meta[base + 3 * mrows] = make_float2(msv[r].w, meta_zero<BITS, ZS>(mzv[r] >> 24));
+      }
+    }
+  }
+  // the wave's own metadata writes precede its reads in LDS program order
   if (ga < gz) {
     for (int g = ga;;) {
       compute(b0, g);
@@ -386,11 +477,19 @@ size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw) {
   return std::max(xs + meta, red) + 16;
 }
 constexpr size_t kLdsBudget = 65536;   // activation bytes per workgroup
+#ifndef SLQ_GEMV_TARGET_BLOCKS
+#define SLQ_GEMV_TARGET_BLOCKS 256
+#endif
+constexpr int64_t kTargetBlocks = SLQ_GEMV_TARGET_BLOCKS;
+#ifndef SLQ_GEMV_TARGET_BLOCKS_TINY
+#define SLQ_GEMV_TARGET_BLOCKS_TINY 64
+#endif
+constexpr int64_t kTargetBlocksTiny = SLQ_GEMV_TARGET_BLOCKS_TINY;
 // Dynamic LDS ceiling per workgroup: activations (<= 64 KiB + pitch padding)
 // plus scales/zero points (<= 32 KiB), or the reduction area (<= 64 KiB).
 constexpr size_t kMaxDynLds = 128 * 1024;
 
-template <int BITS, int MT, int NT, int B>
+template <int BITS, int MT, int NT, int B, bool MV>
 hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *scales,
                        const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                        const GemvPlan &plan, hipStream_t st) {
@@ -403,13 +502,13 @@ hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *sc
   const size_t lds = gemv_lds_bytes(m, MT, NT, plan.gw);
   if (lds > kMaxDynLds) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B>),
+      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B, MV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
   if (attr != hipSuccess) {
     (void)hipGetLastError();   // leave no sticky error behind for later calls
     return attr;
   }
-  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B>), dim3(plan.nblocks, plan.ksplits),
+  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B, MV>), dim3(plan.nblocks, plan.ksplits),
                      dim3(kThreads), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
                      plan.gw, plan.ksplits, y, partial, tickets);
   return hipGetLastError();
@@ -421,12 +520,19 @@ template <int BITS, int MT>
 hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *scales,
                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                       const GemvPlan &plan, hipStream_t st) {
+#define SLQ_GEMV_NT(NT_, B_)                                                                  \
+  case NT_:                                                                                   \
+    return plan.mv ? gemv_launch<BITS, MT, NT_, B_, true>(x, codes, scales, zeros, m, n, k, y, ws, \
+                                                          plan, st)                           \
+                   : gemv_launch<BITS, MT, NT_, B_, false>(x, codes, scales, zeros, m, n, k, y, ws, \
+                                                           plan, st);
   switch (plan.nt) {
-    case 1: return gemv_launch<BITS, MT, 1, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 2: return gemv_launch<BITS, MT, 2, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 4: return gemv_launch<BITS, MT, 4, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    SLQ_GEMV_NT(1, 4)
+    SLQ_GEMV_NT(2, 2)
+    SLQ_GEMV_NT(4, 1)
     default: return hipErrorInvalidValue;
   }
+#undef SLQ_GEMV_NT
 }
 
 template <int BITS>
@@ -450,11 +556,13 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   p.mt = (int)((m + 15) / 16);
   const int64_t G = k / kGroup;
   // Fewest k-blocks such that the activations of a k-block fit the LDS budget
-  // and about 256 workgroups (one per CU) exist; widest row tiles first (they
-  // amortize the activation staging).
+  // and about kTargetBlocks workgroups exist; widest row tiles first (they
+  // amortize the activation staging).  Every split adds a partial-sum round
+  // trip at the end, so splits are only made for lack of workgroups.
   const int64_t gw_max = std::max<int64_t>(1, (int64_t)kLdsBudget / (std::max<int64_t>(m, 1) * 256));
   const int64_t ks_min = std::max<int64_t>(1, (G + gw_max - 1) / gw_max);
-  const int64_t target = 256;
+  // Tiny activations: splits only for lack of workgroups on narrow layers.
+  const int64_t target = m <= 4 ? kTargetBlocksTiny : kTargetBlocks;
   p.nt = 1;
   for (int nt : {4, 2, 1}) {
     if (nt * p.mt > 8) continue;   // register budget
@@ -465,10 +573,24 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
       break;
     }
   }
+  // A wave's share of a k-block is bounded by the metadata it stages through
+  // its registers: kMetaRounds float4 units per lane (MV).
+  auto per_limit = [&](bool mv) {
+    int64_t lim = std::numeric_limits<int64_t>::max();
+    if (mv) lim = std::min<int64_t>(lim, (int64_t)kWave * kMetaRounds * 4 / (16 * p.nt));
+    return lim;
+  };
+  p.mv = (G % 4) == 0 && gw_max >= 4 && per_limit(true) >= 4;
+  const int64_t unit = p.mv ? 4 : 1;
+  const int64_t per_max = std::max<int64_t>(1, per_limit(p.mv) / unit) * unit;
+  const int64_t cap =
+      std::max<int64_t>(unit, std::min<int64_t>(gw_max, per_max * kWaves) / unit * unit);
   const int64_t nb = (n + 16 * p.nt - 1) / (16 * p.nt);
   int64_t ks = std::max<int64_t>(ks_min, (target + nb - 1) / nb);
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, G));
-  p.gw = (int)std::max<int64_t>(1, (G + ks - 1) / ks);
+  int64_t gw = std::max<int64_t>(1, (G + ks - 1) / ks);
+  gw = std::min<int64_t>((gw + unit - 1) / unit * unit, cap);
+  p.gw = (int)gw;
   p.ksplits = (int)std::max<int64_t>(1, (G + p.gw - 1) / p.gw);
   p.nblocks = (int)nb;
   if (p.nblocks > kMaxTicketBlocks && p.ksplits > 1) p.ksplits = 0;   // not supported

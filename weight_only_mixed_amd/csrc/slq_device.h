@@ -39,6 +39,15 @@ __host__ __device__ constexpr uint32_t halves_sel(int lh, int hh) {
          (uint32_t)(4 + 2 * hh + 1) << 24;
 }
 
+// The value of `v`, held in a VGPR the compiler cannot constant-fold.  gfx9
+// VOP3 encodings take no literal operand, so a mask/offset pair of literals
+// would split v_and_or_b32 into v_and + v_or; one operand in a register keeps
+// the three-input form.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
