@@ -87,11 +87,12 @@ def test_dequant_gemm_validation():
     assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, A, None, None) == slq.SLQ_EINVAL  # y aliases x
     assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, B, None, None) == slq.SLQ_EINVAL  # y aliases codes
     assert L.slq_dequant_gemm(A, None, 1, y, None, None) == slq.SLQ_EINVAL
-    # split-K workspace required when the plan uses one
+    # split-K workspace required when the plan uses one (16 activation rows of
+    # K=4096 exceed one workgroup's activation tile, so the plan splits k)
     big = packed(n=1024, k=4096)
-    assert L.slq_gemm_workspace_bytes(1, ctypes.byref(big)) > 0
-    assert L.slq_dequant_gemm(A, ctypes.byref(big), 1, y, None, None) == slq.SLQ_EINVAL
-    assert L.slq_dequant_gemm(A, ctypes.byref(big), 1, y, E + 0x100000 + 8, None) == slq.SLQ_EINVAL
+    assert L.slq_gemm_workspace_bytes(16, ctypes.byref(big)) > 0
+    assert L.slq_dequant_gemm(A, ctypes.byref(big), 16, y, None, None) == slq.SLQ_EINVAL
+    assert L.slq_dequant_gemm(A, ctypes.byref(big), 16, y, E + 0x100000 + 8, None) == slq.SLQ_EINVAL
     # m == 0: valid no-op
     assert L.slq_dequant_gemm(None, ctypes.byref(w), 0, None, None, None) == slq.SLQ_OK
 
