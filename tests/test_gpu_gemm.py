@@ -32,7 +32,9 @@ def full_ref(W, bits, x_bits):
 
 @pytest.mark.parametrize("bits", BITS)
 def test_decode_small_shapes(bits):
-    for (n, k) in [(1, 128), (50, 384), (300, 1024), (1000, 4096)]:
+    # k = 8192 and 8320 (64 and 65 groups) reach the long-k decode variant,
+    # with and without whole 4-group metadata vectors
+    for (n, k) in [(1, 128), (50, 384), (300, 1024), (1000, 4096), (70, 8192), (130, 8320)]:
         W = S.skewed_weights(n, k, 10 * bits + n, row_offset_std=0.005)
         for m in (1, 3, 8, 16, 17, 32, 64):
             say(f"decode bits={bits} m={m} n={n} k={k}")

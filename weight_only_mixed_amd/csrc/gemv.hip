@@ -179,9 +179,10 @@ __device__ __forceinline__ void x_fragments(const uint32_t (&X)[16], uint32_t (&
 // partial sums meet in LDS; with several k-blocks the workgroup partials go to
 // the workspace and the last workgroup of each row block adds them in k-block
 // order.
-template <int BITS, int NT, int B>
+template <int BITS, int NT, int B, bool XD>
 struct Batch {
   Chunk<BITS> c[B][NT];
+  u32x4_t xv[XD ? B : 1][4];   // XD: the lane's 32 activations of each group
 };
 
 // Zero-point operand for the single-m-tile kernels: the bf16 pair the codes
@@ -208,7 +209,7 @@ __device__ __forceinline__ float meta_zero(uint32_t z) {
 // 16*NT rows x [ga, gz) groups.
 constexpr int kMetaRounds = 2;
 
-template <int BITS, int MT, int NT, int B, bool MV>
+template <int BITS, int MT, int NT, int B, bool MV, bool XD>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   // One m-tile: the zero point is folded into a per-row S' chain (see
   // zero_pair); several m-tiles share one S chain per m-tile instead.
   constexpr bool ZS = (MT == 1);
+  static_assert(!XD || MT == 1, "direct activation loads cover one m-tile");
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -236,8 +238,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const int ga = (wave * units / kWaves) * gunit, gz = ((wave + 1) * units / kWaves) * gunit;
 
   // ---- stage activations [M][gcount*128] into LDS in fragment order ----
-  // (an L2-resident operand: the barrier after it is a short wait)
-  for (int i = threadIdx.x; i < M * gcount * 4; i += kThreads) {
+  // (an L2-resident operand: the barrier after it is a short wait).  XD: each
+  // lane loads its own activation chunk with the weight batches instead.
+  for (int i = threadIdx.x; !XD && i < M * gcount * 4; i += kThreads) {
     const int m = i / (gcount * 4), c = i % (gcount * 4);
     const u32x4_t *src =
         reinterpret_cast<const u32x4_t *>(x + (int64_t)m * K + (int64_t)gbase * kGroup + 32 * c);
@@ -255,12 +258,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
   }
-  __syncthreads();   // activations staged
+  if constexpr (!XD) __syncthreads();   // activations staged
 
   // ---- scales and zero points: meta[group][16*NT rows] (a tile's 16 rows of
   // one group are 32 consecutive words: conflict-free), each wave stages its own
   // groups [ga, gz), so no workgroup barrier waits on this HBM round trip ----
-  float2 *meta = reinterpret_cast<float2 *>(lds + M * xpitch);
+  float2 *meta = reinterpret_cast<float2 *>(lds + (XD ? 0 : M * xpitch));
   const int mrows = 16 * NT;
   float4 msv[kMetaRounds];
   uint32_t mzv[kMetaRounds];
@@ -295,10 +298,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   }
   // Loads are unconditional (group index clamped to the wave's last group) so
   // that the two batch buffers stay in flight across the loop back-edge.
-  auto load = [&](Batch<BITS, NT, B> &bt, int g) {
+  // XD: row min(col, M-1) of x, this lane's 32-value chunk of each group
+  const u32x4_t *xrow = reinterpret_cast<const u32x4_t *>(
+      x + (int64_t)min(col, M - 1) * K + (int64_t)gbase * kGroup + 32 * kq);
+  auto load = [&](Batch<BITS, NT, B, XD> &bt, int g) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int gg = min(g + j, gz - 1);
+      if constexpr (XD) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bt.xv[j][q] = xrow[gg * (kGroup / 8) + q];
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) bt.c[j][t] = load_chunk<BITS>(crow[t] + (int64_t)gg * 4 * BITS);
     }
@@ -313,19 +323,34 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Batch<BITS, NT, B> &bt, int g) {
+  auto compute = [&](const Batch<BITS, NT, B, XD> &bt, int g) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int gl = g + j;
       if (gl >= gz) break;
       // x fragments; rows past M repeat row M-1 and only feed unstored outputs
       u32x4_t A[MT][4];
+      if constexpr (XD) {
+        uint32_t X[16], F[16];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = min(16 * mt + col, M - 1);
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds + m * xpitch + (gl * 4 + kq) * 16);
+        for (int q = 0; q < 4; ++q) {
+          X[4 * q + 0] = bt.xv[j][q][0];
+          X[4 * q + 1] = bt.xv[j][q][1];
+          X[4 * q + 2] = bt.xv[j][q][2];
+          X[4 * q + 3] = bt.xv[j][q][3];
+        }
+        x_fragments<BITS>(X, F);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) A[mt][r] = src[r];
+        for (int r = 0; r < 4; ++r) A[0][r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = min(16 * mt + col, M - 1);
+          const u32x4_t *src =
+              reinterpret_cast<const u32x4_t *>(lds + m * xpitch + (gl * 4 + kq) * 16);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) A[mt][r] = src[r];
+        }
       }
       f32x4_t S[MT];
       if constexpr (!ZS) {
@@ -376,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 
   // Ring of two batch buffers: both are filled before the staging barrier, and
   // each is refilled (two batches ahead) as soon as it has been consumed.
-  Batch<BITS, NT, B> b0, b1;
+  Batch<BITS, NT, B, XD> b0, b1;
   if (ga < gz) {
     load(b0, ga);
     load(b1, ga + B);
@@ -470,8 +495,8 @@ constexpr int64_t kMaxTicketBlocks = kTicketBytes / sizeof(unsigned);
 
 // LDS: the activation tile [m][groups*128] in fragment order, reused for the
 // cross-wave reduction.
-size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw) {
-  const size_t xs = (size_t)m * (gw * 64 + 4) * 4;
+size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw, bool xd) {
+  const size_t xs = xd ? 0 : (size_t)m * (gw * 64 + 4) * 4;
   const size_t meta = (size_t)16 * nt * gw * 8;
   const size_t red = (size_t)kWaves * nt * mt * kWave * 16;
   return std::max(xs + meta, red) + 16;
@@ -485,11 +510,16 @@ constexpr int64_t kTargetBlocks = SLQ_GEMV_TARGET_BLOCKS;
 #define SLQ_GEMV_TARGET_BLOCKS_TINY 64
 #endif
 constexpr int64_t kTargetBlocksTiny = SLQ_GEMV_TARGET_BLOCKS_TINY;
+#ifndef SLQ_GEMV_XD_MIN_M
+#define SLQ_GEMV_XD_MIN_M 5
+#endif
+constexpr int64_t kXdMinM = SLQ_GEMV_XD_MIN_M;
+constexpr int64_t kXdMinGroups = 64;
 // Dynamic LDS ceiling per workgroup: activations (<= 64 KiB + pitch padding)
 // plus scales/zero points (<= 32 KiB), or the reduction area (<= 64 KiB).
 constexpr size_t kMaxDynLds = 128 * 1024;
 
-template <int BITS, int MT, int NT, int B, bool MV>
+template <int BITS, int MT, int NT, int B, bool MV, bool XD>
 hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *scales,
                        const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                        const GemvPlan &plan, hipStream_t st) {
@@ -499,16 +529,16 @@ hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *sc
     tickets = static_cast<unsigned *>(ws);
     partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
   }
-  const size_t lds = gemv_lds_bytes(m, MT, NT, plan.gw);
+  const size_t lds = gemv_lds_bytes(m, MT, NT, plan.gw, XD);
   if (lds > kMaxDynLds) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B, MV>),
+      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B, MV, XD>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
   if (attr != hipSuccess) {
     (void)hipGetLastError();   // leave no sticky error behind for later calls
     return attr;
   }
-  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B, MV>), dim3(plan.nblocks, plan.ksplits),
+  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B, MV, XD>), dim3(plan.nblocks, plan.ksplits),
                      dim3(kThreads), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
                      plan.gw, plan.ksplits, y, partial, tickets);
   return hipGetLastError();
@@ -520,12 +550,16 @@ template <int BITS, int MT>
 hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *scales,
                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                       const GemvPlan &plan, hipStream_t st) {
-#define SLQ_GEMV_NT(NT_, B_)                                                                  \
-  case NT_:                                                                                   \
-    return plan.mv ? gemv_launch<BITS, MT, NT_, B_, true>(x, codes, scales, zeros, m, n, k, y, ws, \
-                                                          plan, st)                           \
-                   : gemv_launch<BITS, MT, NT_, B_, false>(x, codes, scales, zeros, m, n, k, y, ws, \
-                                                           plan, st);
+#define SLQ_GEMV_LAUNCH(NT_, B_, MV_, XD_) \
+  gemv_launch<BITS, MT, NT_, B_, MV_, XD_>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
+#define SLQ_GEMV_NT(NT_, B_)                                                            \
+  case NT_:                                                                             \
+    if constexpr (MT == 1) {                                                            \
+      if (plan.xd)                                                                      \
+        return plan.mv ? SLQ_GEMV_LAUNCH(NT_, B_, true, true)                           \
+                       : SLQ_GEMV_LAUNCH(NT_, B_, false, true);                         \
+    }                                                                                   \
+    return plan.mv ? SLQ_GEMV_LAUNCH(NT_, B_, true, false) : SLQ_GEMV_LAUNCH(NT_, B_, false, false);
   switch (plan.nt) {
     SLQ_GEMV_NT(1, 4)
     SLQ_GEMV_NT(2, 2)
@@ -533,6 +567,7 @@ hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *sca
     default: return hipErrorInvalidValue;
   }
 #undef SLQ_GEMV_NT
+#undef SLQ_GEMV_LAUNCH
 }
 
 template <int BITS>
@@ -559,7 +594,14 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // and about kTargetBlocks workgroups exist; widest row tiles first (they
   // amortize the activation staging).  Every split adds a partial-sum round
   // trip at the end, so splits are only made for lack of workgroups.
-  const int64_t gw_max = std::max<int64_t>(1, (int64_t)kLdsBudget / (std::max<int64_t>(m, 1) * 256));
+  // One m-tile of more than a few rows on a long k: activations come straight
+  // from L2 with the weight batches (no LDS tile, so no LDS bound on the
+  // k-block and fewer splits); short k keeps the LDS tile, which measured
+  // faster there.
+  p.xd = p.mt == 1 && m >= kXdMinM && G >= kXdMinGroups;
+  const int64_t gw_max =
+      p.xd ? std::max<int64_t>(1, G)
+           : std::max<int64_t>(1, (int64_t)kLdsBudget / (std::max<int64_t>(m, 1) * 256));
   const int64_t ks_min = std::max<int64_t>(1, (G + gw_max - 1) / gw_max);
   // Tiny activations: splits only for lack of workgroups on narrow layers.
   const int64_t target = m <= 4 ? kTargetBlocksTiny : kTargetBlocks;
@@ -568,7 +610,10 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
     if (nt * p.mt > 8) continue;   // register budget
     if (m <= 4 && nt > 1) continue;   // tiny activations: occupancy matters more
     const int64_t nb = (n + 16 * nt - 1) / (16 * nt);
-    if (nb * ks_min >= target || nt == 1) {
+    // XD: wide tiles amortize each activation load over more rows; splits may
+    // go down to 8 groups per workgroup
+    const int64_t reach = p.xd ? nb * std::max<int64_t>(1, G / 8) : nb * ks_min;
+    if (reach >= target || nt == 1) {
       p.nt = nt;
       break;
     }

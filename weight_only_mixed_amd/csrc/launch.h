@@ -23,7 +23,8 @@ struct GemvPlan {
   int gw;          // 128-groups per k-block (workgroup)
   int nblocks;     // workgroups along n
   int ksplits;     // workgroups along k (0: shape not supported)
-  bool mv;         // a load batch's scales/zero points are one vector load per row
+  bool mv;         // scales/zero points staged as vectors of 4 groups per row
+  bool xd;         // activations loaded by each lane with the weight batches (mt == 1)
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);
