@@ -4,13 +4,24 @@
 // (gist.science summary "Statistically-Lossless Quantization of Large Language
 // Models", Methodology 3 and Inference Speedup; SLQ README, Usage 4).
 //
-// With thousands of activation rows the product is a dense contraction and the
-// bound is the bf16 MFMA rate.  Each workgroup computes a 128x128 tile of y:
-// per 64-wide k step it stages the activation tile and the dequantized weight
-// tile (packed codes -> (q - z) * s in fp32 -> bf16) in LDS, then four
-// wavefronts each run a 4x4 grid of 16x16x32 bf16 MFMAs with fp32
-// accumulation.  The weight tile is dequantized once per workgroup and reused
-// by every activation row of the tile.
+// With thousands of activation rows the product is a dense contraction bound
+// by the bf16 MFMA rate, so the design keeps the matrix cores fed and moves
+// the dequantization off the LDS path:
+//  * A workgroup computes a 128 (m) x 256 (n) tile of y with four wavefronts;
+//    wavefront w owns columns [64w, 64w + 64) and all 128 rows, as a 4 x 2 grid
+//    of 32x32x16 bf16 MFMAs with fp32 accumulators.
+//  * Activations: the 128 x 64 tile of each k step is staged in LDS (double
+//    buffered; the next tile's loads are in flight during the current step's
+//    MFMAs) and read as the A operands.
+//  * Weights never pass through LDS: each lane loads the 32-code chunk of its
+//    column for its half of the k step straight into registers (one chunk per
+//    32-column MFMA tile, prefetched a step ahead) and dequantizes it into the
+//    B operands: w_hat = fl32((q - z) * s) with one fma per code (see Deq),
+//    rounded to bf16.
+//    Every weight code is dequantized by exactly one lane.  The MFMA k slots
+//    are assigned so that a lane's 8 slots of the 4 MFMA steps of a k step
+//    are its chunk's 32 consecutive codes; the A operands read the matching
+//    activations from LDS.
 #include "launch.h"
 #include "slq_device.h"
 
@@ -18,9 +29,19 @@ namespace slq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 128;          // m and n extent of a workgroup tile
-constexpr int kStep = 64;           // k per LDS stage
-constexpr int kPitch = kStep + 8;   // bf16 elements per LDS row (padding vs bank conflicts)
+constexpr int kBM = 128;           // m extent of a workgroup tile
+constexpr int kBN = 256;           // n extent of a workgroup tile (64 per wavefront)
+constexpr int kBK = 64;            // k per step
+constexpr int kPitch = kBK + 8;    // bf16 elements per LDS row (padding vs bank conflicts)
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 32x32x16 bf16 MFMA: D[32x32] += A[32x16] * B[16x32], fp32 accumulate.
+// Lane l supplies A row (l % 32) and B column (l % 32), k slots 8*(l/32)+t;
+// it receives D[8*(i/4) + 4*(l/32) + i%4][l % 32] in element i.
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
 
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
@@ -28,109 +49,250 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
 }
 
 template <int BITS>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+struct Chunk {
+  uint32_t w[BITS];
+};
+
+template <int BITS>
+__device__ __forceinline__ Chunk<BITS> load_chunk(const uint32_t *__restrict__ p) {
+  Chunk<BITS> c;
+  if constexpr (BITS % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < BITS / 4; ++i) {
+      const u32x4_t v = reinterpret_cast<const u32x4_t *>(p)[i];
+      c.w[4 * i + 0] = v[0];
+      c.w[4 * i + 1] = v[1];
+      c.w[4 * i + 2] = v[2];
+      c.w[4 * i + 3] = v[3];
+    }
+  } else if constexpr (BITS % 2 == 0) {
+#pragma unroll
+    for (int i = 0; i < BITS / 2; ++i) {
+      const u32x2_t v = reinterpret_cast<const u32x2_t *>(p)[i];
+      c.w[2 * i + 0] = v[0];
+      c.w[2 * i + 1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) c.w[i] = p[i];
+  }
+  return c;
+}
+
+// w_hat = fl32((q - z) * s) exactly as the definition rounds it, one fma per
+// code: for widths up to 7, u = q - z + 128 is a positive integer below 256
+// (so it is formed with integer adds, byte-parallel where codes sit in bytes,
+// and converted exactly), and fma(u, s, -128 s) computes (q - z) s with a
+// single rounding because -128 s is exact.  8-bit codes subtract z in fp32
+// (exact) and multiply.
+struct Deq {
+  float s;       // scale
+  float c0;      // -128 * s
+  float zf;      // z (8-bit path)
+  uint32_t zo;   // 128 - z in every byte
+};
+
+__device__ __forceinline__ Deq make_deq(float s, uint32_t z) {
+  Deq d;
+  d.s = s;
+  d.c0 = -128.f * s;
+  d.zf = (float)z;
+  d.zo = (128u - z) * 0x01010101u;
+  return d;
+}
+
+// Codes j of a chunk, offset by 128 - z, as exact floats (BITS <= 7).
+template <int BITS>
+__device__ __forceinline__ float code_u(const Chunk<BITS> &c, int j, uint32_t zo) {
+  const int bit = j * BITS, wi = bit / 32, o = bit % 32;
+  uint32_t v;
+  if (o + BITS <= 32) v = (c.w[wi] >> o) & ((1u << BITS) - 1u);
+  else v = alignbit(c.w[wi + 1], c.w[wi], o) & ((1u << BITS) - 1u);
+  return (float)(v + (zo & 0xFFu));
+}
+
+// The 4 B operands of a k step for one 32-column tile: codes 8st..8st+7 of the
+// lane's chunk, dequantized and rounded to bf16.
+template <int BITS>
+__device__ __forceinline__ void dequant_chunk(const Chunk<BITS> &c, const Deq &d, u32x4_t (&b)[4]) {
+  if constexpr (BITS == 4) {
+    // codes in bytes: lo holds codes 0,2,4,6 of a word, hi codes 1,3,5,7
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (c.w[w] & 0x0F0F0F0Fu) + d.zo, hi = ((c.w[w] >> 4) & 0x0F0F0F0Fu) + d.zo;
+      uint32_t p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u0 = (float)((lo >> (8 * e)) & 0xFFu), u1 = (float)((hi >> (8 * e)) & 0xFFu);
+        p[e] = bf16_pair(fmaf(u0, d.s, d.c0), fmaf(u1, d.s, d.c0));
+      }
+      b[w] = u32x4_t{p[0], p[1], p[2], p[3]};   // word w: codes 8w..8w+7 = step w
+    }
+  } else if constexpr (BITS == 2) {
+    // word w holds codes 16w..16w+15; bytes of (word >> 2j) & 0x03.. hold codes 16w+4b+j
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t by[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) by[j] = ((c.w[w] >> (2 * j)) & 0x03030303u) + d.zo;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = 8 * half + 2 * e, k1 = k0 + 1;   // codes of the word
+          const float u0 = (float)((by[k0 % 4] >> (8 * (k0 / 4))) & 0xFFu);
+          const float u1 = (float)((by[k1 % 4] >> (8 * (k1 / 4))) & 0xFFu);
+          p[e] = bf16_pair(fmaf(u0, d.s, d.c0), fmaf(u1, d.s, d.c0));
+        }
+        b[2 * w + half] = u32x4_t{p[0], p[1], p[2], p[3]};
+      }
+    }
+  } else if constexpr (BITS == 8) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = c.w[2 * st + e / 2];
+        const float q0 = (float)((w >> (16 * (e % 2))) & 0xFFu);
+        const float q1 = (float)((w >> (16 * (e % 2) + 8)) & 0xFFu);
+        p[e] = bf16_pair((q0 - d.zf) * d.s, (q1 - d.zf) * d.s);
+      }
+      b[st] = u32x4_t{p[0], p[1], p[2], p[3]};
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p[e] = bf16_pair(fmaf(code_u<BITS>(c, 8 * st + 2 * e, d.zo), d.s, d.c0),
+                         fmaf(code_u<BITS>(c, 8 * st + 2 * e + 1, d.zo), d.s, d.c0));
+      b[st] = u32x4_t{p[0], p[1], p[2], p[3]};
+    }
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     float *__restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kPitch];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int wm = wave / 2, wn = wave % 2;
-  const int col = lane & 15, kq = lane >> 4;
-  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int c32 = lane & 31, h = lane >> 5;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN + 64 * wave;
   const int G = K / kGroup;
   const int64_t wpr = (int64_t)K * BITS / 32;
+  const int steps = K / kBK;
 
-  // Staging roles: thread t fills row t/2, half t%2 (32 k) of both tiles.
+  // activation staging: thread t copies row t/2, k half t%2 (64 bytes)
   const int sr = threadIdx.x >> 1, sh = threadIdx.x & 1;
-  const int xm = min(m0 + sr, M - 1);
-  const int wnr = min(n0 + sr, N - 1);
-  const uint16_t *xsrc = x + (int64_t)xm * K + 32 * sh;
-  const uint32_t *csrc = codes + (int64_t)wnr * wpr + sh * BITS;
-  const float *ssrc = scales + (int64_t)wnr * G;
-  const uint8_t *zsrc = zeros + (int64_t)wnr * G;
-  constexpr uint32_t mask = (1u << BITS) - 1u;
+  const u32x4_t *xsrc = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(m0 + sr, M - 1) * K + 32 * sh);
+  auto load_x = [&](int st, u32x4_t (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = xsrc[st * (kBK / 8) + i];
+  };
+  auto store_x = [&](int buf, const u32x4_t (&v)[4]) {
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(&As[buf][sr * kPitch + 32 * sh]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+  };
 
-  f32x4_t acc[4][4];
+  // weights: column n = n0 + 32t + c32 (rows past N are read, never stored);
+  // the lane's chunk of step st is chunk 2*st + h of the row
+  const uint32_t *crow[2];
+  const float *srow[2];
+  const uint8_t *zrow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = min(n0 + 32 * t + c32, N - 1);
+    crow[t] = codes + (int64_t)n * wpr + h * BITS;
+    srow[t] = scales + (int64_t)n * G;
+    zrow[t] = zeros + (int64_t)n * G;
+  }
+  // chunks, scale and zero point of step st (a step is half a 128-group)
+  auto load_w = [&](int st, Chunk<BITS> (&c)[2], float (&sv)[2], uint32_t (&zv)[2]) {
+    const int g = (st * kBK) / kGroup;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      c[t] = load_chunk<BITS>(crow[t] + (int64_t)st * 2 * BITS);
+      sv[t] = srow[t][g];
+      zv[t] = zrow[t][g];
+    }
+  };
+
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
-  for (int k0 = 0; k0 < K; k0 += kStep) {
-    // activations: 64 bytes per thread
-    {
-      const u32x4_t *px = reinterpret_cast<const u32x4_t *>(xsrc + k0);
-      u32x4_t *dst = reinterpret_cast<u32x4_t *>(As + sr * kPitch + 32 * sh);
+  u32x4_t xv[4];
+  Chunk<BITS> wc[2], wn[2];
+  float sc[2], sn[2];
+  uint32_t zc[2], zn[2];
+  load_x(0, xv);
+  load_w(0, wc, sc, zc);
+  store_x(0, xv);
+  __syncthreads();
+
+  // Each step issues the next step's loads first, so they have the whole
+  // step's MFMA work to land.
+  for (int st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+    const int nx = min(st + 1, steps - 1);   // the last step reloads itself (discarded)
+    load_x(nx, xv);
+    load_w(nx, wn, sn, zn);
+    u32x4_t b[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = px[i];
+    for (int t = 0; t < 2; ++t) dequant_chunk<BITS>(wc[t], make_deq(sc[t], zc[t]), b[t]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      // k slots 8h+t of MFMA step ks <-> k = 32h + 8ks + t within the step
+      u32x4_t a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const u32x4_t *>(&As[buf][(32 * i + c32) * kPitch + 32 * h + 8 * ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], b[t][ks], acc[i][t]);
     }
-    // weights: one 32-code chunk per thread, dequantized to bf16
-    {
-      const uint32_t *pc = csrc + (int64_t)(k0 / 32) * BITS;
-      uint32_t w[BITS];
+    if (st + 1 < steps) store_x(buf ^ 1, xv);
 #pragma unroll
-      for (int i = 0; i < BITS; ++i) w[i] = pc[i];
-      const int g = k0 / kGroup;
-      const float s = ssrc[g];
-      const int z = zsrc[g];
-      uint32_t out[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        uint32_t qv[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int bit = (2 * j + e) * BITS, wi = bit / 32, o = bit % 32;
-          uint32_t v = w[wi] >> o;
-          if (o + BITS > 32) v |= w[wi + 1] << (32 - o);
-          qv[e] = v & mask;
-        }
-        out[j] = bf16_pair((float)((int)qv[0] - z) * s, (float)((int)qv[1] - z) * s);
-      }
-      u32x4_t *dst = reinterpret_cast<u32x4_t *>(Bs + sr * kPitch + 32 * sh);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[i] = u32x4_t{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kStep / 32; ++ks) {
-      u32x4_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const u32x4_t *>(As + (64 * wm + 16 * i + col) * kPitch + 32 * ks + 8 * kq);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const u32x4_t *>(Bs + (64 * wn + 16 * j + col) * kPitch + 32 * ks + 8 * kq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+    for (int t = 0; t < 2; ++t) {
+      wc[t] = wn[t];
+      sc[t] = sn[t];
+      zc[t] = zn[t];
     }
     __syncthreads();
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int t = 0; t < 2; ++t) {
+    const int n = n0 + 32 * t + c32;
+    if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + 64 * wn + 16 * j + col;
-      if (n >= N) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * kq + v;
-        if (m < M) y[(int64_t)m * N + n] = acc[i][j][v];
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
+        if (m < M) y[(int64_t)m * N + n] = acc[i][t][e];
       }
-    }
+  }
 }
 
 template <int BITS>
 hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const float *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
                      hipStream_t st) {
-  const dim3 grid((unsigned)((n + kTile - 1) / kTile), (unsigned)((m + kTile - 1) / kTile));
+  const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_kernel<BITS>), grid, dim3(kThreads), 0, st, x, codes, scales, zeros,
                      (int)m, (int)n, (int)k, y);
   return hipGetLastError();
