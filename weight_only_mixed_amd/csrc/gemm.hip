@@ -7,15 +7,15 @@
 // With thousands of activation rows the product is a dense contraction bound
 // by the bf16 MFMA rate, so the design keeps the matrix cores fed and moves
 // the dequantization off the LDS path:
-//  * A workgroup computes a 128 (m) x 256 (n) tile of y with four wavefronts;
-//    wavefront w owns columns [64w, 64w + 64) and all 128 rows, as a 4 x 2 grid
-//    of 32x32x16 bf16 MFMAs with fp32 accumulators.
-//  * Activations: the 128 x 64 tile of each k step is staged in LDS (double
-//    buffered; the next tile's loads are in flight during the current step's
-//    MFMAs) and read as the A operands.
+//  * A workgroup computes a kBM (m) x 256 (n) tile of y with four wavefronts;
+//    wavefront w owns columns [64w, 64w + 64) and all kBM rows, as a kMT x 2
+//    grid of 32x32x16 bf16 MFMAs with fp32 accumulators.
+//  * Activations: the kBM x 64 tile of each k step is staged in LDS (double
+//    buffered) and read as the A operands; its global loads are issued two
+//    steps ahead.
 //  * Weights never pass through LDS: each lane loads the 32-code chunk of its
 //    column for its half of the k step straight into registers (one chunk per
-//    32-column MFMA tile, prefetched a step ahead) and dequantizes it into the
+//    32-column MFMA tile, prefetched two steps ahead) and dequantizes it into the
 //    B operands: w_hat = fl32((q - z) * s) with one fma per code (see Deq),
 //    rounded to bf16.
 //    Every weight code is dequantized by exactly one lane.  The MFMA k slots
@@ -29,7 +29,11 @@ namespace slq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128;           // m extent of a workgroup tile
+#ifndef SLQ_GEMM_MTILES
+#define SLQ_GEMM_MTILES 4
+#endif
+constexpr int kMT = SLQ_GEMM_MTILES;   // 32-row MFMA tiles per wavefront
+constexpr int kBM = 32 * kMT;      // m extent of a workgroup tile
 constexpr int kBN = 256;           // n extent of a workgroup tile (64 per wavefront)
 constexpr int kBK = 64;            // k per step
 constexpr int kPitch = kBK + 8;    // bf16 elements per LDS row (padding vs bank conflicts)
@@ -43,9 +47,13 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one packed bf16 pair, round to nearest even (a single
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <int BITS>
@@ -111,71 +119,51 @@ __device__ __forceinline__ float code_u(const Chunk<BITS> &c, int j, uint32_t zo
   return (float)(v + (zo & 0xFFu));
 }
 
-// The 4 B operands of a k step for one 32-column tile: codes 8st..8st+7 of the
-// lane's chunk, dequantized and rounded to bf16.
+// B operand of MFMA k-slice ks (codes 8ks..8ks+7 of the lane's chunk) for
+// one 32-column tile, dequantized and rounded to bf16.
 template <int BITS>
-__device__ __forceinline__ void dequant_chunk(const Chunk<BITS> &c, const Deq &d, u32x4_t (&b)[4]) {
+__device__ __forceinline__ u32x4_t dequant_slice(const Chunk<BITS> &c, const Deq &d, int ks) {
+  uint32_t p[4];
   if constexpr (BITS == 4) {
-    // codes in bytes: lo holds codes 0,2,4,6 of a word, hi codes 1,3,5,7
+    // codes in bytes: lo holds codes 0,2,4,6 of word ks, hi codes 1,3,5,7
+    const uint32_t lo = (c.w[ks] & 0x0F0F0F0Fu) + d.zo, hi = ((c.w[ks] >> 4) & 0x0F0F0F0Fu) + d.zo;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = (c.w[w] & 0x0F0F0F0Fu) + d.zo, hi = ((c.w[w] >> 4) & 0x0F0F0F0Fu) + d.zo;
-      uint32_t p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float u0 = (float)((lo >> (8 * e)) & 0xFFu), u1 = (float)((hi >> (8 * e)) & 0xFFu);
-        p[e] = bf16_pair(fmaf(u0, d.s, d.c0), fmaf(u1, d.s, d.c0));
-      }
-      b[w] = u32x4_t{p[0], p[1], p[2], p[3]};   // word w: codes 8w..8w+7 = step w
+    for (int e = 0; e < 4; ++e) {
+      const float u0 = (float)((lo >> (8 * e)) & 0xFFu), u1 = (float)((hi >> (8 * e)) & 0xFFu);
+      p[e] = bf16_pair(fmaf(u0, d.s, d.c0), fmaf(u1, d.s, d.c0));
     }
   } else if constexpr (BITS == 2) {
-    // word w holds codes 16w..16w+15; bytes of (word >> 2j) & 0x03.. hold codes 16w+4b+j
+    // word ks/2 holds codes 16(ks/2)..+15; bytes of (word >> 2j) & 0x03.. hold codes 4b+j
+    const uint32_t w = c.w[ks / 2];
+    uint32_t by[4];
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      uint32_t by[4];
+    for (int j = 0; j < 4; ++j) by[j] = ((w >> (2 * j)) & 0x03030303u) + d.zo;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) by[j] = ((c.w[w] >> (2 * j)) & 0x03030303u) + d.zo;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k0 = 8 * half + 2 * e, k1 = k0 + 1;   // codes of the word
-          const float u0 = (float)((by[k0 % 4] >> (8 * (k0 / 4))) & 0xFFu);
-          const float u1 = (float)((by[k1 % 4] >> (8 * (k1 / 4))) & 0xFFu);
-          p[e] = bf16_pair(fmaf(u0, d.s, d.c0), fmaf(u1, d.s, d.c0));
-        }
-        b[2 * w + half] = u32x4_t{p[0], p[1], p[2], p[3]};
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int k0 = 8 * (ks % 2) + 2 * e, k1 = k0 + 1;   // codes of the word
+      const float u0 = (float)((by[k0 % 4] >> (8 * (k0 / 4))) & 0xFFu);
+      const float u1 = (float)((by[k1 % 4] >> (8 * (k1 / 4))) & 0xFFu);
+      p[e] = bf16_pair(fmaf(u0, d.s, d.c0), fmaf(u1, d.s, d.c0));
     }
   } else if constexpr (BITS == 8) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint32_t p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = c.w[2 * st + e / 2];
-        const float q0 = (float)((w >> (16 * (e % 2))) & 0xFFu);
-        const float q1 = (float)((w >> (16 * (e % 2) + 8)) & 0xFFu);
-        p[e] = bf16_pair((q0 - d.zf) * d.s, (q1 - d.zf) * d.s);
-      }
-      b[st] = u32x4_t{p[0], p[1], p[2], p[3]};
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = c.w[2 * ks + e / 2];
+      const float q0 = (float)((w >> (16 * (e % 2))) & 0xFFu);
+      const float q1 = (float)((w >> (16 * (e % 2) + 8)) & 0xFFu);
+      p[e] = bf16_pair((q0 - d.zf) * d.s, (q1 - d.zf) * d.s);
     }
   } else {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint32_t p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p[e] = bf16_pair(fmaf(code_u<BITS>(c, 8 * st + 2 * e, d.zo), d.s, d.c0),
-                         fmaf(code_u<BITS>(c, 8 * st + 2 * e + 1, d.zo), d.s, d.c0));
-      b[st] = u32x4_t{p[0], p[1], p[2], p[3]};
-    }
+    for (int e = 0; e < 4; ++e)
+      p[e] = bf16_pair(fmaf(code_u<BITS>(c, 8 * ks + 2 * e, d.zo), d.s, d.c0),
+                       fmaf(code_u<BITS>(c, 8 * ks + 2 * e + 1, d.zo), d.s, d.c0));
   }
+  return u32x4_t{p[0], p[1], p[2], p[3]};
 }
 
 template <int BITS>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
+__global__ __launch_bounds__(kThreads, kMT > 4 ? 1 : 2) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     float *__restrict__ y) {
@@ -189,17 +177,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
   const int64_t wpr = (int64_t)K * BITS / 32;
   const int steps = K / kBK;
 
-  // activation staging: thread t copies row t/2, k half t%2 (64 bytes)
+  // activation staging: thread t copies rows t/2 + 128r, k half t%2 (64 bytes each)
+  constexpr int XR = kBM / 128;
   const int sr = threadIdx.x >> 1, sh = threadIdx.x & 1;
-  const u32x4_t *xsrc = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(m0 + sr, M - 1) * K + 32 * sh);
-  auto load_x = [&](int st, u32x4_t (&v)[4]) {
+  const u32x4_t *xsrc[XR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = xsrc[st * (kBK / 8) + i];
+  for (int r = 0; r < XR; ++r)
+    xsrc[r] = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(m0 + sr + 128 * r, M - 1) * K + 32 * sh);
+  auto load_x = [&](int st, u32x4_t (&v)[XR][4]) {
+#pragma unroll
+    for (int r = 0; r < XR; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[r][i] = xsrc[r][st * (kBK / 8) + i];
   };
-  auto store_x = [&](int buf, const u32x4_t (&v)[4]) {
-    u32x4_t *dst = reinterpret_cast<u32x4_t *>(&As[buf][sr * kPitch + 32 * sh]);
+  auto store_x = [&](int buf, const u32x4_t (&v)[XR][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    for (int r = 0; r < XR; ++r) {
+      u32x4_t *dst = reinterpret_cast<u32x4_t *>(&As[buf][(sr + 128 * r) * kPitch + 32 * sh]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = v[r][i];
+    }
   };
 
   // weights: column n = n0 + 32t + c32 (rows past N are read, never stored);
@@ -225,53 +222,62 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     }
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[kMT][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kMT; ++i)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
-  u32x4_t xv[4];
-  Chunk<BITS> wc[2], wn[2];
-  float sc[2], sn[2];
-  uint32_t zc[2], zn[2];
-  load_x(0, xv);
-  load_w(0, wc, sc, zc);
-  store_x(0, xv);
+  // Prefetch ahead: a step's activation tile is requested two steps before it
+  // is needed and its weight chunks one and a half steps before, which covers
+  // an HBM round trip under load.  Two register sets of each alternate between even
+  // and odd steps (no copies: copying a register with a load in flight would
+  // wait for it); loads complete in issue order, so waiting for x(st+1) at
+  // the end of step st does not wait for the step-st requests.
+  u32x4_t xA[XR][4], xB[XR][4];
+  Chunk<BITS> wA[2], wB[2];
+  float sA[2], sB[2];
+  uint32_t zA[2], zB[2];
+  load_x(0, xA);
+  store_x(0, xA);
+  load_w(0, wA, sA, zA);
+  load_w(1, wB, sB, zB);   // steps = 2 * groups >= 2
+  load_x(1, xB);
   __syncthreads();
 
-  // Each step issues the next step's loads first, so they have the whole
-  // step's MFMA work to land.
-  for (int st = 0; st < steps; ++st) {
+  // step st: issue x(st+2) into xi, run the MFMAs on w (= w(st)) dequantized
+  // slice by slice, refill that slot with w(st+2), store xs (= x(st+1)) to the
+  // other buffer
+  auto step = [&](int st, u32x4_t (&xi)[XR][4], const u32x4_t (&xs)[XR][4], Chunk<BITS> (&w)[2],
+                  float (&sw)[2], uint32_t (&zw)[2]) {
     const int buf = st & 1;
-    const int nx = min(st + 1, steps - 1);   // the last step reloads itself (discarded)
-    load_x(nx, xv);
-    load_w(nx, wn, sn, zn);
-    u32x4_t b[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) dequant_chunk<BITS>(wc[t], make_deq(sc[t], zc[t]), b[t]);
+    const int n2 = min(st + 2, steps - 1);   // past the end: reload the last step (discarded)
+    load_x(n2, xi);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+    const Deq d[2] = {make_deq(sw[0], zw[0]), make_deq(sw[1], zw[1])};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       // k slots 8h+t of MFMA step ks <-> k = 32h + 8ks + t within the step
-      u32x4_t a[4];
+      u32x4_t a[kMT], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kMT; ++i)
         a[i] = *reinterpret_cast<const u32x4_t *>(&As[buf][(32 * i + c32) * kPitch + 32 * h + 8 * ks]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int t = 0; t < 2; ++t) b[t] = dequant_slice<BITS>(w[t], d[t], ks);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], b[t][ks], acc[i][t]);
-    }
-    if (st + 1 < steps) store_x(buf ^ 1, xv);
+      for (int i = 0; i < kMT; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      wc[t] = wn[t];
-      sc[t] = sn[t];
-      zc[t] = zn[t];
+        for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], b[t], acc[i][t]);
     }
+    load_w(n2, w, sw, zw);   // the slot is free once its last slice is dequantized
+    if (st + 1 < steps) store_x(buf ^ 1, xs);
     __syncthreads();
+  };
+  for (int st = 0; st < steps; st += 2) {
+    step(st, xA, xB, wA, sA, zA);
+    step(st + 1, xB, xA, wB, sB, zB);
   }
 
 #pragma unroll
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(
     const int n = n0 + 32 * t + c32;
     if (n >= N) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kMT; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
