@@ -179,10 +179,10 @@ __device__ __forceinline__ void x_fragments(const uint32_t (&X)[16], uint32_t (&
 // partial sums meet in LDS; with several k-blocks the workgroup partials go to
 // the workspace and the last workgroup of each row block adds them in k-block
 // order.
-template <int BITS, int NT, int B, bool XD>
+template <int BITS, int MT, int NT, int B, bool XD>
 struct Batch {
   Chunk<BITS> c[B][NT];
-  u32x4_t xv[XD ? B : 1][4];   // XD: the lane's 32 activations of each group
+  u32x4_t xv[XD ? B : 1][XD ? MT : 1][4];   // XD: the lane's 32 activations per m-tile and group
 };
 
 // Zero-point operand for the single-m-tile kernels: the bf16 pair the codes
@@ -218,7 +218,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   // One m-tile: the zero point is folded into a per-row S' chain (see
   // zero_pair); several m-tiles share one S chain per m-tile instead.
   constexpr bool ZS = (MT == 1);
-  static_assert(!XD || MT == 1, "direct activation loads cover one m-tile");
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -298,16 +297,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   }
   // Loads are unconditional (group index clamped to the wave's last group) so
   // that the two batch buffers stay in flight across the loop back-edge.
-  // XD: row min(col, M-1) of x, this lane's 32-value chunk of each group
-  const u32x4_t *xrow = reinterpret_cast<const u32x4_t *>(
-      x + (int64_t)min(col, M - 1) * K + (int64_t)gbase * kGroup + 32 * kq);
-  auto load = [&](Batch<BITS, NT, B, XD> &bt, int g) {
+  // XD: rows min(16 mt + col, M-1) of x, this lane's 32-value chunk of each group
+  const u32x4_t *xrow[XD ? MT : 1];
+#pragma unroll
+  for (int mt = 0; mt < (XD ? MT : 1); ++mt)
+    xrow[mt] = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(16 * mt + col, M - 1) * K +
+                                                 (int64_t)gbase * kGroup + 32 * kq);
+  auto load = [&](Batch<BITS, MT, NT, B, XD> &bt, int g) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int gg = min(g + j, gz - 1);
       if constexpr (XD) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bt.xv[j][q] = xrow[gg * (kGroup / 8) + q];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bt.xv[j][mt][q] = xrow[mt][gg * (kGroup / 8) + q];
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) bt.c[j][t] = load_chunk<BITS>(crow[t] + (int64_t)gg * 4 * BITS);
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Batch<BITS, NT, B, XD> &bt, int g) {
+  auto compute = [&](const Batch<BITS, MT, NT, B, XD> &bt, int g) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int gl = g + j;
@@ -331,17 +335,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       // x fragments; rows past M repeat row M-1 and only feed unstored outputs
       u32x4_t A[MT][4];
       if constexpr (XD) {
-        uint32_t X[16], F[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          X[4 * q + 0] = bt.xv[j][q][0];
-          X[4 * q + 1] = bt.xv[j][q][1];
-          X[4 * q + 2] = bt.xv[j][q][2];
-          X[4 * q + 3] = bt.xv[j][q][3];
+        for (int mt = 0; mt < MT; ++mt) {
+          uint32_t X[16], F[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            X[4 * q + 0] = bt.xv[j][mt][q][0];
+            X[4 * q + 1] = bt.xv[j][mt][q][1];
+            X[4 * q + 2] = bt.xv[j][mt][q][2];
+            X[4 * q + 3] = bt.xv[j][mt][q][3];
+          }
+          x_fragments<BITS>(X, F);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            A[mt][r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
         }
-        x_fragments<BITS>(X, F);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) A[0][r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 
   // Ring of two batch buffers: both are filled before the staging barrier, and
   // each is refilled (two batches ahead) as soon as it has been consumed.
-  Batch<BITS, NT, B, XD> b0, b1;
+  Batch<BITS, MT, NT, B, XD> b0, b1;
   if (ga < gz) {
     load(b0, ga);
     load(b1, ga + B);
@@ -552,14 +560,21 @@ hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *sca
                       const GemvPlan &plan, hipStream_t st) {
 #define SLQ_GEMV_LAUNCH(NT_, B_, MV_, XD_) \
   gemv_launch<BITS, MT, NT_, B_, MV_, XD_>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
+// Direct activation loads with several m-tiles hold MT x 16 registers of x
+// per group: one group per batch.
 #define SLQ_GEMV_NT(NT_, B_)                                                            \
   case NT_:                                                                             \
-    if constexpr (MT == 1) {                                                            \
-      if (plan.xd)                                                                      \
-        return plan.mv ? SLQ_GEMV_LAUNCH(NT_, B_, true, true)                           \
-                       : SLQ_GEMV_LAUNCH(NT_, B_, false, true);                         \
+    if constexpr (NT_ * MT <= 4 || MT == 1) {                                           \
+      if (plan.xd) {                                                                    \
+        constexpr int BX = MT == 1 ? B_ : 1;                                            \
+        return plan.mv ? SLQ_GEMV_LAUNCH(NT_, BX, true, true)                           \
+                       : SLQ_GEMV_LAUNCH(NT_, BX, false, true);                         \
+      }                                                                                 \
     }                                                                                   \
-    return plan.mv ? SLQ_GEMV_LAUNCH(NT_, B_, true, false) : SLQ_GEMV_LAUNCH(NT_, B_, false, false);
+    if constexpr (MT == 1)                                                              \
+      return plan.mv ? SLQ_GEMV_LAUNCH(NT_, B_, true, false)                            \
+                     : SLQ_GEMV_LAUNCH(NT_, B_, false, false);                          \
+    return hipErrorInvalidValue;
   switch (plan.nt) {
     SLQ_GEMV_NT(1, 4)
     SLQ_GEMV_NT(2, 2)
@@ -598,7 +613,9 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // from L2 with the weight batches (no LDS tile, so no LDS bound on the
   // k-block and fewer splits); short k keeps the LDS tile, which measured
   // faster there.
-  p.xd = p.mt == 1 && m >= kXdMinM && G >= kXdMinGroups;
+  // Several m-tiles always load x directly: an LDS tile of 17..64 rows would
+  // cap the k-block at a few groups and multiply the split-K partial sums.
+  p.xd = (p.mt == 1 && m >= kXdMinM && G >= kXdMinGroups) || p.mt > 1;
   const int64_t gw_max =
       p.xd ? std::max<int64_t>(1, G)
            : std::max<int64_t>(1, (int64_t)kLdsBudget / (std::max<int64_t>(m, 1) * 256));
@@ -607,7 +624,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   const int64_t target = m <= 4 ? kTargetBlocksTiny : kTargetBlocks;
   p.nt = 1;
   for (int nt : {4, 2, 1}) {
-    if (nt * p.mt > 8) continue;   // register budget
+    if (nt * p.mt > (p.xd && p.mt > 1 ? 4 : 8)) continue;   // register budget
     if (m <= 4 && nt > 1) continue;   // tiny activations: occupancy matters more
     const int64_t nb = (n + 16 * nt - 1) / (16 * nt);
     // XD: wide tiles amortize each activation load over more rows; splits may
@@ -636,6 +653,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   int64_t gw = std::max<int64_t>(1, (G + ks - 1) / ks);
   gw = std::min<int64_t>((gw + unit - 1) / unit * unit, cap);
   p.gw = (int)gw;
+  p.b = (p.xd && p.mt > 1) ? 1 : 4 / p.nt;
   p.ksplits = (int)std::max<int64_t>(1, (G + p.gw - 1) / p.gw);
   p.nblocks = (int)nb;
   if (p.nblocks > kMaxTicketBlocks && p.ksplits > 1) p.ksplits = 0;   // not supported
