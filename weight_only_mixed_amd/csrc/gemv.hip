@@ -495,6 +495,177 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Decode with 17..64 activation rows.  The activations of a group (up to
+// 64 x 128 bf16) are the large operand next to a 16-row weight tile, so the
+// four wavefronts of a workgroup split rows instead of k: wavefront w owns
+// rows [16w, 16w + 16) of the workgroup's 64, and all four read one copy of
+// each group's activations, staged in LDS in fragment order (double buffered,
+// one barrier per group; the loads of group g+2 are issued during group g).
+// Each wavefront keeps kRowsDepth groups of its codes in flight and stages
+// its rows' scales and zero points for the k-block in LDS.  Zero points use
+// one shared S chain per m-tile (t = (C - S) - z * S / 128, or C - z * S).
+constexpr int kRowsDepth = 4;
+constexpr int kRowsXPitch = 68;   // words per activation row and group (64 + 4 vs bank conflicts)
+
+template <int BITS, int MT>
+__global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
+    const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
+    unsigned *__restrict__ tickets) {
+  static_assert(kThreads == 256, "four wavefronts of 16 rows");
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = K / kGroup;
+  const int kb = blockIdx.y;
+  const int gbase = kb * GW;
+  const int gcount = min(GW, G - gbase);
+  const int nw = blockIdx.x * 64 + 16 * wave;   // this wave's first row
+  const int64_t wpr = (int64_t)K * BITS / 32;
+
+  uint32_t *xbuf[2] = {lds, lds + M * kRowsXPitch};
+  float2 *meta = reinterpret_cast<float2 *>(lds + 2 * M * kRowsXPitch) + wave * gcount * 16;
+
+  // activation staging: thread t owns chunk t % 4 of row t / 4 (clamped past M)
+  const int xm = min((int)threadIdx.x / 4, M - 1), xc = threadIdx.x % 4;
+  const bool xowner = (int)threadIdx.x < 4 * M;
+  const u32x4_t *xsrc =
+      reinterpret_cast<const u32x4_t *>(x + (int64_t)xm * K + (int64_t)gbase * kGroup + 32 * xc);
+  auto xload = [&](int g, u32x4_t (&v)[4]) {
+    const int gg = min(g, gcount - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = xsrc[gg * (kGroup / 8) + q];
+  };
+  auto xstore = [&](uint32_t *buf, const u32x4_t (&v)[4]) {
+    if (!xowner) return;
+    uint32_t X[16], F[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      X[4 * q + 0] = v[q][0];
+      X[4 * q + 1] = v[q][1];
+      X[4 * q + 2] = v[q][2];
+      X[4 * q + 3] = v[q][3];
+    }
+    x_fragments<BITS>(X, F);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(buf + xm * kRowsXPitch + xc * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = u32x4_t{F[4 * q], F[4 * q + 1], F[4 * q + 2], F[4 * q + 3]};
+  };
+
+  const uint32_t *crow = codes + (int64_t)min(nw + col, N - 1) * wpr + (int64_t)gbase * 4 * BITS + kq * BITS;
+  auto cload = [&](int g) { return load_chunk<BITS>(crow + (int64_t)min(g, gcount - 1) * 4 * BITS); };
+
+  // prologue: x(0), the code ring, x(1), then this wave's metadata
+  u32x4_t xr0[4], xr1[4];
+  xload(0, xr0);
+  Chunk<BITS> ring[kRowsDepth];
+#pragma unroll
+  for (int d = 0; d < kRowsDepth; ++d) ring[d] = cload(d);
+  xload(1, xr1);
+  for (int i = lane; i < 16 * gcount; i += kWave) {
+    const int r = i / gcount, gl = i % gcount;
+    const int64_t o = (int64_t)min(nw + r, N - 1) * G + gbase + gl;
+    meta[gl * 16 + r] = make_float2(scales[o], (float)zeros[o]);
+  }
+  xstore(xbuf[0], xr0);
+  __syncthreads();
+
+  const uint32_t magic = in_vgpr(kMagic2);
+  const uint32_t unit1 = (BITS == 8) ? kOne2 : kMagic2;
+  const u32x4_t unit = u32x4_t{unit1, unit1, unit1, unit1};
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // group g: x(g) is in xbuf[g % 2]; x(g+1) waits in register set (g+1) % 2
+  auto body = [&](int g, const Chunk<BITS> &c, u32x4_t (&xfree)[4], const u32x4_t (&xnext)[4]) {
+    xload(g + 2, xfree);
+    const uint32_t *buf = xbuf[g & 1];
+    u32x4_t A[MT][4];
+    f32x4_t S[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = min(16 * mt + col, M - 1);
+      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(buf + m * kRowsXPitch + kq * 16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) A[mt][r] = src[r];
+      S[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[mt] = mfma16(A[mt][r], unit, S[mt]);
+    }
+    uint32_t p[16];
+    unpack_pairs<BITS>(c, p, magic);
+    const float2 sz = meta[g * 16 + col];
+    const float s = sz.x, zf = sz.y;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4_t C = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        C = mfma16(A[mt][r], u32x4_t{p[4 * r], p[4 * r + 1], p[4 * r + 2], p[4 * r + 3]}, C);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float tv;
+        if constexpr (BITS == 8) tv = fmaf(-zf, S[mt][v], C[v]);
+        else tv = fmaf(-zf * 0.0078125f, S[mt][v], C[v] - S[mt][v]);
+        acc[mt][v] = fmaf(s, tv, acc[mt][v]);
+      }
+    }
+    if (g + 1 < gcount) xstore(xbuf[(g + 1) & 1], xnext);
+    __syncthreads();
+  };
+
+  for (int g0 = 0; g0 < gcount; g0 += kRowsDepth) {
+#pragma unroll
+    for (int j = 0; j < kRowsDepth; ++j) {
+      const int g = g0 + j;
+      if (g >= gcount) break;
+      if (j % 2 == 0) body(g, ring[j], xr0, xr1);
+      else body(g, ring[j], xr1, xr0);
+      ring[j] = cload(g + kRowsDepth);
+    }
+  }
+
+  // ---- outputs: rows nw + col, m = 16 mt + 4 kq + v ----
+  const int n = nw + col;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * mt + 4 * kq + v;
+      if (m >= M || n >= N) continue;
+      if (ksplits == 1) y[(int64_t)m * N + n] = acc[mt][v];
+      else
+        __hip_atomic_store(&partial[((int64_t)kb * M + m) * N + n], acc[mt][v], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  if (ksplits == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ unsigned last;
+  if (threadIdx.x == 0) {
+    const unsigned ticket = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    last = (ticket == (unsigned)ksplits - 1u);
+  }
+  __syncthreads();
+  if (!last) return;
+  const int n0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < M * 64; i += kThreads) {
+    const int m = i / 64, nn = n0 + i % 64;
+    if (nn >= N) continue;
+    float sum = 0.f;
+    for (int sp = 0; sp < ksplits; ++sp)
+      sum += __hip_atomic_load(&partial[((int64_t)sp * M + m) * N + nn], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    y[(int64_t)m * N + nn] = sum;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Split-K tickets live in a fixed area at the start of the workspace, so no
 // call's partial sums ever overlap another call's tickets; every completed
 // call leaves all tickets at zero.
@@ -585,10 +756,46 @@ hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *sca
 #undef SLQ_GEMV_LAUNCH
 }
 
+size_t gemv_rows_lds_bytes(int64_t m, int gw) {
+  return (size_t)2 * m * kRowsXPitch * 4 + (size_t)kWaves * gw * 16 * 8 + 16;
+}
+
+template <int BITS, int MT>
+hipError_t gemv_rows_launch(const uint16_t *x, const uint32_t *codes, const float *scales,
+                            const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
+                            void *ws, const GemvPlan &plan, hipStream_t st) {
+  float *partial = nullptr;
+  unsigned *tickets = nullptr;
+  if (plan.ksplits > 1) {
+    tickets = static_cast<unsigned *>(ws);
+    partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
+  }
+  const size_t lds = gemv_rows_lds_bytes(m, plan.gw);
+  if (lds > kMaxDynLds) return hipErrorInvalidValue;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&gemv_rows_kernel<BITS, MT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+  if (attr != hipSuccess) {
+    (void)hipGetLastError();
+    return attr;
+  }
+  hipLaunchKernelGGL((gemv_rows_kernel<BITS, MT>), dim3(plan.nblocks, plan.ksplits),
+                     dim3(kThreads), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
+                     plan.gw, plan.ksplits, y, partial, tickets);
+  return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const float *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      const GemvPlan &plan, hipStream_t st) {
+  if (plan.rows) {
+    switch (plan.mt) {
+      case 3: return gemv_rows_launch<BITS, 3>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      case 4: return gemv_rows_launch<BITS, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (plan.mt) {
     case 1: return gemv_shape<BITS, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
     case 2: return gemv_shape<BITS, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
@@ -605,6 +812,30 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   GemvPlan p;
   p.mt = (int)((m + 15) / 16);
   const int64_t G = k / kGroup;
+  // 33..64 activation rows on a wide or deep layer: the row-split kernel (one
+  // LDS copy of each group's activations for 64 weight rows) beats per-lane
+  // activation loads, whose L2 traffic grows with n * k * m / 16; narrower
+  // layers and 17..32 rows measured faster with per-lane loads.
+  p.rows = p.mt >= 3 && (n >= 8192 || k >= 8192);
+  if (p.rows) {
+    // row-split kernel: 64 rows per workgroup; split k only for lack of
+    // workgroups, keeping at least 8 groups per k-block
+    p.nt = 4;
+    p.mv = false;
+    p.xd = false;
+    p.b = kRowsDepth;
+    const int64_t nb = (n + 63) / 64;
+    int64_t ks = std::max<int64_t>(1, (kTargetBlocks + nb - 1) / nb);
+    ks = std::min<int64_t>(ks, std::max<int64_t>(1, G / 8));
+    int64_t gw = (G + ks - 1) / ks;
+    gw = std::min<int64_t>(std::max<int64_t>(gw, 1), 64);
+    p.gw = (int)gw;
+    p.ksplits = (int)((G + gw - 1) / gw);
+    p.nblocks = (int)nb;
+    if (p.nblocks > kMaxTicketBlocks && p.ksplits > 1) p.ksplits = 0;
+    p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
+    return p;
+  }
   // Fewest k-blocks such that the activations of a k-block fit the LDS budget
   // and about kTargetBlocks workgroups exist; widest row tiles first (they
   // amortize the activation staging).  Every split adds a partial-sum round

@@ -26,6 +26,7 @@ struct GemvPlan {
   int ksplits;     // workgroups along k (0: shape not supported)
   bool mv;         // scales/zero points staged as vectors of 4 groups per row
   bool xd;         // activations loaded by each lane with the weight batches (mt == 1)
+  bool rows;       // 17..64 activation rows: row-split kernel, 64 rows per workgroup
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);

@@ -155,8 +155,11 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
   if (m <= 0 || m >= kMaxDim || check_packed(w, &sz) != SLQ_OK) return buf;
   if (m <= 64) {
     const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
-    snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s>", w->bits, p.mt, p.nt,
-             p.b, p.mv ? "true" : "false", p.xd ? "true" : "false");
+    if (p.rows)
+      snprintf(buf, sizeof buf, "slq::gemv_rows_kernel<%d, %d>", w->bits, p.mt);
+    else
+      snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s>", w->bits, p.mt, p.nt,
+               p.b, p.mv ? "true" : "false", p.xd ? "true" : "false");
   } else {
     snprintf(buf, sizeof buf, "slq::gemm_kernel<%d>", w->bits);
   }
