@@ -15,8 +15,9 @@ The same run measures the other steps of the path and reports them under
 bits 4 and 6), the 224-matmul mixed-bit-width stack (M 1/32/64), EAR/KL over
 512 x 151936 logits, and the symmetric-vs-asymmetric noise ratio of a
 5120x25600 layer.  `roofline` is for the dominant decode kernel instance,
-timed per launch with HIP events on the launch stream.  `cpu_baseline` times
-the CPU oracle on a bounded sample of the sweep.
+timed from a HIP graph of all its sweep launches (kernel time, as rocprofv3
+reports it).  `cpu_baseline` times the CPU oracle on whole passes of the
+sweep (about 10 s of CPU work).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|none|a,b]
 """
@@ -449,7 +450,7 @@ def main():
                 qcache[(name, bits)] = (oracle.pack(q, bits), s, z)
         tb, tt, npts = 0, 0.0, 0
         xcache = {}
-        while tt < 10.0 and npts < 3 * len(sample):   # whole passes until >= 10 s of CPU work
+        while tt < 10.0 and npts < 12 * len(sample):   # whole passes until >= 10 s of CPU work
             for (name, n, k, bits, m) in sample:
                 words, s, z = qcache[(name, bits)]
                 if (m, k) not in xcache:
