@@ -14,8 +14,11 @@
 // which gives KL without a second pass: KL = U / Z_a - (A - B), where A and B
 // are the log-normalizers.  Chunk partials are combined per row in fp64 in a
 // fixed order.  Pass 2 needs A and B (min(p, q) is not decomposable before
-// normalization), re-reads the rows in reverse order so the most recently
-// streamed rows are still cached, and sums min(exp(a - A), exp(b - B)).
+// normalization); it combines the row's chunk statistics into A, B and KL,
+// sums exp(min(a - A, b - B)) = min(p, q) (one exponential per element), and
+// visits rows in reverse order so the most recently streamed rows are still
+// cached.  (Blocking rows so that pass 2 re-reads a block from the Infinity
+// Cache measured slower at every block size.)
 // Every reduction has a fixed shape, so repeated calls are bit-identical.
 #include <algorithm>
 
@@ -126,11 +129,11 @@ __device__ __forceinline__ void online1(float a, float b, float &m, double &z, d
 template <bool WITH_B>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const float *__restrict__ a,
                                                          const float *__restrict__ b,
-                                                         int64_t vocab, Fid f,
+                                                         int64_t vocab, Fid f, int64_t r0,
                                                          double *__restrict__ stats) {
   __shared__ MZ lds[kThreads / kWave];
   const int c = blockIdx.x;
-  const int64_t row = blockIdx.y;
+  const int64_t row = r0 + blockIdx.y;
   const int64_t beg = (int64_t)c * f.chunk;
   const int64_t end = std::min<int64_t>(beg + f.chunk, vocab);
   const float *ar = a + row * vocab;
@@ -175,12 +178,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float *__restrict
 
 // Per row: combine chunk partials in chunk order -> A, B, KL.
 template <bool WITH_B>
-__global__ __launch_bounds__(kThreads) void rows_kernel(const double *__restrict__ stats, int64_t rows,
-                                                        Fid f, double *__restrict__ rowres,
+__global__ __launch_bounds__(kThreads) void rows_kernel(const double *__restrict__ stats, int64_t r0,
+                                                        int64_t r1, Fid f, double *__restrict__ rowres,
                                                         double *__restrict__ lse_out,
                                                         float *__restrict__ kl_rows) {
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= rows) return;
+  const int64_t r = r0 + (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= r1) return;
   MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
   for (int c = 0; c < f.C; ++c) {
     const double *s = stats + (r * f.C + c) * 5;
@@ -213,20 +216,45 @@ __device__ __forceinline__ double block_sum_f64(double v, double *lds) {
 }
 
 // Pass 2: per (chunk, row) partial of sum min(exp(a - A), exp(b - B)).
+// Pass 2 also combines the row's chunk statistics (in chunk order, the same
+// arithmetic in every workgroup of the row) into A, B and KL; chunk 0 records
+// them for the final means.
 __global__ __launch_bounds__(kThreads) void ear_kernel(const float *__restrict__ a,
                                                        const float *__restrict__ b, int64_t rows,
                                                        int64_t vocab, Fid f,
-                                                       const double *__restrict__ rowres,
+                                                       const double *__restrict__ stats,
+                                                       double *__restrict__ rowres,
+                                                       float *__restrict__ kl_rows,
                                                        double *__restrict__ earpart) {
   __shared__ double lds[kThreads / kWave];
+  __shared__ double ab[2];
   const int c = blockIdx.x;
-  const int64_t row = rows - 1 - blockIdx.y;   // reverse of pass 1's order
+  const int64_t row = rows - 1 - blockIdx.y;   // reverse of pass 1: recent rows are still cached
+  if (threadIdx.x == 0) {
+    MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
+    for (int cc = 0; cc < f.C; ++cc) {
+      const double *st = stats + (row * f.C + cc) * 5;
+      ta = mz_combine(ta, MZ{st[0], st[1], st[2]});
+      tb = mz_combine(tb, MZ{st[3], st[4], 0.0});
+    }
+    const double A = ta.m + log(ta.z), B = tb.m + log(tb.z);
+    ab[0] = A;
+    ab[1] = B;
+    if (c == 0) {
+      const double kl = ta.u / ta.z - (A - B);
+      rowres[row * 4 + 0] = A;
+      rowres[row * 4 + 1] = B;
+      rowres[row * 4 + 2] = kl;
+      kl_rows[row] = (float)kl;
+    }
+  }
+  __syncthreads();
   const int64_t beg = (int64_t)c * f.chunk;
   const int64_t end = std::min<int64_t>(beg + f.chunk, vocab);
   // a - A is formed as (a - A_hi) - A_lo with A = A_hi + A_lo split into two
   // floats: the first subtraction is exact wherever p is not negligible, so
   // the exponent keeps full fp32 accuracy even for logits far from zero.
-  const double Ad = rowres[row * 4 + 0], Bd = rowres[row * 4 + 1];
+  const double Ad = ab[0], Bd = ab[1];
   const float Ahi = (float)Ad, Alo = (float)(Ad - (double)Ahi);
   const float Bhi = (float)Bd, Blo = (float)(Bd - (double)Bhi);
   const float *ar = a + row * vocab;
@@ -237,16 +265,16 @@ __global__ __launch_bounds__(kThreads) void ear_kernel(const float *__restrict__
     const float4 *b4 = reinterpret_cast<const float4 *>(br);
     for (int64_t i = beg / 4 + threadIdx.x; i < end / 4; i += kThreads) {
       const float4 va = a4[i], vb = b4[i];
-      const float p0 = fast_exp((va.x - Ahi) - Alo), q0 = fast_exp((vb.x - Bhi) - Blo);
-      const float p1 = fast_exp((va.y - Ahi) - Alo), q1 = fast_exp((vb.y - Bhi) - Blo);
-      const float p2 = fast_exp((va.z - Ahi) - Alo), q2 = fast_exp((vb.z - Bhi) - Blo);
-      const float p3 = fast_exp((va.w - Ahi) - Alo), q3 = fast_exp((vb.w - Bhi) - Blo);
-      acc += (double)((fminf(p0, q0) + fminf(p1, q1)) + (fminf(p2, q2) + fminf(p3, q3)));
+      // min(e^x, e^y) = e^min(x, y): one exponential per element
+      const float m0 = fast_exp(fminf((va.x - Ahi) - Alo, (vb.x - Bhi) - Blo));
+      const float m1 = fast_exp(fminf((va.y - Ahi) - Alo, (vb.y - Bhi) - Blo));
+      const float m2 = fast_exp(fminf((va.z - Ahi) - Alo, (vb.z - Bhi) - Blo));
+      const float m3 = fast_exp(fminf((va.w - Ahi) - Alo, (vb.w - Bhi) - Blo));
+      acc += (double)((m0 + m1) + (m2 + m3));
     }
   } else {
     for (int64_t i = beg + threadIdx.x; i < end; i += kThreads) {
-      const float p = fast_exp((ar[i] - Ahi) - Alo), q = fast_exp((br[i] - Bhi) - Blo);
-      acc += (double)fminf(p, q);
+      acc += (double)fast_exp(fminf((ar[i] - Ahi) - Alo, (br[i] - Bhi) - Blo));
     }
   }
   const double t = block_sum_f64(acc, lds);
@@ -288,11 +316,11 @@ hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *l
   const Fid f = fid_plan(rows, vocab);
   double *stats = static_cast<double *>(ws);
   hipLaunchKernelGGL((stats_kernel<false>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a,
-                     nullptr, vocab, f, stats);
+                     nullptr, vocab, f, (int64_t)0, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, stats, rows, f, nullptr, lse, nullptr);
+                     dim3(kThreads), 0, s, stats, (int64_t)0, rows, f, nullptr, lse, nullptr);
   return hipGetLastError();
 }
 
@@ -303,14 +331,11 @@ hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t v
   double *rowres = stats + (size_t)rows * f.C * 5;
   double *earpart = rowres + (size_t)rows * 4;
   hipLaunchKernelGGL((stats_kernel<true>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
-                     vocab, f, stats);
+                     vocab, f, (int64_t)0, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rows_kernel<true>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, stats, rows, f, rowres, nullptr, kl);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(ear_kernel, dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b, rows,
-                     vocab, f, rowres, earpart);
+  hipLaunchKernelGGL(ear_kernel, dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
+                     (int64_t)rows, vocab, f, stats, rowres, kl, earpart);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(final_kernel, dim3(1), dim3(kThreads), 0, s, earpart, rowres, rows, f, ear,
                      means);
