@@ -32,11 +32,21 @@ constexpr int kThreads = 256;
 #ifndef SLQ_GEMM_MTILES
 #define SLQ_GEMM_MTILES 4
 #endif
-constexpr int kMT = SLQ_GEMM_MTILES;   // 32-row MFMA tiles per wavefront
-constexpr int kBM = 32 * kMT;      // m extent of a workgroup tile
-constexpr int kBN = 256;           // n extent of a workgroup tile (64 per wavefront)
-constexpr int kBK = 64;            // k per step
-constexpr int kPitch = kBK + 8;    // bf16 elements per LDS row (padding vs bank conflicts)
+#ifndef SLQ_GEMM_NTILES
+#define SLQ_GEMM_NTILES 2
+#endif
+#ifndef SLQ_GEMM_WAVES_M
+#define SLQ_GEMM_WAVES_M 1
+#endif
+constexpr int kMT = SLQ_GEMM_MTILES;    // 32-row MFMA tiles per wavefront
+constexpr int kNTW = SLQ_GEMM_NTILES;   // 32-column MFMA tiles per wavefront
+constexpr int kWM = SLQ_GEMM_WAVES_M;   // wavefronts along m (the rest along n)
+constexpr int kWN = 4 / kWM;
+constexpr int kBM = 32 * kMT * kWM;     // m extent of a workgroup tile
+constexpr int kBN = 32 * kNTW * kWN;    // n extent of a workgroup tile
+constexpr int kBK = 64;                 // k per step
+constexpr int kPitch = kBK + 8;         // bf16 elements per LDS row (padding vs bank conflicts)
+constexpr size_t kLdsBytes = (size_t)2 * kBM * kPitch * 2;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -163,16 +173,19 @@ __device__ __forceinline__ u32x4_t dequant_slice(const Chunk<BITS> &c, const Deq
 }
 
 template <int BITS>
-__global__ __launch_bounds__(kThreads, kMT > 4 ? 1 : 2) void gemm_kernel(
+__global__ __launch_bounds__(kThreads, kMT * kNTW > 8 ? 1 : 2) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     float *__restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kPitch];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_x[];
+  uint16_t *As[2] = {lds_x, lds_x + kBM * kPitch};
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / kWN, wn = wave % kWN;
   const int c32 = lane & 31, h = lane >> 5;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN + 64 * wave;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN + 32 * kNTW * wn;
+  const int am = 32 * kMT * wm;   // first LDS activation row of this wave
   const int G = K / kGroup;
   const int64_t wpr = (int64_t)K * BITS / 32;
   const int steps = K / kBK;
@@ -201,32 +214,32 @@ __global__ __launch_bounds__(kThreads, kMT > 4 ? 1 : 2) void gemm_kernel(
 
   // weights: column n = n0 + 32t + c32 (rows past N are read, never stored);
   // the lane's chunk of step st is chunk 2*st + h of the row
-  const uint32_t *crow[2];
-  const float *srow[2];
-  const uint8_t *zrow[2];
+  const uint32_t *crow[kNTW];
+  const float *srow[kNTW];
+  const uint8_t *zrow[kNTW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kNTW; ++t) {
     const int n = min(n0 + 32 * t + c32, N - 1);
     crow[t] = codes + (int64_t)n * wpr + h * BITS;
     srow[t] = scales + (int64_t)n * G;
     zrow[t] = zeros + (int64_t)n * G;
   }
   // chunks, scale and zero point of step st (a step is half a 128-group)
-  auto load_w = [&](int st, Chunk<BITS> (&c)[2], float (&sv)[2], uint32_t (&zv)[2]) {
+  auto load_w = [&](int st, Chunk<BITS> (&c)[kNTW], float (&sv)[kNTW], uint32_t (&zv)[kNTW]) {
     const int g = (st * kBK) / kGroup;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kNTW; ++t) {
       c[t] = load_chunk<BITS>(crow[t] + (int64_t)st * 2 * BITS);
       sv[t] = srow[t][g];
       zv[t] = zrow[t][g];
     }
   };
 
-  f32x16_t acc[kMT][2];
+  f32x16_t acc[kMT][kNTW];
 #pragma unroll
   for (int i = 0; i < kMT; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < kNTW; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
@@ -237,9 +250,9 @@ __global__ __launch_bounds__(kThreads, kMT > 4 ? 1 : 2) void gemm_kernel(
   // wait for it); loads complete in issue order, so waiting for x(st+1) at
   // the end of step st does not wait for the step-st requests.
   u32x4_t xA[XR][4], xB[XR][4];
-  Chunk<BITS> wA[2], wB[2];
-  float sA[2], sB[2];
-  uint32_t zA[2], zB[2];
+  Chunk<BITS> wA[kNTW], wB[kNTW];
+  float sA[kNTW], sB[kNTW];
+  uint32_t zA[kNTW], zB[kNTW];
   load_x(0, xA);
   store_x(0, xA);
   load_w(0, wA, sA, zA);
@@ -250,26 +263,36 @@ __global__ __launch_bounds__(kThreads, kMT > 4 ? 1 : 2) void gemm_kernel(
   // step st: issue x(st+2) into xi, run the MFMAs on w (= w(st)) dequantized
   // slice by slice, refill that slot with w(st+2), store xs (= x(st+1)) to the
   // other buffer
-  auto step = [&](int st, u32x4_t (&xi)[XR][4], const u32x4_t (&xs)[XR][4], Chunk<BITS> (&w)[2],
-                  float (&sw)[2], uint32_t (&zw)[2]) {
+  auto step = [&](int st, u32x4_t (&xi)[XR][4], const u32x4_t (&xs)[XR][4], Chunk<BITS> (&w)[kNTW],
+                  float (&sw)[kNTW], uint32_t (&zw)[kNTW]) {
     const int buf = st & 1;
     const int n2 = min(st + 2, steps - 1);   // past the end: reload the last step (discarded)
     load_x(n2, xi);
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
-    const Deq d[2] = {make_deq(sw[0], zw[0]), make_deq(sw[1], zw[1])};
+    Deq d[kNTW];
+#pragma unroll
+    for (int t = 0; t < kNTW; ++t) d[t] = make_deq(sw[t], zw[t]);
+    // k slots 8h+t of MFMA slice ks <-> k = 32h + 8ks + t within the step; the
+    // A operands of slice ks+1 are read from LDS before slice ks's MFMAs
+    auto read_a = [&](int ks, u32x4_t (&a)[kMT]) {
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+        a[i] = *reinterpret_cast<const u32x4_t *>(&As[buf][(am + 32 * i + c32) * kPitch + 32 * h + 8 * ks]);
+    };
+    u32x4_t a0[kMT], a1[kMT];
+    read_a(0, a0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      // k slots 8h+t of MFMA step ks <-> k = 32h + 8ks + t within the step
-      u32x4_t a[kMT], b[2];
+      u32x4_t(&a)[kMT] = (ks & 1) ? a1 : a0;
+      u32x4_t(&an)[kMT] = (ks & 1) ? a0 : a1;
+      if (ks + 1 < 4) read_a(ks + 1, an);
+      u32x4_t b[kNTW];
+#pragma unroll
+      for (int t = 0; t < kNTW; ++t) b[t] = dequant_slice<BITS>(w[t], d[t], ks);
 #pragma unroll
       for (int i = 0; i < kMT; ++i)
-        a[i] = *reinterpret_cast<const u32x4_t *>(&As[buf][(32 * i + c32) * kPitch + 32 * h + 8 * ks]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) b[t] = dequant_slice<BITS>(w[t], d[t], ks);
-#pragma unroll
-      for (int i = 0; i < kMT; ++i)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], b[t], acc[i][t]);
+        for (int t = 0; t < kNTW; ++t) acc[i][t] = mfma32(a[i], b[t], acc[i][t]);
     }
     load_w(n2, w, sw, zw);   // the slot is free once its last slice is dequantized
     if (st + 1 < steps) store_x(buf ^ 1, xs);
@@ -281,14 +304,14 @@ __global__ __launch_bounds__(kThreads, kMT > 4 ? 1 : 2) void gemm_kernel(
   }
 
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kNTW; ++t) {
     const int n = n0 + 32 * t + c32;
     if (n >= N) continue;
 #pragma unroll
     for (int i = 0; i < kMT; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
+        const int m = m0 + am + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
         if (m < M) y[(int64_t)m * N + n] = acc[i][t][e];
       }
   }
@@ -298,9 +321,16 @@ template <int BITS>
 hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const float *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
                      hipStream_t st) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) {
+    (void)hipGetLastError();   // leave no sticky error behind for later calls
+    return attr;
+  }
   const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gemm_kernel<BITS>), grid, dim3(kThreads), 0, st, x, codes, scales, zeros,
-                     (int)m, (int)n, (int)k, y);
+  hipLaunchKernelGGL((gemm_kernel<BITS>), grid, dim3(kThreads), kLdsBytes, st, x, codes, scales,
+                     zeros, (int)m, (int)n, (int)k, y);
   return hipGetLastError();
 }
 
