@@ -36,6 +36,8 @@ def load(path: str):
     L.oracle_gemm_pairs.argtypes = [_u16p, _i64, _f32p, _i64p, _i64p, _i64, _f64p, _f64p]
     L.oracle_row_lse.argtypes = [_f32p, _i64, _i64, _f64p]
     L.oracle_ear_kl.argtypes = [_f32p, _f32p, _i64, _i64, _f64p, _f64p, _f64p]
+    L.oracle_ear_kl_topk.argtypes = [_f32p, _f32p, _i64, _i64, _i64, ctypes.c_double, _f64p, _f64p,
+                                     _f64p]
     L.oracle_quant_error.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _int, _f64p]
     L.oracle_bits_per_param.argtypes = [_int, _int, _int]
     L.oracle_bits_per_param.restype = ctypes.c_double
@@ -143,6 +145,21 @@ def ear_kl(a, b):
     kl = np.empty(rows, np.float64)
     means = np.empty(2, np.float64)
     lib().oracle_ear_kl(a, b, rows, vocab, ear, kl, means)
+    return ear, kl, means
+
+
+def ear_kl_topk(a, b, k: int, temperature: float = 1.0):
+    """Per-row top-K EAR and top-K KL(p||q) at a temperature (fp64), plus means.
+    The top-K set is the K largest reference logits, ties to the lower index."""
+    a = _c(a, np.float32)
+    b = _c(b, np.float32)
+    rows, vocab = a.shape
+    if not (1 <= k <= min(vocab, 4096)):
+        raise ValueError("k must be in [1, min(vocab, 4096)]")
+    ear = np.empty(rows, np.float64)
+    kl = np.empty(rows, np.float64)
+    means = np.empty(2, np.float64)
+    lib().oracle_ear_kl_topk(a, b, rows, vocab, k, float(temperature), ear, kl, means)
     return ear, kl, means
 
 

@@ -234,6 +234,17 @@ void oracle_row_lse(const float *a, int64_t rows, int64_t vocab, double *lse) {
   for (int64_t r = 0; r < rows; ++r) lse[r] = row_lse(a + r * vocab, vocab);
 }
 
+/* Arithmetic means over rows (positions) of the per-row EAR and KL. */
+static void row_means(const double *ear, const double *kl, int64_t rows, double *means) {
+  double se = 0.0, sk = 0.0;
+  for (int64_t r = 0; r < rows; ++r) {
+    se += ear[r];
+    sk += kl[r];
+  }
+  means[0] = rows > 0 ? se / (double)rows : 0.0;
+  means[1] = rows > 0 ? sk / (double)rows : 0.0;
+}
+
 /*
  * Fidelity of a quantized model's next-token distribution q against the
  * reference p, per row (position):
@@ -263,13 +274,65 @@ void oracle_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab,
     ear[r] = e;
     kl[r] = d;
   }
-  double se = 0.0, sk = 0.0;
+  row_means(ear, kl, rows, means);
+}
+
+/*
+ * Top-K fidelity ([SLQ-gist] Methodology 2: EAR summed over the top-K tokens
+ * of each position; [SLQ-readme] Evaluation: EAR and top-K KL of a model
+ * against its base), at temperature T > 0:
+ *   p = softmax(a / T), q = softmax(b / T) over the full vocabulary;
+ *   S_r = the K tokens of largest p (equivalently largest a), ties to the
+ *         lower token index (reading R16);
+ *   EAR_r = sum_{v in S_r} min(p_v, q_v),
+ *   KL_r  = sum_{v in S_r} p_v (log p_v - log q_v)   (natural log),
+ * with no renormalization over S_r (R17), and the means over rows.
+ * K = vocab and T = 1 give oracle_ear_kl.
+ */
+static double row_lse_t(const float *a, int64_t vocab, double T) {
+  double m = -INFINITY;
+  for (int64_t v = 0; v < vocab; ++v)
+    if ((double)a[v] / T > m) m = (double)a[v] / T;
+  double z = 0.0;
+  for (int64_t v = 0; v < vocab; ++v) z += exp((double)a[v] / T - m);
+  return m + log(z);
+}
+
+void oracle_ear_kl_topk(const float *a, const float *b, int64_t rows, int64_t vocab, int64_t K,
+                        double T, double *ear, double *kl, double *means) {
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
-    se += ear[r];
-    sk += kl[r];
+    const float *ar = a + r * vocab;
+    const float *br = b + r * vocab;
+    /* selection: best[0..cnt) sorted by (value desc, index asc); scanning in
+       index order, a later token displaces a kept one only when strictly larger */
+    int64_t best[4096];
+    int64_t cnt = 0;
+    for (int64_t v = 0; v < vocab; ++v) {
+      if (cnt == K && !(ar[v] > ar[best[K - 1]])) continue;
+      int64_t pos = (cnt < K) ? cnt : K - 1;
+      while (pos > 0 && ar[v] > ar[best[pos - 1]]) {
+        best[pos] = best[pos - 1];
+        --pos;
+      }
+      best[pos] = v;
+      if (cnt < K) ++cnt;
+    }
+    const double A = row_lse_t(ar, vocab, T);
+    const double B = row_lse_t(br, vocab, T);
+    double e = 0.0, d = 0.0;
+    for (int64_t i = 0; i < cnt; ++i) {
+      const int64_t v = best[i];
+      const double lp = (double)ar[v] / T - A;
+      const double lq = (double)br[v] / T - B;
+      const double p = exp(lp), q = exp(lq);
+      e += (p < q) ? p : q;
+      d += p * (lp - lq);
+    }
+    ear[r] = e;
+    kl[r] = d;
   }
-  means[0] = rows > 0 ? se / (double)rows : 0.0;
-  means[1] = rows > 0 ? sk / (double)rows : 0.0;
+  row_means(ear, kl, rows, means);
 }
 
 /*

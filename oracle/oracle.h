@@ -22,6 +22,8 @@ void oracle_gemm_pairs(const uint16_t *x, int64_t k, const float *w_hat_rows,
 void oracle_row_lse(const float *a, int64_t rows, int64_t vocab, double *lse);
 void oracle_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab,
                    double *ear, double *kl, double *means);
+void oracle_ear_kl_topk(const float *a, const float *b, int64_t rows, int64_t vocab, int64_t K,
+                        double T, double *ear, double *kl, double *means);
 void oracle_quant_error(const float *W, const float *w_hat, const float *scales,
                         int64_t n, int64_t k, int group, double *out);
 double oracle_bits_per_param(int bits, int meta_bits, int group);

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from tests import (test_oracle_fidelity, test_oracle_gamma, test_oracle_gemm,
-                   test_oracle_pack, test_oracle_quant)
+                   test_oracle_pack, test_oracle_quant, test_oracle_topk)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 HDR_DIR = os.path.dirname(SRC)
@@ -37,9 +37,20 @@ MUTANTS = {
     "gemm_transposed_weight": ("double wv = (double)w_hat[c * k + j];", "double wv = (double)w_hat[j * n + c];"),
     "gemm_bound_without_abs": ("b += fabs(xv) * fabs(wv);\n      }\n      y[i",
                                "b += xv * wv;\n      }\n      y[i"),
-    "lse_drops_max": ("return m + log(z);", "return log(z);"),
-    "ear_max_not_min": ("e += (p < q) ? p : q;", "e += (p > q) ? p : q;"),
-    "kl_reversed": ("d += p * (lp - lq);", "d += q * (lq - lp);"),
+    "lse_drops_max": ("z += exp((double)a[v] - m);\n  return m + log(z);",
+                      "z += exp((double)a[v] - m);\n  return log(z);"),
+    "ear_max_not_min": ("double q = exp(lq);\n      e += (p < q) ? p : q;",
+                        "double q = exp(lq);\n      e += (p > q) ? p : q;"),
+    "kl_reversed": ("double q = exp(lq);\n      e += (p < q) ? p : q;\n      d += p * (lp - lq);",
+                    "double q = exp(lq);\n      e += (p < q) ? p : q;\n      d += q * (lq - lp);"),
+    "topk_tie_to_higher_index": ("if (cnt == K && !(ar[v] > ar[best[K - 1]])) continue;",
+                                 "if (cnt == K && !(ar[v] >= ar[best[K - 1]])) continue;"),
+    "topk_selects_smallest": ("while (pos > 0 && ar[v] > ar[best[pos - 1]]) {",
+                              "while (pos > 0 && ar[v] < ar[best[pos - 1]]) {"),
+    "topk_ear_max_not_min": ("const double p = exp(lp), q = exp(lq);\n      e += (p < q) ? p : q;",
+                             "const double p = exp(lp), q = exp(lq);\n      e += (p > q) ? p : q;"),
+    "topk_temperature_only_on_p": ("const double lq = (double)br[v] / T - B;",
+                                   "const double lq = (double)br[v] - B;"),
     "kl_wrong_normalizer_sign": ("double lq = (double)br[v] - B;", "double lq = (double)br[v] + B;"),
     "mean_over_rows_minus_one": ("means[0] = rows > 0 ? se / (double)rows : 0.0;",
                                  "means[0] = rows > 1 ? se / (double)(rows - 1) : 0.0;"),
@@ -52,7 +63,7 @@ def _pin_calls():
     """Every pin with every parameter value, as zero-argument callables."""
     calls = []
     for mod in (test_oracle_quant, test_oracle_pack, test_oracle_gemm,
-                test_oracle_fidelity, test_oracle_gamma):
+                test_oracle_fidelity, test_oracle_gamma, test_oracle_topk):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
