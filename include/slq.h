@@ -169,6 +169,30 @@ slq_status slq_ear_kl(const float *logits_p, const float *logits_q, int64_t rows
                       float *ear_rows, float *kl_rows, double *means, void *workspace,
                       slq_stream stream);
 
+/* Largest K slq_ear_kl_topk accepts. */
+#define SLQ_TOPK_MAX 64
+
+/*
+ * Top-K fidelity at a temperature (gist.science summary, Methodology 2: EAR
+ * taken over the top-K tokens of each position; README, Evaluation: top-K KL).
+ * With p = softmax(a / T), q = softmax(b / T) over the full vocabulary and
+ * S_r the K tokens with the largest reference logits a[r][.] (equal logits:
+ * the lower token index first):
+ *   EAR_r = sum_{v in S_r} min(p_v, q_v)
+ *   KL_r  = sum_{v in S_r} p_v log(p_v / q_v)      (no renormalization over S_r)
+ * and means[0] = mean_r EAR_r, means[1] = mean_r KL_r.  K = vocab gives the
+ * full-vocabulary metrics of slq_ear_kl.
+ * In : logits_p (reference), logits_q: fp32 [rows][vocab] (device, 16-byte
+ *      aligned); 1 <= K <= min(vocab, SLQ_TOPK_MAX); temperature finite, > 0.
+ * Out: ear_rows, kl_rows fp32 [rows]; means fp64 [2].
+ * workspace: slq_ear_kl_workspace_bytes(rows, vocab) bytes, 256-byte aligned.
+ * Errors: SLQ_EINVAL for K or temperature out of range and for the argument
+ * faults slq_ear_kl rejects.  Deterministic: repeated calls are bit-equal.
+ */
+slq_status slq_ear_kl_topk(const float *logits_p, const float *logits_q, int64_t rows,
+                           int64_t vocab, int64_t K, double temperature, float *ear_rows,
+                           float *kl_rows, double *means, void *workspace, slq_stream stream);
+
 /* Workspace bytes slq_quant_error needs for w. */
 size_t slq_quant_error_workspace_bytes(const slq_packed *w);
 

@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for name in names:
         assert hasattr(L, name), name
 
@@ -105,6 +105,21 @@ def test_fidelity_and_error_validation():
     assert L.slq_ear_kl(A, B, 4, 10, C, C + 64, D, None, None) == slq.SLQ_EINVAL   # no workspace
     assert L.slq_ear_kl(A + 4, B, 4, 12, C, C + 64, D, E, None) == slq.SLQ_EINVAL  # misaligned
     assert L.slq_ear_kl(A, B, 0, 10, None, None, None, None, None) == slq.SLQ_OK
+    T = L.slq_ear_kl_topk
+    assert T(A, B, 4, 100, 0, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL      # K = 0
+    assert T(A, B, 4, 100, 65, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL     # K > SLQ_TOPK_MAX
+    assert T(A, B, 4, 8, 9, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL        # K > vocab
+    assert T(A, B, 4, 100, 10, 0.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL     # T = 0
+    assert T(A, B, 4, 100, 10, -1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL
+    assert T(A, B, 4, 100, 10, float("nan"), C, C + 64, D, E, None) == slq.SLQ_EINVAL
+    assert T(A, B, 4, 100, 10, float("inf"), C, C + 64, D, E, None) == slq.SLQ_EINVAL
+    assert T(A, B, 4, 100, 10, 1e-300, C, C + 64, D, E, None) == slq.SLQ_EINVAL  # log2(e)/T overflows fp32
+    assert T(A, B, 4, 100, 10, 1e300, C, C + 64, D, E, None) == slq.SLQ_EINVAL   # log2(e)/T underflows
+    assert T(A, B, 4, 100, 10, 1.0, C, C, D, E, None) == slq.SLQ_EINVAL          # ear == kl
+    assert T(A, B, 4, 100, 10, 1.0, C, C + 64, D, None, None) == slq.SLQ_EINVAL  # no workspace
+    assert T(A + 4, B, 4, 100, 10, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL  # misaligned
+    assert T(A, B, 4, 0, 1, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL        # empty vocab
+    assert T(A, B, 0, 10, 5, 1.0, None, None, None, None, None) == slq.SLQ_OK
     assert L.slq_row_lse(A, 4, 0, C, E, None) == slq.SLQ_EINVAL
     assert L.slq_row_lse(A, 4, 10, A, E, None) == slq.SLQ_EINVAL                   # lse aliases input
     assert L.slq_quant_error(A, ctypes.byref(packed(bits=1)), C, E, None) == slq.SLQ_EINVAL

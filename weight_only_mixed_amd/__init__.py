@@ -56,6 +56,8 @@ def lib():
         L.slq_ear_kl_workspace_bytes.restype = _sz
         L.slq_row_lse.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
         L.slq_ear_kl.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+        L.slq_ear_kl_topk.argtypes = [_vp, _vp, _i64, _i64, _i64, ctypes.c_double, _vp, _vp, _vp,
+                                      _vp, _vp]
         L.slq_quant_error_workspace_bytes.argtypes = [_pp]
         L.slq_quant_error_workspace_bytes.restype = _sz
         L.slq_quant_error.argtypes = [_vp, _pp, _vp, _vp, _vp]
@@ -64,7 +66,7 @@ def lib():
         L.slq_strerror.argtypes = [_int]
         L.slq_strerror.restype = ctypes.c_char_p
         for f in ("slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm", "slq_row_lse",
-                  "slq_ear_kl", "slq_quant_error"):
+                  "slq_ear_kl", "slq_ear_kl_topk", "slq_quant_error"):
             getattr(L, f).restype = _int
         _LIB = L
     return _LIB
@@ -201,6 +203,24 @@ def slq_ear_kl(logits_p: torch.Tensor, logits_q: torch.Tensor):
     return ear, kl, means
 
 
+def slq_ear_kl_topk(logits_p: torch.Tensor, logits_q: torch.Tensor, k: int,
+                    temperature: float = 1.0):
+    """Top-k EAR and top-k KL(p||q) at a temperature, per row (fp32), and their
+    means (fp64 [2]) on the device."""
+    assert logits_p.shape == logits_q.shape and logits_p.dtype == torch.float32
+    assert logits_p.is_contiguous() and logits_q.is_contiguous()
+    rows, vocab = logits_p.shape
+    dev = logits_p.device
+    ear = torch.empty(rows, dtype=torch.float32, device=dev)
+    kl = torch.empty(rows, dtype=torch.float32, device=dev)
+    means = torch.empty(2, dtype=torch.float64, device=dev)
+    ws = workspace(lib().slq_ear_kl_workspace_bytes(rows, vocab), dev, "fidelity")
+    _check(lib().slq_ear_kl_topk(_ptr(logits_p), _ptr(logits_q), rows, vocab, int(k),
+                                 float(temperature), _ptr(ear), _ptr(kl), _ptr(means), _ptr(ws),
+                                 _stream(logits_p)), "slq_ear_kl_topk")
+    return ear, kl, means
+
+
 def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
     """fp64 [2] on the device: (sum (w - w_hat)^2, sum_g s_g^2)."""
     desc = pw.c()
@@ -213,4 +233,4 @@ def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
 
 __all__ = ["lib", "SlqError", "SlqPacked", "PackedWeight", "alloc_packed", "workspace",
            "gemm_workspace_bytes", "kernel_name", "slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm",
-           "slq_row_lse", "slq_ear_kl", "slq_quant_error", "SLQ_ASYM", "SLQ_SYM", "GROUP"]
+           "slq_row_lse", "slq_ear_kl", "slq_ear_kl_topk", "slq_quant_error", "SLQ_ASYM", "SLQ_SYM", "GROUP"]

@@ -29,7 +29,8 @@ namespace slq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2e_d = 1.4426950408889634;
+constexpr float kLog2e = (float)kLog2e_d;
 
 struct Fid {
   int C;          // chunks per row
@@ -59,42 +60,46 @@ __device__ __forceinline__ float fast_exp(float v) { return exp2f(v * kLog2e); }
 struct MZ {
   double m, z, u;
 };
-__device__ __forceinline__ MZ mz_combine(MZ p, MZ q) {
+// invT: the sums are of exp((x - m) * invT) (a softmax at temperature 1 / invT).
+__device__ __forceinline__ MZ mz_combine(MZ p, MZ q, double invT = 1.0) {
   if (q.m == -INFINITY) return p;
   if (p.m == -INFINITY) return q;
   const double M = p.m > q.m ? p.m : q.m;
-  const double fp = exp(p.m - M), fq = exp(q.m - M);
+  const double fp = exp((p.m - M) * invT), fq = exp((q.m - M) * invT);
   return MZ{M, p.z * fp + q.z * fq, p.u * fp + q.u * fq};
 }
 __device__ __forceinline__ MZ mz_shfl(MZ v, int o) {
   return MZ{__shfl_xor(v.m, o, kWave), __shfl_xor(v.z, o, kWave), __shfl_xor(v.u, o, kWave)};
 }
-__device__ MZ mz_block(MZ v, MZ *lds) {
+__device__ MZ mz_block(MZ v, MZ *lds, double invT) {
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = mz_combine(v, mz_shfl(v, o));
+  for (int o = 1; o < kWave; o <<= 1) v = mz_combine(v, mz_shfl(v, o), invT);
   const int wave = threadIdx.x / kWave;
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) lds[wave] = v;
   __syncthreads();
   MZ t = lds[0];
-  for (int i = 1; i < kThreads / kWave; ++i) t = mz_combine(t, lds[i]);
+  for (int i = 1; i < kThreads / kWave; ++i) t = mz_combine(t, lds[i], invT);
   return t;
 }
 
-// Online update of (m, z, u) with 4 new values of a (u only when WITH_U).
+// Online update of (m, z, u) with 4 new values of a (u only when WITH_U); the
+// terms are exp2((a - m) * c) with c = log2(e) / temperature.  The shift by the
+// running maximum comes before the scaling, so large logits lose nothing to it.
 // The difference a - b enters u in fp64, where it is exact: with logits far
 // from zero an fp32 difference would lose more than the KL being measured.
 template <bool WITH_U>
-__device__ __forceinline__ void online4(float4 a, float4 b, float &m, double &z, double &u) {
+__device__ __forceinline__ void online4(float4 a, float4 b, float &m, double &z, double &u,
+                                        float c) {
   const float mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
   if (mx > m) {
-    const float f = fast_exp(m - mx);   // m = -inf gives 0
+    const float f = exp2f((m - mx) * c);   // m = -inf gives 0
     z *= (double)f;
     if (WITH_U) u *= (double)f;
     m = mx;
   }
-  const float e0 = fast_exp(a.x - m), e1 = fast_exp(a.y - m), e2 = fast_exp(a.z - m),
-              e3 = fast_exp(a.w - m);
+  const float e0 = exp2f((a.x - m) * c), e1 = exp2f((a.y - m) * c), e2 = exp2f((a.z - m) * c),
+              e3 = exp2f((a.w - m) * c);
   if (!WITH_U) {
     z += (double)((e0 + e1) + (e2 + e3));
   } else {
@@ -113,23 +118,27 @@ __device__ __forceinline__ void online4(float4 a, float4 b, float &m, double &z,
 
 // Online update with one value (rows whose length is not a multiple of 4).
 template <bool WITH_U>
-__device__ __forceinline__ void online1(float a, float b, float &m, double &z, double &u) {
+__device__ __forceinline__ void online1(float a, float b, float &m, double &z, double &u,
+                                        float c) {
   if (a > m) {
-    const float f = fast_exp(m - a);
+    const float f = exp2f((m - a) * c);
     z *= (double)f;
     if (WITH_U) u *= (double)f;
     m = a;
   }
-  const float e = fast_exp(a - m);
+  const float e = exp2f((a - m) * c);
   z += (double)e;
   if (WITH_U) u = fma((double)e, (double)a - (double)b, u);
 }
 
 // Pass 1: per (chunk, row) partial (m_a, Z_a, U, m_b, Z_b).
+// At temperature T: escale = log2(e) / T and invT = 1 / T (log2(e) and 1 for
+// the plain metrics); m stays in the logits' own units.
 template <bool WITH_B>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const float *__restrict__ a,
                                                          const float *__restrict__ b,
                                                          int64_t vocab, Fid f, int64_t r0,
+                                                         float escale, double invT,
                                                          double *__restrict__ stats) {
   __shared__ MZ lds[kThreads / kWave];
   const int c = blockIdx.x;
@@ -149,23 +158,23 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const float *__restrict
       const float4 va = a4[i];
       if (WITH_B) {
         const float4 vb = b4[i];
-        online4<true>(va, vb, ma, za, ua);
-        online4<false>(vb, vb, mb, zb, ub);
+        online4<true>(va, vb, ma, za, ua, escale);
+        online4<false>(vb, vb, mb, zb, ub, escale);
       } else {
-        online4<false>(va, va, ma, za, ua);
+        online4<false>(va, va, ma, za, ua, escale);
       }
     }
   } else {
     for (int64_t i = beg + threadIdx.x; i < end; i += kThreads) {
       const float va = ar[i];
       const float vb = WITH_B ? br[i] : 0.f;
-      online1<WITH_B>(va, vb, ma, za, ua);
-      if (WITH_B) online1<false>(vb, vb, mb, zb, ub);
+      online1<WITH_B>(va, vb, ma, za, ua, escale);
+      if (WITH_B) online1<false>(vb, vb, mb, zb, ub, escale);
     }
   }
-  const MZ ra = mz_block(MZ{(double)ma, za, ua}, lds);
+  const MZ ra = mz_block(MZ{(double)ma, za, ua}, lds, invT);
   MZ rb{0.0, 0.0, 0.0};
-  if (WITH_B) rb = mz_block(MZ{(double)mb, zb, 0.0}, lds);
+  if (WITH_B) rb = mz_block(MZ{(double)mb, zb, 0.0}, lds, invT);
   if (threadIdx.x == 0) {
     double *o = stats + (row * f.C + c) * 5;
     o[0] = ra.m;
@@ -304,6 +313,143 @@ __global__ __launch_bounds__(kThreads) void final_kernel(const double *__restric
   }
 }
 
+// ---- top-K EAR / top-K KL ----
+// A token's selection key: larger logit first, then lower index.  Float bits
+// are mapped to an order-preserving unsigned integer in the high half; the
+// complemented index fills the low half.
+__device__ __forceinline__ uint64_t topk_key(float v, uint32_t idx) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+template <int KT>
+__device__ __forceinline__ void topk_insert(uint64_t (&list)[KT], uint64_t key) {
+  // list is sorted descending; keys are unique (distinct indices)
+  if (key <= list[KT - 1]) return;
+  list[KT - 1] = key;
+#pragma unroll
+  for (int i = KT - 1; i > 0; --i) {
+    const uint64_t hi = list[i - 1], lo = list[i];
+    list[i - 1] = hi > lo ? hi : lo;
+    list[i] = hi > lo ? lo : hi;
+  }
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+// One workgroup per row: the row's normalizers from the chunk statistics, a
+// per-thread top-KT list over the row, k rounds of block-wide maximum to
+// pick the row's k tokens, then EAR and KL terms of those tokens in fp64.
+template <int KT>
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ a,
+                                                        const float *__restrict__ b, int64_t vocab,
+                                                        Fid f, int k, double invT,
+                                                        const double *__restrict__ stats,
+                                                        double *__restrict__ rowres,
+                                                        float *__restrict__ ear_rows,
+                                                        float *__restrict__ kl_rows) {
+  __shared__ double ab[4];   // m_a, log Z_a, m_b, log Z_b
+  __shared__ uint64_t wbest[kThreads / kWave];
+  __shared__ uint32_t sel[KT];
+  const int64_t row = blockIdx.x;
+  const float *ar = a + row * vocab;
+  const float *br = b + row * vocab;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (threadIdx.x == 0) {
+    MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
+    for (int c = 0; c < f.C; ++c) {
+      const double *st = stats + (row * f.C + c) * 5;
+      ta = mz_combine(ta, MZ{st[0], st[1], 0.0}, invT);
+      tb = mz_combine(tb, MZ{st[3], st[4], 0.0}, invT);
+    }
+    ab[0] = ta.m;
+    ab[1] = log(ta.z);
+    ab[2] = tb.m;
+    ab[3] = log(tb.z);
+  }
+  uint64_t list[KT];
+#pragma unroll
+  for (int i = 0; i < KT; ++i) list[i] = 0;   // below every real key
+  if ((vocab & 3) == 0) {
+    const float4 *a4 = reinterpret_cast<const float4 *>(ar);
+    for (int64_t i = threadIdx.x; i < vocab / 4; i += kThreads) {
+      const float4 v = a4[i];
+      const uint32_t base = (uint32_t)(4 * i);
+      topk_insert<KT>(list, topk_key(v.x, base));
+      topk_insert<KT>(list, topk_key(v.y, base + 1));
+      topk_insert<KT>(list, topk_key(v.z, base + 2));
+      topk_insert<KT>(list, topk_key(v.w, base + 3));
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < vocab; i += kThreads) topk_insert<KT>(list, topk_key(ar[i], (uint32_t)i));
+  }
+  // k rounds: the largest head across the workgroup wins and is popped
+  for (int j = 0; j < k; ++j) {
+    const uint64_t w = wave_max_u64(list[0]);
+    if (lane == 0) wbest[wave] = w;
+    __syncthreads();
+    uint64_t best = wbest[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / kWave; ++i) best = best > wbest[i] ? best : wbest[i];
+    if (list[0] == best) {   // unique owner
+#pragma unroll
+      for (int i = 0; i < KT - 1; ++i) list[i] = list[i + 1];
+      list[KT - 1] = 0;
+    }
+    if (threadIdx.x == 0) sel[j] = 0xFFFFFFFFu - (uint32_t)best;
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  double e = 0.0, d = 0.0;
+  if (lane < k) {
+    const uint32_t v = sel[lane];
+    const double lp = ((double)ar[v] - ab[0]) * invT - ab[1];
+    const double lq = ((double)br[v] - ab[2]) * invT - ab[3];
+    const double p = exp(lp), q = exp(lq);
+    e = p < q ? p : q;
+    d = p * (lp - lq);
+  }
+  // fixed-shape tree sum over the wave
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    e += __shfl_xor(e, o, kWave);
+    d += __shfl_xor(d, o, kWave);
+  }
+  if (lane == 0) {
+    rowres[row * 4 + 2] = d;
+    rowres[row * 4 + 3] = e;
+    ear_rows[row] = (float)e;
+    kl_rows[row] = (float)d;
+  }
+}
+
+// Means of the per-row top-K EAR and KL; one workgroup, fixed order.
+__global__ __launch_bounds__(kThreads) void topk_final_kernel(const double *__restrict__ rowres,
+                                                              int64_t rows,
+                                                              double *__restrict__ means) {
+  __shared__ double lds[kThreads / kWave];
+  double se = 0.0, sk = 0.0;
+  for (int64_t r = threadIdx.x; r < rows; r += kThreads) {
+    se += rowres[r * 4 + 3];
+    sk += rowres[r * 4 + 2];
+  }
+  const double te = block_sum_f64(se, lds);
+  const double tk = block_sum_f64(sk, lds);
+  if (threadIdx.x == 0) {
+    means[0] = rows > 0 ? te / (double)rows : 0.0;
+    means[1] = rows > 0 ? tk / (double)rows : 0.0;
+  }
+}
+
 }  // namespace
 
 size_t fidelity_workspace(int64_t rows, int64_t vocab) {
@@ -316,7 +462,7 @@ hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *l
   const Fid f = fid_plan(rows, vocab);
   double *stats = static_cast<double *>(ws);
   hipLaunchKernelGGL((stats_kernel<false>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a,
-                     nullptr, vocab, f, (int64_t)0, stats);
+                     nullptr, vocab, f, (int64_t)0, kLog2e, 1.0, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
@@ -331,7 +477,7 @@ hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t v
   double *rowres = stats + (size_t)rows * f.C * 5;
   double *earpart = rowres + (size_t)rows * 4;
   hipLaunchKernelGGL((stats_kernel<true>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
-                     vocab, f, (int64_t)0, stats);
+                     vocab, f, (int64_t)0, kLog2e, 1.0, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ear_kernel, dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
@@ -339,6 +485,30 @@ hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t v
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(final_kernel, dim3(1), dim3(kThreads), 0, s, earpart, rowres, rows, f, ear,
                      means);
+  return hipGetLastError();
+}
+
+hipError_t launch_ear_kl_topk(const float *a, const float *b, int64_t rows, int64_t vocab, int k,
+                              double invT, float *ear, float *kl, double *means, void *ws,
+                              hipStream_t s) {
+  const Fid f = fid_plan(rows, vocab);
+  double *stats = static_cast<double *>(ws);
+  double *rowres = stats + (size_t)rows * f.C * 5;
+  hipLaunchKernelGGL((stats_kernel<true>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
+                     vocab, f, (int64_t)0, (float)(kLog2e_d * invT), invT, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (k <= 16)
+    hipLaunchKernelGGL((topk_kernel<16>), dim3((unsigned)rows), dim3(kThreads), 0, s, a, b, vocab,
+                       f, k, invT, stats, rowres, ear, kl);
+  else if (k <= 32)
+    hipLaunchKernelGGL((topk_kernel<32>), dim3((unsigned)rows), dim3(kThreads), 0, s, a, b, vocab,
+                       f, k, invT, stats, rowres, ear, kl);
+  else
+    hipLaunchKernelGGL((topk_kernel<kTopKMax>), dim3((unsigned)rows), dim3(kThreads), 0, s, a, b,
+                       vocab, f, k, invT, stats, rowres, ear, kl);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kThreads), 0, s, rowres, rows, means);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // C ABI of libslq: argument validation on the host, then the HIP launchers.
 // Every check runs before the first HIP call, so an invalid request returns
 // SLQ_EINVAL / SLQ_ENOTSUP with nothing enqueued and outputs untouched.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -187,12 +188,11 @@ slq_status slq_row_lse(const float *logits, int64_t rows, int64_t vocab, double 
                                       static_cast<hipStream_t>(stream)));
 }
 
-slq_status slq_ear_kl(const float *logits_p, const float *logits_q, int64_t rows, int64_t vocab,
-                      float *ear_rows, float *kl_rows, double *means, void *workspace,
-                      slq_stream stream) {
-  if (rows < 0 || vocab < 0 || rows >= kMaxDim || vocab >= kMaxDim) return SLQ_EINVAL;
-  if (rows == 0) return SLQ_OK;
-  if (vocab == 0) return SLQ_EINVAL;
+namespace {
+
+// Argument checks shared by the two EAR / KL entry points.
+slq_status check_ear_kl(const float *logits_p, const float *logits_q, int64_t rows, int64_t vocab,
+                        float *ear_rows, float *kl_rows, double *means, void *workspace) {
   const size_t lb = (size_t)(rows * vocab) * sizeof(float);
   const size_t rb = (size_t)rows * sizeof(float);
   const size_t wsb = slq_ear_kl_workspace_bytes(rows, vocab);
@@ -208,8 +208,43 @@ slq_status slq_ear_kl(const float *logits_p, const float *logits_q, int64_t rows
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outb[i], outs[j], outb[j])) return SLQ_EINVAL;
   }
+  return SLQ_OK;
+}
+
+}  // namespace
+
+slq_status slq_ear_kl(const float *logits_p, const float *logits_q, int64_t rows, int64_t vocab,
+                      float *ear_rows, float *kl_rows, double *means, void *workspace,
+                      slq_stream stream) {
+  if (rows < 0 || vocab < 0 || rows >= kMaxDim || vocab >= kMaxDim) return SLQ_EINVAL;
+  if (rows == 0) return SLQ_OK;
+  if (vocab == 0) return SLQ_EINVAL;
+  const slq_status st =
+      check_ear_kl(logits_p, logits_q, rows, vocab, ear_rows, kl_rows, means, workspace);
+  if (st != SLQ_OK) return st;
   return from_hip(slq::launch_ear_kl(logits_p, logits_q, rows, vocab, ear_rows, kl_rows, means,
                                      workspace, static_cast<hipStream_t>(stream)));
+}
+
+slq_status slq_ear_kl_topk(const float *logits_p, const float *logits_q, int64_t rows,
+                           int64_t vocab, int64_t K, double temperature, float *ear_rows,
+                           float *kl_rows, double *means, void *workspace, slq_stream stream) {
+  static_assert(SLQ_TOPK_MAX == slq::kTopKMax, "top-K limit of the header and the kernels");
+  if (rows < 0 || vocab < 0 || rows >= kMaxDim || vocab >= kMaxDim) return SLQ_EINVAL;
+  if (K < 1 || K > SLQ_TOPK_MAX || (vocab > 0 && K > vocab)) return SLQ_EINVAL;
+  if (!(temperature > 0.0) || !std::isfinite(temperature)) return SLQ_EINVAL;
+  const double invT = 1.0 / temperature;
+  // the fp32 exponent scale log2(e) / T must be finite and nonzero
+  const float c = (float)(1.4426950408889634 * invT);
+  if (!(c > 0.0f) || !std::isfinite(c)) return SLQ_EINVAL;
+  if (rows == 0) return SLQ_OK;
+  if (vocab == 0) return SLQ_EINVAL;
+  const slq_status st =
+      check_ear_kl(logits_p, logits_q, rows, vocab, ear_rows, kl_rows, means, workspace);
+  if (st != SLQ_OK) return st;
+  return from_hip(slq::launch_ear_kl_topk(logits_p, logits_q, rows, vocab, (int)K, invT, ear_rows,
+                                          kl_rows, means, workspace,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 size_t slq_quant_error_workspace_bytes(const slq_packed *w) {
