@@ -387,7 +387,7 @@ def main():
     if "fidelity" in rows_sel:
         log("bench: EAR/KL 512 x 151936")
         res = {}
-        tot_b, tot_ms = 0, 0.0
+        tot_b, tot_ms, tk_b, tk_ms = 0, 0.0, 0, 0.0
         for sigma in S.FIDELITY_SIGMAS:
             a, b = S.fidelity_logits(S.FIDELITY_ROWS, S.VOCAB, sigma, S.seed_for(5) + int(sigma * 1000))
             ad, bd = to_dev(a), to_dev(b)
@@ -402,15 +402,28 @@ def main():
             tot_b += nb
             tot_ms += ms
             mh = means.cpu().numpy()
+            # top-10 EAR / KL at temperature 1 (the form the sensitivity search uses)
+            _, _, tmeans = slq.slq_ear_kl_topk(ad, bd, 10, 1.0)
+            torch.cuda.synchronize()
+            with Timer(torch) as T:
+                for _ in range(3):
+                    slq.slq_ear_kl_topk(ad, bd, 10, 1.0)
+            tms = T.ms / 3
+            tk_b += nb
+            tk_ms += tms
+            th = tmeans.cpu().numpy()
             res[f"sigma={sigma}"] = {"ms": round(ms, 4), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
-                                     "ear_mean": float(mh[0]), "kl_mean": float(mh[1])}
+                                     "ear_mean": float(mh[0]), "kl_mean": float(mh[1]),
+                                     "top10_ms": round(tms, 4), "top10_ear_mean": float(th[0]),
+                                     "top10_kl_mean": float(th[1])}
             del ad, bd
             torch.cuda.empty_cache()
         gbs = tot_b / (tot_ms * 1e-3) / 1e9
         res["GBps"] = round(gbs, 1)
         res["frac_hbm"] = round(gbs / HBM_PEAK_GBS, 4)
+        res["top10_GBps"] = round(tk_b / (tk_ms * 1e-3) / 1e9, 1)   # same two logit tensors read
         rows["ear_kl"] = res
-        log(f"bench: EAR/KL {gbs:.1f} GB/s")
+        log(f"bench: EAR/KL {gbs:.1f} GB/s, top-10 EAR/KL {res['top10_GBps']} GB/s")
 
     # ---------------- gamma-squared ----------------
     if "gamma" in rows_sel:

@@ -79,3 +79,26 @@ def test_workload_512x151936_k10(sigma):
 def test_workload_512x151936_k64_temperature():
     a, b = S.fidelity_logits(S.FIDELITY_ROWS, S.VOCAB, 0.05, S.seed_for(7))
     check(a, b, 64, 0.8, "512x151936")
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending"])
+def test_sorted_rows(order):
+    """Rising logits admit every element to the candidate buffers (the most
+    cut-backs); falling ones admit almost none after the first."""
+    base = np.linspace(-20, 20, 40000, dtype=np.float32)
+    a = np.stack([base if order == "ascending" else base[::-1]] * 3)
+    b = (a + np.random.Generator(np.random.PCG64(2)).standard_normal(a.shape) * 0.1).astype(np.float32)
+    for k in (1, 10, 64):
+        check(a, b, k, 1.0, order)
+
+
+def test_more_rows_than_one_grid_column():
+    """70000 rows: more than one launch of the (chunk, row) grid."""
+    a, b = S.fidelity_logits(70000, 12, 0.3, 21)
+    check(a, b, 5, 1.0, "70000x12")
+    ear, kl, means = slq.slq_ear_kl(gpu(a), gpu(b))
+    e_ref, k_ref, m_ref = oracle.ear_kl(a, b)
+    assert np.abs(ear.cpu().numpy() - e_ref).max() <= FID_TOL
+    assert np.abs(kl.cpu().numpy() - k_ref).max() <= FID_TOL
+    lse = slq.slq_row_lse(gpu(a)).cpu().numpy()
+    assert np.abs(lse - oracle.row_lse(a)).max() <= 1e-6 * max(1.0, np.abs(lse).max())

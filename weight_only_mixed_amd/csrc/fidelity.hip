@@ -29,6 +29,7 @@ namespace slq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int64_t kRowBatch = 65535;   // rows per launch of the (chunk, row) grids: grid.y limit
 constexpr double kLog2e_d = 1.4426950408889634;
 constexpr float kLog2e = (float)kLog2e_d;
 
@@ -49,9 +50,12 @@ Fid fid_plan(int64_t rows, int64_t vocab) {
   return f;
 }
 
-// Workspace: stats [rows][C][5] | rowres [rows][4] | earpart [rows][C]  (doubles)
+// Workspace (8-byte words): stats [rows][C][5] | rowres [rows][4] |
+// earpart [rows][C] | top-K keys u64 [rows][C][kTopKMax] |
+// top-K quantized logits f32 [rows][C][kTopKMax] (half a word each)
 size_t ws_doubles(int64_t rows, const Fid &f) {
-  return (size_t)rows * f.C * 5 + (size_t)rows * 4 + (size_t)rows * f.C;
+  return (size_t)rows * f.C * 5 + (size_t)rows * 4 + (size_t)rows * f.C +
+         (size_t)rows * f.C * kTopKMax + (size_t)rows * f.C * kTopKMax / 2 + 1;
 }
 
 __device__ __forceinline__ float fast_exp(float v) { return exp2f(v * kLog2e); }
@@ -229,7 +233,7 @@ __device__ __forceinline__ double block_sum_f64(double v, double *lds) {
 // arithmetic in every workgroup of the row) into A, B and KL; chunk 0 records
 // them for the final means.
 __global__ __launch_bounds__(kThreads) void ear_kernel(const float *__restrict__ a,
-                                                       const float *__restrict__ b, int64_t rows,
+                                                       const float *__restrict__ b, int64_t row_end,
                                                        int64_t vocab, Fid f,
                                                        const double *__restrict__ stats,
                                                        double *__restrict__ rowres,
@@ -238,7 +242,8 @@ __global__ __launch_bounds__(kThreads) void ear_kernel(const float *__restrict__
   __shared__ double lds[kThreads / kWave];
   __shared__ double ab[2];
   const int c = blockIdx.x;
-  const int64_t row = rows - 1 - blockIdx.y;   // reverse of pass 1: recent rows are still cached
+  // rows below row_end in reverse order of pass 1: the most recent rows are still cached
+  const int64_t row = row_end - 1 - blockIdx.y;
   if (threadIdx.x == 0) {
     MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
     for (int cc = 0; cc < f.C; ++cc) {
@@ -316,53 +321,198 @@ __global__ __launch_bounds__(kThreads) void final_kernel(const double *__restric
 // ---- top-K EAR / top-K KL ----
 // A token's selection key: larger logit first, then lower index.  Float bits
 // are mapped to an order-preserving unsigned integer in the high half; the
-// complemented index fills the low half.
+// complemented index fills the low half, so keys of one row are distinct and
+// every real key is above 0.
 __device__ __forceinline__ uint64_t topk_key(float v, uint32_t idx) {
   const uint32_t u = __float_as_uint(v);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - idx);
 }
-
-template <int KT>
-__device__ __forceinline__ void topk_insert(uint64_t (&list)[KT], uint64_t key) {
-  // list is sorted descending; keys are unique (distinct indices)
-  if (key <= list[KT - 1]) return;
-  list[KT - 1] = key;
-#pragma unroll
-  for (int i = KT - 1; i > 0; --i) {
-    const uint64_t hi = list[i - 1], lo = list[i];
-    list[i - 1] = hi > lo ? hi : lo;
-    list[i] = hi > lo ? lo : hi;
-  }
+__device__ __forceinline__ float topk_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    const uint64_t w = __shfl_xor(v, o, kWave);
     v = v > w ? v : w;
   }
   return v;
 }
 
-// One workgroup per row: the row's normalizers from the chunk statistics, a
-// per-thread top-KT list over the row, k rounds of block-wide maximum to
-// pick the row's k tokens, then EAR and KL terms of those tokens in fp64.
+constexpr int kCandCap = 512;   // per-wave candidate buffer (entries)
+
+// Keeps the `take` largest of the first `count` candidates of one wave's
+// buffer, in descending order at its front.  Round j finds the largest key
+// below the previous round's; its owner lane writes it (and its b logit) to
+// slot j.  Returns the last key taken (0 if none).  All lanes of the wave call
+// it together; count <= CAP.
+template <int CAP>
+__device__ uint64_t wave_take(uint64_t *ck, float *cb, int count, int take) {
+  constexpr int PER = CAP / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t key[PER];
+  float bv[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int e = r * kWave + lane;
+    key[r] = e < count ? ck[e] : 0;
+    bv[r] = e < count ? cb[e] : 0.f;
+  }
+  uint64_t prev = ~0ull, w = 0;
+  for (int j = 0; j < take; ++j) {
+    uint64_t lm = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) lm = (key[r] < prev && key[r] > lm) ? key[r] : lm;
+    w = wave_max_u64(lm);
+    if (lm == w) {   // the unique owner
+#pragma unroll
+      for (int r = 0; r < PER; ++r)
+        if (key[r] == w) {
+          ck[j] = w;
+          cb[j] = bv[r];
+        }
+    }
+    prev = w;
+  }
+  return w;
+}
+
+// Pass 1 of the top-K metrics, per (chunk, row): the chunk's softmax partials
+// (m, Z) of both logit rows at temperature T, and the chunk's K largest
+// reference keys with the quantized model's logit at each.  Each wave filters
+// its elements against a rising threshold (the K-th largest value it has kept)
+// into an LDS buffer and cuts the buffer back to K whenever it could overflow;
+// the four waves' lists are merged at the end.
 template <int KT>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ a,
-                                                        const float *__restrict__ b, int64_t vocab,
-                                                        Fid f, int k, double invT,
-                                                        const double *__restrict__ stats,
-                                                        double *__restrict__ rowres,
-                                                        float *__restrict__ ear_rows,
-                                                        float *__restrict__ kl_rows) {
-  __shared__ double ab[4];   // m_a, log Z_a, m_b, log Z_b
-  __shared__ uint64_t wbest[kThreads / kWave];
-  __shared__ uint32_t sel[KT];
-  const int64_t row = blockIdx.x;
+__global__ __launch_bounds__(kThreads) void topk_stats_kernel(
+    const float *__restrict__ a, const float *__restrict__ b, int64_t vocab, Fid f, int64_t r0,
+    int k, float escale, double invT, double *__restrict__ stats, uint64_t *__restrict__ cand_key,
+    float *__restrict__ cand_b) {
+  __shared__ MZ lds[kThreads / kWave];
+  __shared__ uint64_t ck[kThreads / kWave][kCandCap];
+  __shared__ float cb[kThreads / kWave][kCandCap];
+  const int c = blockIdx.x;
+  const int64_t row = r0 + blockIdx.y;
+  const int64_t beg = (int64_t)c * f.chunk;
+  const int64_t end = std::min<int64_t>(beg + f.chunk, vocab);
   const float *ar = a + row * vocab;
   const float *br = b + row * vocab;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  uint64_t *wk = ck[wave];
+  float *wb = cb[wave];
+
+  float ma = -INFINITY, mb = -INFINITY;
+  double za = 0.0, zb = 0.0, unused = 0.0;
+  int n = 0;                  // wave-uniform buffer fill
+  float theta = -INFINITY;    // wave-uniform admission threshold
+  const uint64_t below = (1ull << lane) - 1;
+  auto offer = [&](bool ok, float v, float bvv, uint32_t idx) {
+    const bool in = ok && v >= theta;
+    const uint64_t mask = __ballot(in);
+    if (mask) {
+      if (in) {
+        const int pos = n + __popcll(mask & below);
+        wk[pos] = topk_key(v, idx);
+        wb[pos] = bvv;
+      }
+      n += __popcll(mask);
+    }
+  };
+  auto compact = [&]() {
+    if (n > kCandCap - 4 * kWave) {
+      const int take = n < k ? n : k;
+      const uint64_t last = wave_take<kCandCap>(wk, wb, n, take);
+      n = take;
+      if (take == k) theta = topk_value(last);
+    }
+  };
+  if ((vocab & 3) == 0) {
+    const float4 *a4 = reinterpret_cast<const float4 *>(ar);
+    const float4 *b4 = reinterpret_cast<const float4 *>(br);
+    for (int64_t i0 = beg / 4; i0 < end / 4; i0 += kThreads) {   // same trip count for all lanes
+      const int64_t i = i0 + threadIdx.x;
+      const bool ok = i < end / 4;
+      float4 va = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY), vb = va;
+      if (ok) {
+        va = a4[i];
+        vb = b4[i];
+        online4<false>(va, va, ma, za, unused, escale);
+        online4<false>(vb, vb, mb, zb, unused, escale);
+      }
+      const uint32_t base = (uint32_t)(4 * i);
+      offer(ok, va.x, vb.x, base);
+      offer(ok, va.y, vb.y, base + 1);
+      offer(ok, va.z, vb.z, base + 2);
+      offer(ok, va.w, vb.w, base + 3);
+      compact();
+    }
+  } else {
+    for (int64_t i0 = beg; i0 < end; i0 += kThreads) {
+      const int64_t i = i0 + threadIdx.x;
+      const bool ok = i < end;
+      float va = -INFINITY, vb = -INFINITY;
+      if (ok) {
+        va = ar[i];
+        vb = br[i];
+        online1<false>(va, va, ma, za, unused, escale);
+        online1<false>(vb, vb, mb, zb, unused, escale);
+      }
+      offer(ok, va, vb, (uint32_t)i);
+      compact();
+    }
+  }
+  const MZ ra = mz_block(MZ{(double)ma, za, 0.0}, lds, invT);
+  const MZ rb = mz_block(MZ{(double)mb, zb, 0.0}, lds, invT);
+  // each wave's top min(n, k), then wave 0 merges the four lists
+  __shared__ uint64_t mk[kThreads / kWave * KT];
+  __shared__ float mbv[kThreads / kWave * KT];
+  __shared__ int mcount[kThreads / kWave];
+  const int take = n < k ? n : k;
+  wave_take<kCandCap>(wk, wb, n, take);
+  for (int j = lane; j < KT; j += kWave) {
+    mk[wave * KT + j] = j < take ? wk[j] : 0;
+    mbv[wave * KT + j] = j < take ? wb[j] : 0.f;
+  }
+  if (lane == 0) mcount[wave] = take;
+  __syncthreads();
+  if (wave == 0) {
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) total += mcount[w];
+    const int t2 = total < k ? total : k;
+    wave_take<kThreads / kWave * KT>(mk, mbv, kThreads / kWave * KT, t2);
+    uint64_t *ok_ = cand_key + (row * f.C + c) * kTopKMax;
+    float *ob = cand_b + (row * f.C + c) * kTopKMax;
+    for (int j = lane; j < k; j += kWave) {
+      ok_[j] = j < t2 ? mk[j] : 0;
+      ob[j] = j < t2 ? mbv[j] : 0.f;
+    }
+    if (lane == 0) {
+      double *o = stats + (row * f.C + c) * 5;
+      o[0] = ra.m;
+      o[1] = ra.z;
+      o[2] = 0.0;
+      o[3] = rb.m;
+      o[4] = rb.z;
+    }
+  }
+}
+
+// Pass 2, one workgroup per row: normalizers from the chunk partials, the row's
+// K largest keys from the chunks' lists (k rounds of block-wide maximum below
+// the previous one), then the EAR and KL terms of those tokens in fp64.
+__global__ __launch_bounds__(kThreads) void topk_rows_kernel(
+    const double *__restrict__ stats, const uint64_t *__restrict__ cand_key,
+    const float *__restrict__ cand_b, Fid f, int k, double invT, double *__restrict__ rowres,
+    float *__restrict__ ear_rows, float *__restrict__ kl_rows) {
+  __shared__ double ab[4];   // m_a, log Z_a, m_b, log Z_b
+  __shared__ uint64_t wbest[kThreads / kWave];
+  __shared__ uint64_t selk[kTopKMax];
+  __shared__ float selb[kTopKMax];
+  const int64_t row = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   if (threadIdx.x == 0) {
     MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
@@ -376,51 +526,41 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     ab[2] = tb.m;
     ab[3] = log(tb.z);
   }
-  uint64_t list[KT];
-#pragma unroll
-  for (int i = 0; i < KT; ++i) list[i] = 0;   // below every real key
-  if ((vocab & 3) == 0) {
-    const float4 *a4 = reinterpret_cast<const float4 *>(ar);
-    for (int64_t i = threadIdx.x; i < vocab / 4; i += kThreads) {
-      const float4 v = a4[i];
-      const uint32_t base = (uint32_t)(4 * i);
-      topk_insert<KT>(list, topk_key(v.x, base));
-      topk_insert<KT>(list, topk_key(v.y, base + 1));
-      topk_insert<KT>(list, topk_key(v.z, base + 2));
-      topk_insert<KT>(list, topk_key(v.w, base + 3));
-    }
-  } else {
-    for (int64_t i = threadIdx.x; i < vocab; i += kThreads) topk_insert<KT>(list, topk_key(ar[i], (uint32_t)i));
-  }
-  // k rounds: the largest head across the workgroup wins and is popped
+  const int64_t ne = (int64_t)f.C * k;   // chunk c's list: entries [c * kTopKMax, + k)
+  const uint64_t *rk = cand_key + row * f.C * kTopKMax;
+  const float *rb = cand_b + row * f.C * kTopKMax;
+  uint64_t prev = ~0ull;
   for (int j = 0; j < k; ++j) {
-    const uint64_t w = wave_max_u64(list[0]);
+    uint64_t lm = 0;
+    for (int64_t e = threadIdx.x; e < ne; e += kThreads) {
+      const uint64_t v = rk[(e / k) * kTopKMax + e % k];
+      lm = (v < prev && v > lm) ? v : lm;
+    }
+    const uint64_t w = wave_max_u64(lm);
     if (lane == 0) wbest[wave] = w;
     __syncthreads();
     uint64_t best = wbest[0];
 #pragma unroll
     for (int i = 1; i < kThreads / kWave; ++i) best = best > wbest[i] ? best : wbest[i];
-    if (list[0] == best) {   // unique owner
-#pragma unroll
-      for (int i = 0; i < KT - 1; ++i) list[i] = list[i + 1];
-      list[KT - 1] = 0;
+    if (lm == best && best != 0) {   // the unique owner records the quantized logit
+      for (int64_t e = threadIdx.x; e < ne; e += kThreads)
+        if (rk[(e / k) * kTopKMax + e % k] == best) selb[j] = rb[(e / k) * kTopKMax + e % k];
     }
-    if (threadIdx.x == 0) sel[j] = 0xFFFFFFFFu - (uint32_t)best;
+    if (threadIdx.x == 0) selk[j] = best;
+    prev = best;
     __syncthreads();
   }
   if (wave != 0) return;
   double e = 0.0, d = 0.0;
   if (lane < k) {
-    const uint32_t v = sel[lane];
-    const double lp = ((double)ar[v] - ab[0]) * invT - ab[1];
-    const double lq = ((double)br[v] - ab[2]) * invT - ab[3];
+    const double lp = ((double)topk_value(selk[lane]) - ab[0]) * invT - ab[1];
+    const double lq = ((double)selb[lane] - ab[2]) * invT - ab[3];
     const double p = exp(lp), q = exp(lq);
     e = p < q ? p : q;
     d = p * (lp - lq);
   }
-  // fixed-shape tree sum over the wave
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
+  for (int o = 32; o >= 1; o >>= 1) {   // fixed-shape tree sum over the wave
     e += __shfl_xor(e, o, kWave);
     d += __shfl_xor(d, o, kWave);
   }
@@ -461,10 +601,13 @@ hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *l
                           hipStream_t s) {
   const Fid f = fid_plan(rows, vocab);
   double *stats = static_cast<double *>(ws);
-  hipLaunchKernelGGL((stats_kernel<false>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a,
-                     nullptr, vocab, f, (int64_t)0, kLog2e, 1.0, stats);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowBatch) {
+    const unsigned nr = (unsigned)std::min<int64_t>(kRowBatch, rows - r0);
+    hipLaunchKernelGGL((stats_kernel<false>), dim3(f.C, nr), dim3(kThreads), 0, s, a, nullptr,
+                       vocab, f, r0, kLog2e, 1.0, stats);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((rows_kernel<false>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, stats, (int64_t)0, rows, f, nullptr, lse, nullptr);
   return hipGetLastError();
@@ -476,13 +619,19 @@ hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t v
   double *stats = static_cast<double *>(ws);
   double *rowres = stats + (size_t)rows * f.C * 5;
   double *earpart = rowres + (size_t)rows * 4;
-  hipLaunchKernelGGL((stats_kernel<true>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
-                     vocab, f, (int64_t)0, kLog2e, 1.0, stats);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ear_kernel, dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
-                     (int64_t)rows, vocab, f, stats, rowres, kl, earpart);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e;
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowBatch) {
+    const unsigned nr = (unsigned)std::min<int64_t>(kRowBatch, rows - r0);
+    hipLaunchKernelGGL((stats_kernel<true>), dim3(f.C, nr), dim3(kThreads), 0, s, a, b, vocab, f,
+                       r0, kLog2e, 1.0, stats);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  for (int64_t hi = rows; hi > 0; hi -= kRowBatch) {   // last rows first, as they were read last
+    const unsigned nr = (unsigned)std::min<int64_t>(kRowBatch, hi);
+    hipLaunchKernelGGL(ear_kernel, dim3(f.C, nr), dim3(kThreads), 0, s, a, b, hi, vocab, f, stats,
+                       rowres, kl, earpart);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(final_kernel, dim3(1), dim3(kThreads), 0, s, earpart, rowres, rows, f, ear,
                      means);
   return hipGetLastError();
@@ -494,19 +643,25 @@ hipError_t launch_ear_kl_topk(const float *a, const float *b, int64_t rows, int6
   const Fid f = fid_plan(rows, vocab);
   double *stats = static_cast<double *>(ws);
   double *rowres = stats + (size_t)rows * f.C * 5;
-  hipLaunchKernelGGL((stats_kernel<true>), dim3(f.C, (unsigned)rows), dim3(kThreads), 0, s, a, b,
-                     vocab, f, (int64_t)0, (float)(kLog2e_d * invT), invT, stats);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (k <= 16)
-    hipLaunchKernelGGL((topk_kernel<16>), dim3((unsigned)rows), dim3(kThreads), 0, s, a, b, vocab,
-                       f, k, invT, stats, rowres, ear, kl);
-  else if (k <= 32)
-    hipLaunchKernelGGL((topk_kernel<32>), dim3((unsigned)rows), dim3(kThreads), 0, s, a, b, vocab,
-                       f, k, invT, stats, rowres, ear, kl);
-  else
-    hipLaunchKernelGGL((topk_kernel<kTopKMax>), dim3((unsigned)rows), dim3(kThreads), 0, s, a, b,
-                       vocab, f, k, invT, stats, rowres, ear, kl);
+  uint64_t *cand_key = reinterpret_cast<uint64_t *>(rowres + (size_t)rows * 4 + (size_t)rows * f.C);
+  float *cand_b = reinterpret_cast<float *>(cand_key + (size_t)rows * f.C * kTopKMax);
+  const float escale = (float)(kLog2e_d * invT);
+  hipError_t e;
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowBatch) {
+    const dim3 grid(f.C, (unsigned)std::min<int64_t>(kRowBatch, rows - r0));
+    if (k <= 16)
+      hipLaunchKernelGGL((topk_stats_kernel<16>), grid, dim3(kThreads), 0, s, a, b, vocab, f, r0,
+                         k, escale, invT, stats, cand_key, cand_b);
+    else if (k <= 32)
+      hipLaunchKernelGGL((topk_stats_kernel<32>), grid, dim3(kThreads), 0, s, a, b, vocab, f, r0,
+                         k, escale, invT, stats, cand_key, cand_b);
+    else
+      hipLaunchKernelGGL((topk_stats_kernel<kTopKMax>), grid, dim3(kThreads), 0, s, a, b, vocab, f,
+                         r0, k, escale, invT, stats, cand_key, cand_b);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, stats, cand_key,
+                     cand_b, f, k, invT, rowres, ear, kl);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kThreads), 0, s, rowres, rows, means);
   return hipGetLastError();
