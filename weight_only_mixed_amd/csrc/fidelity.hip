@@ -52,10 +52,11 @@ Fid fid_plan(int64_t rows, int64_t vocab) {
 
 // Workspace (8-byte words): stats [rows][C][5] | rowres [rows][4] |
 // earpart [rows][C] | top-K keys u64 [rows][C][kTopKMax] |
-// top-K quantized logits f32 [rows][C][kTopKMax] (half a word each)
+// top-K quantized logits f32 [rows][C][kTopKMax] (half a word each) | pad |
+// top-K ticket u32
 size_t ws_doubles(int64_t rows, const Fid &f) {
   return (size_t)rows * f.C * 5 + (size_t)rows * 4 + (size_t)rows * f.C +
-         (size_t)rows * f.C * kTopKMax + (size_t)rows * f.C * kTopKMax / 2 + 1;
+         (size_t)rows * f.C * kTopKMax + (size_t)rows * f.C * kTopKMax / 2 + 2;
 }
 
 __device__ __forceinline__ float fast_exp(float v) { return exp2f(v * kLog2e); }
@@ -344,15 +345,41 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 constexpr int kCandCap = 512;   // per-wave candidate buffer (entries)
 
-// Keeps the `take` largest of the first `count` candidates of one wave's
-// buffer, in descending order at its front.  Round j finds the largest key
-// below the previous round's; its owner lane writes it (and its b logit) to
-// slot j.  Returns the last key taken (0 if none).  All lanes of the wave call
-// it together; count <= CAP.
+// The K-th largest of the keys the wave holds (PER per lane, 0 = no entry),
+// by radix selection from the top bit down: a bit is kept when at least K keys
+// lie at or above the prefix with it set.  Counts are popcounts of ballots, so
+// the search runs in scalar registers with no data exchange between lanes.
+// Keys are distinct, so exactly K keys are >= the result; the low half is only
+// searched when the high half leaves a tie.  Needs >= K nonzero keys.
+template <int PER>
+__device__ uint64_t kth_key(const uint64_t (&key)[PER], int k) {
+  uint64_t prefix = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t cand = prefix | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) cnt += __popcll(__ballot(key[r] >= cand));
+    if (cnt >= k) prefix = cand;
+    if (bit == 32) {
+      int at = 0;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) at += __popcll(__ballot(key[r] >= prefix));
+      if (at == k) return prefix;
+    }
+  }
+  return prefix;
+}
+
+// Cuts one wave's candidate buffer (first `count` entries) back to its k
+// largest keys, stored at the front in lane order.  Returns the new count;
+// `kth` is the smallest key kept when the buffer held more than k, else 0.
 template <int CAP>
-__device__ uint64_t wave_take(uint64_t *ck, float *cb, int count, int take) {
+__device__ int wave_keep(uint64_t *ck, float *cb, int count, int k, uint64_t &kth) {
+  kth = 0;
+  if (count <= k) return count;
   constexpr int PER = CAP / kWave;
   const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t below = (1ull << lane) - 1;
   uint64_t key[PER];
   float bv[PER];
 #pragma unroll
@@ -361,36 +388,34 @@ __device__ uint64_t wave_take(uint64_t *ck, float *cb, int count, int take) {
     key[r] = e < count ? ck[e] : 0;
     bv[r] = e < count ? cb[e] : 0.f;
   }
-  uint64_t prev = ~0ull, w = 0;
-  for (int j = 0; j < take; ++j) {
-    uint64_t lm = 0;
+  kth = kth_key<PER>(key, k);
+  int base = 0;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) lm = (key[r] < prev && key[r] > lm) ? key[r] : lm;
-    w = wave_max_u64(lm);
-    if (lm == w) {   // the unique owner
-#pragma unroll
-      for (int r = 0; r < PER; ++r)
-        if (key[r] == w) {
-          ck[j] = w;
-          cb[j] = bv[r];
-        }
+  for (int r = 0; r < PER; ++r) {
+    const bool keep = key[r] >= kth;
+    const uint64_t m = __ballot(keep);
+    if (keep) {
+      const int pos = base + __popcll(m & below);
+      ck[pos] = key[r];
+      cb[pos] = bv[r];
     }
-    prev = w;
+    base += __popcll(m);
   }
-  return w;
+  return k;
 }
 
 // Pass 1 of the top-K metrics, per (chunk, row): the chunk's softmax partials
 // (m, Z) of both logit rows at temperature T, and the chunk's K largest
-// reference keys with the quantized model's logit at each.  Each wave filters
-// its elements against a rising threshold (the K-th largest value it has kept)
-// into an LDS buffer and cuts the buffer back to K whenever it could overflow;
-// the four waves' lists are merged at the end.
+// reference keys with the quantized model's logit at each (in no particular
+// order; key 0 pads a chunk shorter than K).  Each wave filters its elements
+// against a rising threshold (the K-th largest value it has kept) into an LDS
+// buffer and cuts the buffer back to K whenever it could overflow; the four
+// waves' lists are merged at the end.  Also clears pass 2's ticket.
 template <int KT>
 __global__ __launch_bounds__(kThreads) void topk_stats_kernel(
     const float *__restrict__ a, const float *__restrict__ b, int64_t vocab, Fid f, int64_t r0,
     int k, float escale, double invT, double *__restrict__ stats, uint64_t *__restrict__ cand_key,
-    float *__restrict__ cand_b) {
+    float *__restrict__ cand_b, unsigned *__restrict__ ticket) {
   __shared__ MZ lds[kThreads / kWave];
   __shared__ uint64_t ck[kThreads / kWave][kCandCap];
   __shared__ float cb[kThreads / kWave][kCandCap];
@@ -422,32 +447,49 @@ __global__ __launch_bounds__(kThreads) void topk_stats_kernel(
     }
   };
   auto compact = [&]() {
-    if (n > kCandCap - 4 * kWave) {
-      const int take = n < k ? n : k;
-      const uint64_t last = wave_take<kCandCap>(wk, wb, n, take);
-      n = take;
-      if (take == k) theta = topk_value(last);
+    if (n > kCandCap - 4 * kWave) {   // the next offers could overflow: n > 256 >= k
+      uint64_t kth;
+      n = wave_keep<kCandCap>(wk, wb, n, k, kth);
+      theta = topk_value(kth);
     }
   };
   if ((vocab & 3) == 0) {
     const float4 *a4 = reinterpret_cast<const float4 *>(ar);
     const float4 *b4 = reinterpret_cast<const float4 *>(br);
-    for (int64_t i0 = beg / 4; i0 < end / 4; i0 += kThreads) {   // same trip count for all lanes
-      const int64_t i = i0 + threadIdx.x;
-      const bool ok = i < end / 4;
-      float4 va = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY), vb = va;
-      if (ok) {
-        va = a4[i];
-        vb = b4[i];
-        online4<false>(va, va, ma, za, unused, escale);
-        online4<false>(vb, vb, mb, zb, unused, escale);
+    constexpr int kU = 4;   // float4 pairs in flight per lane
+    // same trip count for all lanes of the wave (the ballots need every lane)
+    for (int64_t i0 = beg / 4; i0 < end / 4; i0 += kU * kThreads) {
+      float4 va[kU], vb[kU];
+      bool ok[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kThreads + threadIdx.x;
+        ok[u] = i < end / 4;
+        va[u] = vb[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (ok[u]) {
+          va[u] = a4[i];
+          vb[u] = b4[i];
+        }
       }
-      const uint32_t base = (uint32_t)(4 * i);
-      offer(ok, va.x, vb.x, base);
-      offer(ok, va.y, vb.y, base + 1);
-      offer(ok, va.z, vb.z, base + 2);
-      offer(ok, va.w, vb.w, base + 3);
-      compact();
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (ok[u]) {
+          online4<false>(va[u], va[u], ma, za, unused, escale);
+          online4<false>(vb[u], vb[u], mb, zb, unused, escale);
+          mx = fmaxf(mx, fmaxf(fmaxf(va[u].x, va[u].y), fmaxf(va[u].z, va[u].w)));
+        }
+      if (__ballot(mx >= theta)) {   // rare once the threshold has risen
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t base = (uint32_t)(4 * (i0 + u * kThreads + threadIdx.x));
+          offer(ok[u], va[u].x, vb[u].x, base);
+          offer(ok[u], va[u].y, vb[u].y, base + 1);
+          offer(ok[u], va[u].z, vb[u].z, base + 2);
+          offer(ok[u], va[u].w, vb[u].w, base + 3);
+          compact();
+        }
+      }
     }
   } else {
     for (int64_t i0 = beg; i0 < end; i0 += kThreads) {
@@ -470,25 +512,46 @@ __global__ __launch_bounds__(kThreads) void topk_stats_kernel(
   __shared__ uint64_t mk[kThreads / kWave * KT];
   __shared__ float mbv[kThreads / kWave * KT];
   __shared__ int mcount[kThreads / kWave];
-  const int take = n < k ? n : k;
-  wave_take<kCandCap>(wk, wb, n, take);
+  uint64_t kth;
+  const int take = wave_keep<kCandCap>(wk, wb, n, k, kth);
   for (int j = lane; j < KT; j += kWave) {
     mk[wave * KT + j] = j < take ? wk[j] : 0;
     mbv[wave * KT + j] = j < take ? wb[j] : 0.f;
   }
   if (lane == 0) mcount[wave] = take;
+  if (r0 == 0 && c == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ticket = 0u;   // for pass 2
   __syncthreads();
   if (wave == 0) {
+    constexpr int PER = kThreads / kWave * KT / kWave;
     int total = 0;
 #pragma unroll
     for (int w = 0; w < kThreads / kWave; ++w) total += mcount[w];
-    const int t2 = total < k ? total : k;
-    wave_take<kThreads / kWave * KT>(mk, mbv, kThreads / kWave * KT, t2);
+    uint64_t key[PER];
+    float bv[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      key[r] = mk[r * kWave + lane];
+      bv[r] = mbv[r * kWave + lane];
+    }
+    const uint64_t thr = total > k ? kth_key<PER>(key, k) : 1;   // every real key is >= 1
     uint64_t *ok_ = cand_key + (row * f.C + c) * kTopKMax;
     float *ob = cand_b + (row * f.C + c) * kTopKMax;
-    for (int j = lane; j < k; j += kWave) {
-      ok_[j] = j < t2 ? mk[j] : 0;
-      ob[j] = j < t2 ? mbv[j] : 0.f;
+    const uint64_t below = (1ull << lane) - 1;
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const bool keep = key[r] >= thr;
+      const uint64_t m = __ballot(keep);
+      if (keep) {
+        const int pos = base + __popcll(m & below);
+        ok_[pos] = key[r];
+        ob[pos] = bv[r];
+      }
+      base += __popcll(m);
+    }
+    for (int j = base + lane; j < k; j += kWave) {   // fewer than k elements in the chunk
+      ok_[j] = 0;
+      ob[j] = 0.f;
     }
     if (lane == 0) {
       double *o = stats + (row * f.C + c) * 5;
@@ -501,82 +564,94 @@ __global__ __launch_bounds__(kThreads) void topk_stats_kernel(
   }
 }
 
-// Pass 2, one workgroup per row: normalizers from the chunk partials, the row's
-// K largest keys from the chunks' lists (k rounds of block-wide maximum below
-// the previous one), then the EAR and KL terms of those tokens in fp64.
+// Pass 2, one wave per row: the row's normalizers from the chunk partials, the
+// K-th largest key among the chunk lists by radix selection, and the EAR and
+// KL terms of the K keys at or above it in fp64 (lane order, then a fixed
+// tree).  The last workgroup to finish (ticket) forms the means over all rows
+// in a fixed order.
 __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
     const double *__restrict__ stats, const uint64_t *__restrict__ cand_key,
-    const float *__restrict__ cand_b, Fid f, int k, double invT, double *__restrict__ rowres,
-    float *__restrict__ ear_rows, float *__restrict__ kl_rows) {
-  __shared__ double ab[4];   // m_a, log Z_a, m_b, log Z_b
-  __shared__ uint64_t wbest[kThreads / kWave];
-  __shared__ uint64_t selk[kTopKMax];
-  __shared__ float selb[kTopKMax];
-  const int64_t row = blockIdx.x;
+    const float *__restrict__ cand_b, int64_t rows, Fid f, int k, double invT,
+    double *__restrict__ rowres, float *__restrict__ ear_rows, float *__restrict__ kl_rows,
+    unsigned *__restrict__ ticket, double *__restrict__ means) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  if (threadIdx.x == 0) {
-    MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
-    for (int c = 0; c < f.C; ++c) {
-      const double *st = stats + (row * f.C + c) * 5;
-      ta = mz_combine(ta, MZ{st[0], st[1], 0.0}, invT);
-      tb = mz_combine(tb, MZ{st[3], st[4], 0.0}, invT);
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
+  if (row < rows) {
+    double st[4] = {0.0, 0.0, 0.0, 0.0};   // m_a, log Z_a, m_b, log Z_b
+    if (lane == 0) {
+      MZ ta{-INFINITY, 0.0, 0.0}, tb{-INFINITY, 0.0, 0.0};
+      for (int c = 0; c < f.C; ++c) {
+        const double *sp = stats + (row * f.C + c) * 5;
+        ta = mz_combine(ta, MZ{sp[0], sp[1], 0.0}, invT);
+        tb = mz_combine(tb, MZ{sp[3], sp[4], 0.0}, invT);
+      }
+      st[0] = ta.m;
+      st[1] = log(ta.z);
+      st[2] = tb.m;
+      st[3] = log(tb.z);
     }
-    ab[0] = ta.m;
-    ab[1] = log(ta.z);
-    ab[2] = tb.m;
-    ab[3] = log(tb.z);
-  }
-  const int64_t ne = (int64_t)f.C * k;   // chunk c's list: entries [c * kTopKMax, + k)
-  const uint64_t *rk = cand_key + row * f.C * kTopKMax;
-  const float *rb = cand_b + row * f.C * kTopKMax;
-  uint64_t prev = ~0ull;
-  for (int j = 0; j < k; ++j) {
-    uint64_t lm = 0;
-    for (int64_t e = threadIdx.x; e < ne; e += kThreads) {
-      const uint64_t v = rk[(e / k) * kTopKMax + e % k];
-      lm = (v < prev && v > lm) ? v : lm;
-    }
-    const uint64_t w = wave_max_u64(lm);
-    if (lane == 0) wbest[wave] = w;
-    __syncthreads();
-    uint64_t best = wbest[0];
 #pragma unroll
-    for (int i = 1; i < kThreads / kWave; ++i) best = best > wbest[i] ? best : wbest[i];
-    if (lm == best && best != 0) {   // the unique owner records the quantized logit
-      for (int64_t e = threadIdx.x; e < ne; e += kThreads)
-        if (rk[(e / k) * kTopKMax + e % k] == best) selb[j] = rb[(e / k) * kTopKMax + e % k];
-    }
-    if (threadIdx.x == 0) selk[j] = best;
-    prev = best;
-    __syncthreads();
-  }
-  if (wave != 0) return;
-  double e = 0.0, d = 0.0;
-  if (lane < k) {
-    const double lp = ((double)topk_value(selk[lane]) - ab[0]) * invT - ab[1];
-    const double lq = ((double)selb[lane] - ab[2]) * invT - ab[3];
-    const double p = exp(lp), q = exp(lq);
-    e = p < q ? p : q;
-    d = p * (lp - lq);
-  }
+    for (int i = 0; i < 4; ++i) st[i] = __shfl(st[i], 0, kWave);
+    const int64_t ne = (int64_t)f.C * k;   // chunk c's list: entries [c * kTopKMax, + k)
+    const uint64_t *rk = cand_key + row * f.C * kTopKMax;
+    const float *rb = cand_b + row * f.C * kTopKMax;
+    auto at = [&](int64_t e) { return (e / k) * kTopKMax + e % k; };
+    auto term = [&](uint64_t key, float bq, double &e, double &d) {
+      const double lp = ((double)topk_value(key) - st[0]) * invT - st[1];
+      const double lq = ((double)bq - st[2]) * invT - st[3];
+      const double p = exp(lp), q = exp(lq);
+      e += p < q ? p : q;
+      d += p * (lp - lq);
+    };
+    double e = 0.0, d = 0.0;
+    constexpr int kPer = 16;   // lists of up to 1024 entries stay in registers
+    if (ne <= (int64_t)kPer * kWave) {
+      uint64_t key[kPer];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {   // fixed-shape tree sum over the wave
-    e += __shfl_xor(e, o, kWave);
-    d += __shfl_xor(d, o, kWave);
+      for (int r = 0; r < kPer; ++r) {
+        const int64_t i = (int64_t)r * kWave + lane;
+        key[r] = i < ne ? rk[at(i)] : 0;
+      }
+      const uint64_t thr = kth_key<kPer>(key, k);
+#pragma unroll
+      for (int r = 0; r < kPer; ++r)
+        if (key[r] >= thr) term(key[r], rb[at((int64_t)r * kWave + lane)], e, d);
+    } else {   // long lists (few rows, long vocabulary): count from memory
+      uint64_t prefix = 0;
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = prefix | (1ull << bit);
+        int cnt = 0;
+        for (int64_t i0 = 0; i0 < ne; i0 += kWave) {
+          const int64_t i = i0 + lane;
+          cnt += __popcll(__ballot(i < ne && rk[at(i < ne ? i : 0)] >= cand));
+        }
+        if (cnt >= k) prefix = cand;
+      }
+      for (int64_t i = lane; i < ne; i += kWave) {
+        const uint64_t key = rk[at(i)];
+        if (key >= prefix) term(key, rb[at(i)], e, d);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {   // fixed-shape tree sum over the wave
+      e += __shfl_xor(e, o, kWave);
+      d += __shfl_xor(d, o, kWave);
+    }
+    if (lane == 0) {
+      rowres[row * 4 + 2] = d;
+      rowres[row * 4 + 3] = e;
+      ear_rows[row] = (float)e;
+      kl_rows[row] = (float)d;
+      __threadfence();   // the row's results before this workgroup's ticket
+    }
   }
-  if (lane == 0) {
-    rowres[row * 4 + 2] = d;
-    rowres[row * 4 + 3] = e;
-    ear_rows[row] = (float)e;
-    kl_rows[row] = (float)d;
-  }
-}
-
-// Means of the per-row top-K EAR and KL; one workgroup, fixed order.
-__global__ __launch_bounds__(kThreads) void topk_final_kernel(const double *__restrict__ rowres,
-                                                              int64_t rows,
-                                                              double *__restrict__ means) {
+  __shared__ bool last;
   __shared__ double lds[kThreads / kWave];
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();   // every other workgroup's rows are visible from here
   double se = 0.0, sk = 0.0;
   for (int64_t r = threadIdx.x; r < rows; r += kThreads) {
     se += rowres[r * 4 + 3];
@@ -585,8 +660,8 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const double *__re
   const double te = block_sum_f64(se, lds);
   const double tk = block_sum_f64(sk, lds);
   if (threadIdx.x == 0) {
-    means[0] = rows > 0 ? te / (double)rows : 0.0;
-    means[1] = rows > 0 ? tk / (double)rows : 0.0;
+    means[0] = te / (double)rows;
+    means[1] = tk / (double)rows;
   }
 }
 
@@ -645,25 +720,25 @@ hipError_t launch_ear_kl_topk(const float *a, const float *b, int64_t rows, int6
   double *rowres = stats + (size_t)rows * f.C * 5;
   uint64_t *cand_key = reinterpret_cast<uint64_t *>(rowres + (size_t)rows * 4 + (size_t)rows * f.C);
   float *cand_b = reinterpret_cast<float *>(cand_key + (size_t)rows * f.C * kTopKMax);
+  unsigned *ticket = reinterpret_cast<unsigned *>(cand_b + (size_t)rows * f.C * kTopKMax + 1);
   const float escale = (float)(kLog2e_d * invT);
   hipError_t e;
   for (int64_t r0 = 0; r0 < rows; r0 += kRowBatch) {
     const dim3 grid(f.C, (unsigned)std::min<int64_t>(kRowBatch, rows - r0));
     if (k <= 16)
       hipLaunchKernelGGL((topk_stats_kernel<16>), grid, dim3(kThreads), 0, s, a, b, vocab, f, r0,
-                         k, escale, invT, stats, cand_key, cand_b);
+                         k, escale, invT, stats, cand_key, cand_b, ticket);
     else if (k <= 32)
       hipLaunchKernelGGL((topk_stats_kernel<32>), grid, dim3(kThreads), 0, s, a, b, vocab, f, r0,
-                         k, escale, invT, stats, cand_key, cand_b);
+                         k, escale, invT, stats, cand_key, cand_b, ticket);
     else
       hipLaunchKernelGGL((topk_stats_kernel<kTopKMax>), grid, dim3(kThreads), 0, s, a, b, vocab, f,
-                         r0, k, escale, invT, stats, cand_key, cand_b);
+                         r0, k, escale, invT, stats, cand_key, cand_b, ticket);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, stats, cand_key,
-                     cand_b, f, k, invT, rowres, ear, kl);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(1), dim3(kThreads), 0, s, rowres, rows, means);
+  const unsigned wgs = (unsigned)((rows + kThreads / kWave - 1) / (kThreads / kWave));
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(wgs), dim3(kThreads), 0, s, stats, cand_key, cand_b,
+                     rows, f, k, invT, rowres, ear, kl, ticket, means);
   return hipGetLastError();
 }
 
