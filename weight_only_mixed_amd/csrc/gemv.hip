@@ -209,8 +209,8 @@ __device__ __forceinline__ float meta_zero(uint32_t z) {
 // 16*NT rows x [ga, gz) groups.
 constexpr int kMetaRounds = 2;
 
-template <int BITS, int MT, int NT, int B, bool MV, bool XD>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(
+template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV>
+__global__ __launch_bounds__(WV * kWave) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
@@ -234,12 +234,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   // in units of 4 groups (MV) or single groups
   const int gunit = MV ? 4 : 1;
   const int units = gcount / gunit;
-  const int ga = (wave * units / kWaves) * gunit, gz = ((wave + 1) * units / kWaves) * gunit;
+  const int ga = (wave * units / WV) * gunit, gz = ((wave + 1) * units / WV) * gunit;
 
   // ---- stage activations [M][gcount*128] into LDS in fragment order ----
   // (an L2-resident operand: the barrier after it is a short wait).  XD: each
   // lane loads its own activation chunk with the weight batches instead.
-  for (int i = threadIdx.x; !XD && i < M * gcount * 4; i += kThreads) {
+  for (int i = threadIdx.x; !XD && i < M * gcount * 4; i += WV * kWave) {
     const int m = i / (gcount * 4), c = i % (gcount * 4);
     const u32x4_t *src =
         reinterpret_cast<const u32x4_t *>(x + (int64_t)m * K + (int64_t)gbase * kGroup + 32 * c);
@@ -295,8 +295,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int n = min(n0 + 16 * t + col, N - 1);   // rows past N are read, never stored
     crow[t] = codes + (int64_t)n * wpr + (int64_t)gbase * 4 * BITS + kq * BITS;
   }
-  // Loads are unconditional (group index clamped to the wave's last group) so
-  // that the two batch buffers stay in flight across the loop back-edge.
+  // Loads past the wave's last group are skipped (a wave-uniform branch):
+  // reloading the last group instead kept the two buffers' instruction shape
+  // but cost a wait for redundant loads before the reduction barrier.
   // XD: rows min(16 mt + col, M-1) of x, this lane's 32-value chunk of each group
   const u32x4_t *xrow[XD ? MT : 1];
 #pragma unroll
@@ -306,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   auto load = [&](Batch<BITS, MT, NT, B, XD> &bt, int g) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int gg = min(g + j, gz - 1);
+      if (g + j >= gz) break;   // past the wave's last group: nothing to wait for at the end
+      const int gg = g + j;
       if constexpr (XD) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
   }
 
-  // ---- reduce the 4 waves' partials in LDS (reusing the activation area) ----
+  // ---- reduce the WV waves' partials in LDS (reusing the activation area) ----
   __syncthreads();
   f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
 #pragma unroll
@@ -449,12 +451,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) red[((wave * NT + t) * MT + mt) * kWave + lane] = acc[t][mt];
   __syncthreads();
-  // wave w sums the (t, mt) tiles with (t * MT + mt) % 4 == w, adding waves in order
-  for (int e = wave; e < NT * MT; e += kWaves) {
+  // wave w sums the (t, mt) tiles with (t * MT + mt) % WV == w, adding waves in order
+  for (int e = wave; e < NT * MT; e += WV) {
     const int t = e / MT, mt = e % MT;
     f32x4_t sum = red[(t * MT + mt) * kWave + lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += red[((w * NT + t) * MT + mt) * kWave + lane];
+    for (int w = 1; w < WV; ++w) sum += red[((w * NT + t) * MT + mt) * kWave + lane];
     const int n = n0 + 16 * t + col;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   __syncthreads();
   if (!last) return;
   const int rows = 16 * NT;
-  for (int i = threadIdx.x; i < M * rows; i += kThreads) {
+  for (int i = threadIdx.x; i < M * rows; i += WV * kWave) {
     const int m = i / rows, n = n0 + i % rows;
     if (n >= N) continue;
     float sum = 0.f;
@@ -624,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
       if (g >= gcount) break;
       if (j % 2 == 0) body(g, ring[j], xr0, xr1);
       else body(g, ring[j], xr1, xr0);
-      ring[j] = cload(g + kRowsDepth);
+      if (g + kRowsDepth < gcount) ring[j] = cload(g + kRowsDepth);
     }
   }
 
@@ -674,10 +676,10 @@ constexpr int64_t kMaxTicketBlocks = kTicketBytes / sizeof(unsigned);
 
 // LDS: the activation tile [m][groups*128] in fragment order, reused for the
 // cross-wave reduction.
-size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw, bool xd) {
+size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw, bool xd, int wv) {
   const size_t xs = xd ? 0 : (size_t)m * (gw * 64 + 4) * 4;
   const size_t meta = (size_t)16 * nt * gw * 8;
-  const size_t red = (size_t)kWaves * nt * mt * kWave * 16;
+  const size_t red = (size_t)wv * nt * mt * kWave * 16;
   return std::max(xs + meta, red) + 16;
 }
 constexpr size_t kLdsBudget = 65536;   // activation bytes per workgroup
@@ -694,11 +696,32 @@ constexpr int64_t kTargetBlocksTiny = SLQ_GEMV_TARGET_BLOCKS_TINY;
 #endif
 constexpr int64_t kXdMinM = SLQ_GEMV_XD_MIN_M;
 constexpr int64_t kXdMinGroups = 64;
+// Groups per load batch for 1, 2 and 4 row tiles (two batches in flight).
+#ifndef SLQ_GEMV_B_NT1
+#define SLQ_GEMV_B_NT1 4
+#endif
+#ifndef SLQ_GEMV_B_NT2
+#define SLQ_GEMV_B_NT2 2
+#endif
+#ifndef SLQ_GEMV_B_NT4
+#define SLQ_GEMV_B_NT4 1
+#endif
+constexpr int kBatchNt1 = SLQ_GEMV_B_NT1, kBatchNt2 = SLQ_GEMV_B_NT2, kBatchNt4 = SLQ_GEMV_B_NT4;
+// One m-tile on a grid of at most kWvBlocks workgroups (one per CU or fewer):
+// 16 wavefronts per workgroup (8 when activations are loaded per lane, whose
+// register footprint would spill at 16) instead of 4, all on the same rows,
+// so that each SIMD has several wavefronts to overlap load latency, unpacking
+// and MFMA chains.  Larger grids keep 4: wider workgroups would no longer all
+// be resident at once.
+#ifndef SLQ_GEMV_WV_BLOCKS
+#define SLQ_GEMV_WV_BLOCKS 256
+#endif
+constexpr int64_t kWvBlocks = SLQ_GEMV_WV_BLOCKS;
 // Dynamic LDS ceiling per workgroup: activations (<= 64 KiB + pitch padding)
 // plus scales/zero points (<= 32 KiB), or the reduction area (<= 64 KiB).
 constexpr size_t kMaxDynLds = 128 * 1024;
 
-template <int BITS, int MT, int NT, int B, bool MV, bool XD>
+template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV>
 hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *scales,
                        const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                        const GemvPlan &plan, hipStream_t st) {
@@ -708,29 +731,36 @@ hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *sc
     tickets = static_cast<unsigned *>(ws);
     partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
   }
-  const size_t lds = gemv_lds_bytes(m, MT, NT, plan.gw, XD);
+  const size_t lds = gemv_lds_bytes(m, MT, NT, plan.gw, XD, WV);
   if (lds > kMaxDynLds) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B, MV, XD>),
+      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B, MV, XD, WV>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
   if (attr != hipSuccess) {
     (void)hipGetLastError();   // leave no sticky error behind for later calls
     return attr;
   }
-  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B, MV, XD>), dim3(plan.nblocks, plan.ksplits),
-                     dim3(kThreads), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
+  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B, MV, XD, WV>), dim3(plan.nblocks, plan.ksplits),
+                     dim3(WV * kWave), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
                      plan.gw, plan.ksplits, y, partial, tickets);
   return hipGetLastError();
 }
 
-// Groups per load batch: NT * B = 4 chunk loads per batch per lane, two
-// batches in flight.
+// Groups per load batch: kBatchNt* (NT * B = 4 chunk loads per batch per
+// lane by default), two batches in flight.
 template <int BITS, int MT>
 hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *scales,
                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                       const GemvPlan &plan, hipStream_t st) {
-#define SLQ_GEMV_LAUNCH(NT_, B_, MV_, XD_) \
-  gemv_launch<BITS, MT, NT_, B_, MV_, XD_>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
+// One m-tile may use 8 waves per workgroup, or 16 with LDS-staged activations
+// (more waves on the same rows for occupancy); several m-tiles use 4.
+#define SLQ_GEMV_LAUNCH_WV(NT_, B_, MV_, XD_, WV_) \
+  gemv_launch<BITS, MT, NT_, B_, MV_, XD_, WV_>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
+#define SLQ_GEMV_LAUNCH(NT_, B_, MV_, XD_)                                                  \
+  (MT == 1 && !XD_ && plan.wv == 16                                                         \
+       ? SLQ_GEMV_LAUNCH_WV(NT_, B_, MV_, XD_, (MT == 1 && !XD_ ? 16 : 4))                 \
+   : MT == 1 && plan.wv == 8 ? SLQ_GEMV_LAUNCH_WV(NT_, B_, MV_, XD_, (MT == 1 ? 8 : 4))     \
+                             : SLQ_GEMV_LAUNCH_WV(NT_, B_, MV_, XD_, 4))
 // Direct activation loads with several m-tiles hold MT x 16 registers of x
 // per group: one group per batch.
 #define SLQ_GEMV_NT(NT_, B_)                                                            \
@@ -747,13 +777,14 @@ hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *sca
                      : SLQ_GEMV_LAUNCH(NT_, B_, false, false);                          \
     return hipErrorInvalidValue;
   switch (plan.nt) {
-    SLQ_GEMV_NT(1, 4)
-    SLQ_GEMV_NT(2, 2)
-    SLQ_GEMV_NT(4, 1)
+    SLQ_GEMV_NT(1, kBatchNt1)
+    SLQ_GEMV_NT(2, kBatchNt2)
+    SLQ_GEMV_NT(4, kBatchNt4)
     default: return hipErrorInvalidValue;
   }
 #undef SLQ_GEMV_NT
 #undef SLQ_GEMV_LAUNCH
+#undef SLQ_GEMV_LAUNCH_WV
 }
 
 size_t gemv_rows_lds_bytes(int64_t m, int gw) {
@@ -817,6 +848,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // activation loads, whose L2 traffic grows with n * k * m / 16; narrower
   // layers and 17..32 rows measured faster with per-lane loads.
   p.rows = p.mt >= 3 && (n >= 8192 || k >= 8192);
+  p.wv = kWaves;
   if (p.rows) {
     // row-split kernel: 64 rows per workgroup; split k only for lack of
     // workgroups, keeping at least 8 groups per k-block
@@ -876,15 +908,30 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   p.mv = (G % 4) == 0 && gw_max >= 4 && per_limit(true) >= 4;
   const int64_t unit = p.mv ? 4 : 1;
   const int64_t per_max = std::max<int64_t>(1, per_limit(p.mv) / unit) * unit;
-  const int64_t cap =
-      std::max<int64_t>(unit, std::min<int64_t>(gw_max, per_max * kWaves) / unit * unit);
   const int64_t nb = (n + 16 * p.nt - 1) / (16 * p.nt);
   int64_t ks = std::max<int64_t>(ks_min, (target + nb - 1) / nb);
   ks = std::min<int64_t>(ks, std::max<int64_t>(1, G));
-  int64_t gw = std::max<int64_t>(1, (G + ks - 1) / ks);
-  gw = std::min<int64_t>((gw + unit - 1) / unit * unit, cap);
+  // groups per k-block when wv waves share it
+  auto k_block = [&](int wv) {
+    const int64_t cap =
+        std::max<int64_t>(unit, std::min<int64_t>(gw_max, per_max * wv) / unit * unit);
+    const int64_t g = std::max<int64_t>(1, (G + ks - 1) / ks);
+    return std::min<int64_t>((g + unit - 1) / unit * unit, cap);
+  };
+  int wv = kWaves;
+  if (p.mt == 1) {
+    int w = p.xd ? 8 : 16;
+    int64_t g = k_block(w);
+    while (w > kWaves && g / unit < w) {   // at least one unit of groups per wave
+      w /= 2;
+      g = k_block(w);
+    }
+    if (w > kWaves && nb * std::max<int64_t>(1, (G + g - 1) / g) <= kWvBlocks) wv = w;
+  }
+  p.wv = wv;
+  const int64_t gw = k_block(wv);
   p.gw = (int)gw;
-  p.b = (p.xd && p.mt > 1) ? 1 : 4 / p.nt;
+  p.b = (p.xd && p.mt > 1) ? 1 : p.nt == 1 ? kBatchNt1 : p.nt == 2 ? kBatchNt2 : kBatchNt4;
   p.ksplits = (int)std::max<int64_t>(1, (G + p.gw - 1) / p.gw);
   p.nblocks = (int)nb;
   if (p.nblocks > kMaxTicketBlocks && p.ksplits > 1) p.ksplits = 0;   // not supported

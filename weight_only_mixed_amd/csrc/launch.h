@@ -20,6 +20,7 @@ hipError_t launch_quant_error(const float *W, const uint32_t *codes, const float
 struct GemvPlan {
   int mt;          // 16-row tiles of x
   int nt;          // 16-row weight tiles per workgroup
+  int wv;          // wavefronts per workgroup (all on the same rows, splitting k)
   int b;           // groups per load batch
   int gw;          // 128-groups per k-block (workgroup)
   int nblocks;     // workgroups along n

@@ -159,8 +159,8 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
     if (p.rows)
       snprintf(buf, sizeof buf, "slq::gemv_rows_kernel<%d, %d>", w->bits, p.mt);
     else
-      snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s>", w->bits, p.mt, p.nt,
-               p.b, p.mv ? "true" : "false", p.xd ? "true" : "false");
+      snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s, %d>", w->bits, p.mt,
+               p.nt, p.b, p.mv ? "true" : "false", p.xd ? "true" : "false", p.wv);
   } else {
     snprintf(buf, sizeof buf, "slq::gemm_kernel<%d>", w->bits);
   }
