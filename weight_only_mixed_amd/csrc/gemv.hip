@@ -682,7 +682,10 @@ size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw, bool xd, int wv) {
   const size_t red = (size_t)wv * nt * mt * kWave * 16;
   return std::max(xs + meta, red) + 16;
 }
-constexpr size_t kLdsBudget = 65536;   // activation bytes per workgroup
+#ifndef SLQ_GEMV_LDS_BUDGET
+#define SLQ_GEMV_LDS_BUDGET 65536
+#endif
+constexpr size_t kLdsBudget = SLQ_GEMV_LDS_BUDGET;   // activation bytes per workgroup
 #ifndef SLQ_GEMV_TARGET_BLOCKS
 #define SLQ_GEMV_TARGET_BLOCKS 256
 #endif
@@ -695,7 +698,14 @@ constexpr int64_t kTargetBlocksTiny = SLQ_GEMV_TARGET_BLOCKS_TINY;
 #define SLQ_GEMV_XD_MIN_M 5
 #endif
 constexpr int64_t kXdMinM = SLQ_GEMV_XD_MIN_M;
-constexpr int64_t kXdMinGroups = 64;
+#ifndef SLQ_GEMV_XD_MIN_GROUPS
+#define SLQ_GEMV_XD_MIN_GROUPS 64
+#endif
+constexpr int64_t kXdMinGroups = SLQ_GEMV_XD_MIN_GROUPS;
+#ifndef SLQ_GEMV_ROWS_MIN_MT
+#define SLQ_GEMV_ROWS_MIN_MT 3
+#endif
+constexpr int kRowsMinMt = SLQ_GEMV_ROWS_MIN_MT;   // fewest m-tiles for the row-split kernel
 // Groups per load batch for 1, 2 and 4 row tiles (two batches in flight).
 #ifndef SLQ_GEMV_B_NT1
 #define SLQ_GEMV_B_NT1 4
@@ -822,6 +832,8 @@ hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const float *scal
                      const GemvPlan &plan, hipStream_t st) {
   if (plan.rows) {
     switch (plan.mt) {
+      case 1: return gemv_rows_launch<BITS, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      case 2: return gemv_rows_launch<BITS, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
       case 3: return gemv_rows_launch<BITS, 3>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
       case 4: return gemv_rows_launch<BITS, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
       default: return hipErrorInvalidValue;
@@ -847,7 +859,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // LDS copy of each group's activations for 64 weight rows) beats per-lane
   // activation loads, whose L2 traffic grows with n * k * m / 16; narrower
   // layers and 17..32 rows measured faster with per-lane loads.
-  p.rows = p.mt >= 3 && (n >= 8192 || k >= 8192);
+  p.rows = p.mt >= kRowsMinMt && (n >= 8192 || k >= 8192);
   p.wv = kWaves;
   if (p.rows) {
     // row-split kernel: 64 rows per workgroup; split k only for lack of
