@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default="all", help="extra rows: all, none, or a comma list of "
-                    "quantize,gemm,stack,fidelity,gamma")
+                    "quantize,gemm,stack,fidelity,allocation,gamma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--pmc", default=None, metavar="KERNEL",
@@ -128,7 +128,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     torch.manual_seed(0)
-    rows_sel = {"quantize", "gemm", "stack", "fidelity", "gamma"} if args.rows == "all" else (
+    rows_sel = {"quantize", "gemm", "stack", "fidelity", "allocation", "gamma"} if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
 
     def to_dev(a):
@@ -424,6 +424,29 @@ def main():
         res["top10_GBps"] = round(tk_b / (tk_ms * 1e-3) / 1e9, 1)   # same two logit tensors read
         rows["ear_kl"] = res
         log(f"bench: EAR/KL {gbs:.1f} GB/s, top-10 EAR/KL {res['top10_GBps']} GB/s")
+
+    # ---------------- bit-width allocation ----------------
+    if "allocation" in rows_sel:
+        log("bench: bit-width allocation, 224 projections x bits 2..8")
+        sz, cs, tau, names = S.allocation_table()
+        Wb = int(sz.max(axis=1).sum())
+        szd, csd = to_dev(sz), to_dev(cs)
+        ch, res, _, _ = slq.slq_mckp_search(szd, csd, Wb, tau)
+        torch.cuda.synchronize()
+        with Timer(torch) as T:
+            for _ in range(3):
+                slq.slq_mckp_search(szd, csd, Wb, tau)
+        ms = T.ms / 3
+        Lb, nb = sz.shape
+        # per item: one read of the previous row, one write of the next, one choice byte
+        nbytes = Lb * (Wb + 1) * (8 + 8 + 1)
+        r = res.cpu().numpy()
+        bits = np.arange(2, 9)[ch.cpu().numpy()]
+        rows["allocation"] = {"ms": round(ms, 3), "items": Lb, "options": nb, "budgets": Wb + 1,
+                              "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                              "status": int(r[0]), "budget_units": int(r[1]),
+                              "mean_bits": round(float((bits * sz[:, 0]).sum() / sz[:, 0].sum()), 3)}
+        log(f"bench: allocation {ms:.3f} ms")
 
     # ---------------- gamma-squared ----------------
     if "gamma" in rows_sel:

@@ -193,6 +193,34 @@ slq_status slq_ear_kl_topk(const float *logits_p, const float *logits_q, int64_t
                            int64_t vocab, int64_t K, double temperature, float *ear_rows,
                            float *kl_rows, double *means, void *workspace, slq_stream stream);
 
+/* Workspace bytes slq_mckp_search needs for L items and budgets 0..W. */
+size_t slq_mckp_workspace_bytes(int64_t L, int64_t W);
+
+/*
+ * Bit-width allocation (gist.science summary, 3. The SLQ Pipeline: a
+ * multiple-choice knapsack over the cost table solved exactly under a bit
+ * budget; README, Pipeline: binary-searched down to the target).
+ * Item l (a layer or projection) takes exactly one of nb options (bit-widths);
+ * option j occupies sizes[l*nb+j] budget units and costs costs[l*nb+j]
+ * (predicted degradation).  best(w) = least total cost with total size <= w
+ * (+inf when nothing fits), exact for every w in 0..W; the result is the
+ * smallest budget with best(w) finite and <= tau, and the selection attaining
+ * it (equal costs: the lower option index, read back from the last item).
+ * In : sizes int64 [L][nb] (device; negative sizes are never selected),
+ *      costs fp64 [L][nb] (device), 1 <= L, 1 <= nb <= 127, 0 <= W < 2^31 - 1,
+ *      tau not NaN.
+ * Out: choice int32 [L] (option per item, -1 when nothing fits in W);
+ *      result int64 [3] = {status, budget, size}: status 0 found, 1 even W
+ *      misses tau (budget -1, choice = the selection at W), 2 nothing fits
+ *      (budget and size -1); cost fp64 [1] = best(budget), or best(W);
+ *      best fp64 [W+1] or NULL: best(0..W).
+ * workspace: slq_mckp_workspace_bytes(L, W) bytes, 256-byte aligned.
+ * Deterministic and bit-identical across calls (fp64 sums in item order).
+ */
+slq_status slq_mckp_search(const int64_t *sizes, const double *costs, int64_t L, int32_t nb,
+                           int64_t W, double tau, int32_t *choice, int64_t *result, double *cost,
+                           double *best, void *workspace, slq_stream stream);
+
 /* Workspace bytes slq_quant_error needs for w. */
 size_t slq_quant_error_workspace_bytes(const slq_packed *w);
 

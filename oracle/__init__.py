@@ -41,6 +41,11 @@ def load(path: str):
     L.oracle_quant_error.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _int, _f64p]
     L.oracle_bits_per_param.argtypes = [_int, _int, _int]
     L.oracle_bits_per_param.restype = ctypes.c_double
+    L.oracle_mckp_search.argtypes = [_i64, _int, _i64p, _f64p, _i64, ctypes.c_double,
+                                     np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS"),
+                                     ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    L.oracle_mckp_search.restype = _int
     return L
 
 
@@ -174,3 +179,25 @@ def quant_error(W, w_hat, scales, group: int = 128):
 
 def bits_per_param(bits: int, meta_bits: int, group: int = 128) -> float:
     return lib().oracle_bits_per_param(bits, meta_bits, group)
+
+
+def mckp_search(sizes, costs, W: int, tau: float, with_best: bool = False):
+    """Bit-width allocation: exact multiple-choice knapsack over the cost table
+    for every budget 0..W, then the smallest budget whose optimal cost is <= tau.
+
+    sizes int64 [L][nb] (budget units), costs float64 [L][nb].  Returns
+    (status, choice int32 [L], budget, size, cost[, best float64 [W+1]]);
+    status 0: found, 1: W does not meet tau (choice at W), 2: nothing fits."""
+    sizes = _c(sizes, np.int64)
+    costs = _c(costs, np.float64)
+    L, nb = sizes.shape
+    if costs.shape != sizes.shape or not (1 <= nb <= 127) or W < 0 or (sizes < 0).any():
+        raise ValueError("bad knapsack instance")
+    choice = np.empty(L, np.int32)
+    budget, size, cost = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_double()
+    best = np.empty(W + 1, np.float64) if with_best else None
+    st = lib().oracle_mckp_search(L, nb, sizes, costs, int(W), float(tau), choice,
+                                  ctypes.byref(budget), ctypes.byref(size), ctypes.byref(cost),
+                                  best.ctypes.data if with_best else None)
+    out = (st, choice, budget.value, size.value, cost.value)
+    return out + (best,) if with_best else out

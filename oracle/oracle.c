@@ -22,6 +22,10 @@
  *               its base).
  *  [SLQ-blog-en] "SLQ: Bridging the Gap ..." : The Motivation (next-token
  *               probability distribution), The Math of Asymmetry.
+ *  [SLQ-summary] gist.science summary, "3. The SLQ Pipeline": bit-width
+ *               allocation as a multiple-choice knapsack problem solved exactly
+ *               (ILP) under a bit budget; [SLQ-readme] Pipeline paragraph: the
+ *               solve is binary-searched down to the target.
  * Where the pages leave a step open, the reading taken is stated at the
  * function (readings R1..R12 in the design notes).
  *
@@ -32,6 +36,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -371,4 +376,94 @@ void oracle_quant_error(const float *W, const float *w_hat, const float *scales,
  */
 double oracle_bits_per_param(int bits, int meta_bits, int group) {
   return (double)bits + (double)meta_bits / (double)group;
+}
+
+/*
+ * Bit-width allocation ([SLQ-summary] "3. The SLQ Pipeline": a multiple-choice
+ * knapsack over the cost table, solved exactly under a budget; [SLQ-readme]
+ * Pipeline: binary-searched down to the target).
+ *
+ * Items l = 0..L-1 (layers or projection groups) each take exactly one of nb
+ * options (bit-widths); option j of item l occupies sizes[l*nb+j] budget units
+ * and costs costs[l*nb+j] (predicted degradation).  For a budget w,
+ *   best(w) = min over selections with sum of sizes <= w of the sum of costs
+ * (+inf when nothing fits), computed by the textbook exact recurrence over the
+ * items in order:  f_0(w) = 0,  f_{l+1}(w) = min_j f_l(w - s_lj) + c_lj  over
+ * the options with s_lj <= w, ties to the lower j.  best is non-increasing in
+ * w, so the smallest budget in [0, W] at which something fits and best(w) <=
+ * tau is found by binary search; the selection is then read back from the
+ * recorded choices.
+ *
+ * Returns 0 when such a budget exists (budget_out = it), 1 when even W does
+ * not meet tau (budget_out = -1, choice = the selection at W), 2 when nothing
+ * fits in W (choice all -1).  best_out (optional) receives best(0..W).
+ */
+int oracle_mckp_search(int64_t L, int nb, const int64_t *sizes, const double *costs, int64_t W,
+                       double tau, int32_t *choice, int64_t *budget_out, int64_t *size_out,
+                       double *cost_out, double *best_out) {
+  const int64_t NW = W + 1;
+  double *prev = (double *)malloc(sizeof(double) * NW);
+  double *cur = (double *)malloc(sizeof(double) * NW);
+  int8_t *pick = (int8_t *)malloc((size_t)(L > 0 ? L : 1) * NW);
+  for (int64_t w = 0; w < NW; ++w) prev[w] = 0.0;   /* no items: cost 0 at any budget */
+  for (int64_t l = 0; l < L; ++l) {
+    for (int64_t w = 0; w < NW; ++w) {
+      double b = INFINITY;
+      int j_best = -1;
+      for (int j = 0; j < nb; ++j) {
+        const int64_t sz = sizes[l * nb + j];
+        if (sz > w) continue;
+        const double v = prev[w - sz] + costs[l * nb + j];
+        if (v < b) {
+          b = v;
+          j_best = j;
+        }
+      }
+      cur[w] = b;
+      pick[l * NW + w] = (int8_t)j_best;
+    }
+    double *t = prev;
+    prev = cur;
+    cur = t;
+  }
+  /* prev now holds best(0..W) */
+  if (best_out)
+    for (int64_t w = 0; w < NW; ++w) best_out[w] = prev[w];
+  /* a budget meets the target when something fits and its best cost <= tau */
+#define MEETS(w) (isfinite(prev[w]) && prev[w] <= tau)
+  int status;
+  int64_t budget;
+  if (!MEETS(W)) {
+    status = isinf(prev[W]) ? 2 : 1;
+    budget = W;
+  } else {
+    int64_t lo = 0, hi = W;   /* invariant: budget hi meets the target */
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (MEETS(mid)) hi = mid;
+      else lo = mid + 1;
+    }
+#undef MEETS
+    status = 0;
+    budget = lo;
+  }
+  int64_t total = 0;
+  if (status == 2) {
+    for (int64_t l = 0; l < L; ++l) choice[l] = -1;
+  } else {
+    int64_t w = budget;
+    for (int64_t l = L - 1; l >= 0; --l) {
+      const int j = pick[l * NW + w];
+      choice[l] = j;
+      w -= sizes[l * nb + j];
+      total += sizes[l * nb + j];
+    }
+  }
+  *budget_out = status == 0 ? budget : -1;
+  *size_out = status == 2 ? -1 : total;
+  *cost_out = status == 2 ? INFINITY : prev[budget];
+  free(prev);
+  free(cur);
+  free(pick);
+  return status;
 }

@@ -27,6 +27,9 @@ void oracle_ear_kl_topk(const float *a, const float *b, int64_t rows, int64_t vo
 void oracle_quant_error(const float *W, const float *w_hat, const float *scales,
                         int64_t n, int64_t k, int group, double *out);
 double oracle_bits_per_param(int bits, int meta_bits, int group);
+int oracle_mckp_search(int64_t L, int nb, const int64_t *sizes, const double *costs, int64_t W,
+                       double tau, int32_t *choice, int64_t *budget_out, int64_t *size_out,
+                       double *cost_out, double *best_out);
 
 #ifdef __cplusplus
 }

@@ -127,6 +127,41 @@ def mixed_bit_map(layers: int = 32, seed: int = seed_for(3)):
     return out
 
 
+def allocation_table(layers: int = 32, shapes=None, bits=tuple(range(2, 9)),
+                     meta_bits: int = 40, seed: int = seed_for(3, 1)):
+    """Synthetic per-(projection, bit-width) table for the bit-width allocation
+    of a `layers`-deep decoder (Llama-3-8B projection shapes by default).
+
+    sizes[i][j]: storage of projection i at bits[j] in budget units of
+    (unit groups) x 8 bits, i.e. G_i / unit * (128 * b + meta_bits) / 8 with
+    G_i = n * k / 128 groups and unit = gcd of the G_i.
+    costs[i][j]: a stand-in for the Shapley cost table, s_i * 4^-b (rounding
+    noise variance falls by 4 per bit), with a per-size sensitivity of 256 for
+    k/v, 16 for q/o and 1 for the MLP (a lognormal jitter of 0.3 per
+    projection), so that the optimum at the class mid-points puts k/v, q/o and
+    the MLP in the bit-width classes of the mixed stack.
+    tau: the cost of the class mid-points, sum_i s_i (4^-lo + 4^-hi) / 2.
+    Returns (sizes int64 [L][nb], costs float64 [L][nb], tau, names)."""
+    shapes = LLAMA3_8B_PROJ if shapes is None else shapes
+    g = rng(seed)
+    groups = {p: shapes[p][0] * shapes[p][1] // 128 for p in PROJ_ORDER}
+    unit = int(np.gcd.reduce(np.array(list(groups.values()), np.int64)))
+    per = {"q": 16.0, "o": 16.0, "k": 256.0, "v": 256.0, "gate": 1.0, "up": 1.0, "down": 1.0}
+    assert (128 * np.array(bits) + meta_bits).min() % 8 == 0 and meta_bits % 8 == 0
+    sizes, costs, names = [], [], []
+    tau = 0.0
+    for layer in range(layers):
+        for p in PROJ_ORDER:
+            u = groups[p] // unit
+            sizes.append([u * (128 * b + meta_bits) // 8 for b in bits])
+            sens = u * per[p] * float(np.exp(0.3 * g.standard_normal()))
+            costs.append([sens * 4.0 ** (-b) for b in bits])
+            lo, hi = BIT_CLASSES[p]
+            tau += sens * (4.0 ** (-lo) + 4.0 ** (-hi)) / 2
+            names.append(f"{layer}.{p}")
+    return np.array(sizes, np.int64), np.array(costs, np.float64), tau, names
+
+
 def uniform_group_weights(n_groups: int, lo: float, hi: float, seed: int,
                           group: int = 128) -> np.ndarray:
     """Rows of uniform[lo, hi] samples with both endpoints pinned in every group.

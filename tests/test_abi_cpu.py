@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for name in names:
         assert hasattr(L, name), name
 
@@ -120,6 +120,18 @@ def test_fidelity_and_error_validation():
     assert T(A + 4, B, 4, 100, 10, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL  # misaligned
     assert T(A, B, 4, 0, 1, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL        # empty vocab
     assert T(A, B, 0, 10, 5, 1.0, None, None, None, None, None) == slq.SLQ_OK
+    M = L.slq_mckp_search
+    assert M(A, B, 0, 7, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL   # L = 0
+    assert M(A, B, 4, 0, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL   # nb = 0
+    assert M(A, B, 4, 128, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL  # nb > 127
+    assert M(A, B, 4, 7, -1, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL   # W < 0
+    assert M(A, B, 4, 7, 100, float("nan"), C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL
+    assert M(A, B, 4, 7, 100, 1.0, C, C + 256, C + 512, None, None, None) == slq.SLQ_EINVAL  # no ws
+    assert M(A, B, 4, 7, 100, 1.0, C, C, C + 512, None, E, None) == slq.SLQ_EINVAL        # aliasing
+    assert M(A, B, 4, 7, 100, 1.0, A, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL  # over sizes
+    assert M(A + 4, B, 4, 7, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL  # align
+    assert L.slq_mckp_workspace_bytes(224, 221312) >= 2 * 221313 * 8 + 224 * 221313
+    assert L.slq_mckp_workspace_bytes(0, 10) == 0
     assert L.slq_row_lse(A, 4, 0, C, E, None) == slq.SLQ_EINVAL
     assert L.slq_row_lse(A, 4, 10, A, E, None) == slq.SLQ_EINVAL                   # lse aliases input
     assert L.slq_quant_error(A, ctypes.byref(packed(bits=1)), C, E, None) == slq.SLQ_EINVAL

@@ -14,7 +14,7 @@ import tempfile
 import pytest
 
 import oracle
-from tests import (test_oracle_fidelity, test_oracle_gamma, test_oracle_gemm,
+from tests import (test_oracle_fidelity, test_oracle_gamma, test_oracle_gemm, test_oracle_mckp,
                    test_oracle_pack, test_oracle_quant, test_oracle_topk)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -56,6 +56,11 @@ MUTANTS = {
                                  "means[0] = rows > 1 ? se / (double)(rows - 1) : 0.0;"),
     "sse_not_squared": ("rs += e * e;", "rs += fabs(e);"),
     "bpp_meta_per_group": ("(double)meta_bits / (double)group", "(double)meta_bits / (double)(2 * group)"),
+    "mckp_size_strictly_below": ("if (sz > w) continue;", "if (sz >= w) continue;"),
+    "mckp_max_not_min": ("        if (v < b) {\n          b = v;", "        if (!(v < b) || isinf(b)) {\n          b = v;"),
+    "mckp_ties_to_higher": ("        if (v < b) {\n          b = v;", "        if (v <= b) {\n          b = v;"),
+    "mckp_search_off_by_one": ("      else lo = mid + 1;", "      else lo = mid + 2;"),
+    "mckp_readback_wrong_row": ("const int j = pick[l * NW + w];", "const int j = pick[(L - 1 - l) * NW + w];"),
 }
 
 
@@ -63,7 +68,7 @@ def _pin_calls():
     """Every pin with every parameter value, as zero-argument callables."""
     calls = []
     for mod in (test_oracle_quant, test_oracle_pack, test_oracle_gemm,
-                test_oracle_fidelity, test_oracle_gamma, test_oracle_topk):
+                test_oracle_fidelity, test_oracle_gamma, test_oracle_topk, test_oracle_mckp):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue

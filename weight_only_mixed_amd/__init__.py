@@ -58,6 +58,10 @@ def lib():
         L.slq_ear_kl.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
         L.slq_ear_kl_topk.argtypes = [_vp, _vp, _i64, _i64, _i64, ctypes.c_double, _vp, _vp, _vp,
                                       _vp, _vp]
+        L.slq_mckp_workspace_bytes.argtypes = [_i64, _i64]
+        L.slq_mckp_workspace_bytes.restype = _sz
+        L.slq_mckp_search.argtypes = [_vp, _vp, _i64, ctypes.c_int32, _i64, ctypes.c_double, _vp,
+                                      _vp, _vp, _vp, _vp, _vp]
         L.slq_quant_error_workspace_bytes.argtypes = [_pp]
         L.slq_quant_error_workspace_bytes.restype = _sz
         L.slq_quant_error.argtypes = [_vp, _pp, _vp, _vp, _vp]
@@ -66,7 +70,7 @@ def lib():
         L.slq_strerror.argtypes = [_int]
         L.slq_strerror.restype = ctypes.c_char_p
         for f in ("slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm", "slq_row_lse",
-                  "slq_ear_kl", "slq_ear_kl_topk", "slq_quant_error"):
+                  "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_quant_error"):
             getattr(L, f).restype = _int
         _LIB = L
     return _LIB
@@ -221,6 +225,28 @@ def slq_ear_kl_topk(logits_p: torch.Tensor, logits_q: torch.Tensor, k: int,
     return ear, kl, means
 
 
+def slq_mckp_search(sizes: torch.Tensor, costs: torch.Tensor, W: int, tau: float,
+                    with_best: bool = False):
+    """Bit-width allocation on the device: exact multiple-choice knapsack for
+    budgets 0..W, smallest budget whose best cost is <= tau.  sizes int64
+    [L][nb], costs float64 [L][nb] (device).  Returns (choice int32 [L],
+    result int64 [3] = status, budget, size; cost float64 [1]; best or None)."""
+    assert sizes.dtype == torch.int64 and costs.dtype == torch.float64
+    assert sizes.shape == costs.shape and sizes.is_contiguous() and costs.is_contiguous()
+    L, nb = sizes.shape
+    dev = sizes.device
+    choice = torch.empty(L, dtype=torch.int32, device=dev)
+    result = torch.empty(3, dtype=torch.int64, device=dev)
+    cost = torch.empty(1, dtype=torch.float64, device=dev)
+    best = torch.empty(W + 1, dtype=torch.float64, device=dev) if with_best else None
+    ws = workspace(lib().slq_mckp_workspace_bytes(L, W), dev, "mckp")
+    _check(lib().slq_mckp_search(_ptr(sizes), _ptr(costs), L, nb, int(W), float(tau),
+                                 _ptr(choice), _ptr(result), _ptr(cost),
+                                 _ptr(best) if with_best else None, _ptr(ws), _stream(sizes)),
+           "slq_mckp_search")
+    return choice, result, cost, best
+
+
 def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
     """fp64 [2] on the device: (sum (w - w_hat)^2, sum_g s_g^2)."""
     desc = pw.c()
@@ -233,4 +259,4 @@ def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
 
 __all__ = ["lib", "SlqError", "SlqPacked", "PackedWeight", "alloc_packed", "workspace",
            "gemm_workspace_bytes", "kernel_name", "slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm",
-           "slq_row_lse", "slq_ear_kl", "slq_ear_kl_topk", "slq_quant_error", "SLQ_ASYM", "SLQ_SYM", "GROUP"]
+           "slq_row_lse", "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_quant_error", "SLQ_ASYM", "SLQ_SYM", "GROUP"]

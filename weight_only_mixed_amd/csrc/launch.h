@@ -47,6 +47,10 @@ hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *l
                           hipStream_t s);
 hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab, float *ear,
                          float *kl, double *means, void *ws, hipStream_t s);
+size_t mckp_workspace(int64_t L, int64_t W);
+hipError_t launch_mckp(const int64_t *sizes, const double *costs, int64_t L, int nb, int64_t W,
+                       double tau, int32_t *choice, int64_t *result, double *cost, double *best,
+                       void *ws, hipStream_t s);
 constexpr int kTopKMax = 64;   // largest k of the top-K metrics
 // invT = 1 / temperature.
 hipError_t launch_ear_kl_topk(const float *a, const float *b, int64_t rows, int64_t vocab, int k,

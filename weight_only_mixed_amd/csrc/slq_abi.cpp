@@ -247,6 +247,36 @@ slq_status slq_ear_kl_topk(const float *logits_p, const float *logits_q, int64_t
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t slq_mckp_workspace_bytes(int64_t L, int64_t W) {
+  if (L < 1 || L >= kMaxDim || W < 0 || W >= kMaxDim - 1) return 0;
+  return slq::mckp_workspace(L, W);
+}
+
+slq_status slq_mckp_search(const int64_t *sizes, const double *costs, int64_t L, int32_t nb,
+                           int64_t W, double tau, int32_t *choice, int64_t *result, double *cost,
+                           double *best, void *workspace, slq_stream stream) {
+  if (L < 1 || L >= kMaxDim || nb < 1 || nb > 127 || W < 0 || W >= kMaxDim - 1) return SLQ_EINVAL;
+  if (std::isnan(tau)) return SLQ_EINVAL;
+  if (!sizes || !costs || !choice || !result || !cost || !workspace) return SLQ_EINVAL;
+  if (!aligned(sizes, 8) || !aligned(costs, 8) || !aligned(choice, 4) || !aligned(result, 8) ||
+      !aligned(cost, 8) || !aligned(workspace, 256) || (best && !aligned(best, 8)))
+    return SLQ_EINVAL;
+  const size_t tb = (size_t)L * nb * 8;
+  const size_t wsb = slq_mckp_workspace_bytes(L, W);
+  const void *outs[5] = {choice, result, cost, workspace, best};
+  const size_t outb[5] = {(size_t)L * 4, 3 * sizeof(int64_t), sizeof(double), wsb,
+                          best ? (size_t)(W + 1) * sizeof(double) : 0};
+  for (int i = 0; i < 5; ++i) {
+    if (!outs[i]) continue;
+    if (overlap(outs[i], outb[i], sizes, tb) || overlap(outs[i], outb[i], costs, tb))
+      return SLQ_EINVAL;
+    for (int j = i + 1; j < 5; ++j)
+      if (outs[j] && overlap(outs[i], outb[i], outs[j], outb[j])) return SLQ_EINVAL;
+  }
+  return from_hip(slq::launch_mckp(sizes, costs, L, nb, W, tau, choice, result, cost, best,
+                                   workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t slq_quant_error_workspace_bytes(const slq_packed *w) {
   PackedSizes sz;
   if (check_packed(w, &sz) != SLQ_OK) return 0;
