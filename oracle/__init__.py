@@ -46,6 +46,16 @@ def load(path: str):
                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     L.oracle_mckp_search.restype = _int
+    L.oracle_f16_value.argtypes = [ctypes.c_uint16]
+    L.oracle_f16_value.restype = ctypes.c_double
+    L.oracle_f16_round_up.argtypes = [ctypes.c_float]
+    L.oracle_f16_round_up.restype = ctypes.c_uint16
+    L.oracle_compact_zero_bits.argtypes = [_int]
+    L.oracle_compact_zero_bits.restype = _int
+    L.oracle_quantize_compact.argtypes = [_f32p, _i64, _i64, _int, _int, _int, _u8p, _u16p, _u8p]
+    L.oracle_pack_zeros.argtypes = [_u8p, _i64, _int, _u8p]
+    L.oracle_pack_zeros.restype = _i64
+    L.oracle_dequantize_compact.argtypes = [_u8p, _u16p, _u8p, _i64, _i64, _int, _int, _f32p]
     return L
 
 
@@ -201,3 +211,44 @@ def mckp_search(sizes, costs, W: int, tau: float, with_best: bool = False):
                                   best.ctypes.data if with_best else None)
     out = (st, choice, budget.value, size.value, cost.value)
     return out + (best,) if with_best else out
+
+
+def f16_value(bits: int) -> float:
+    return lib().oracle_f16_value(int(bits))
+
+
+def f16_round_up(s: float) -> int:
+    """Bits of the smallest binary16 value >= s (s > 0), saturating at 65504."""
+    return int(lib().oracle_f16_round_up(float(s)))
+
+
+def compact_zero_bits(bits: int) -> int:
+    return lib().oracle_compact_zero_bits(bits)
+
+
+def quantize_compact(W, bits: int, group: int = 128, symmetric: bool = False):
+    """Codes uint8 [n][k], binary16 scale bits uint16 [n][G], zero points uint8 [n][G]."""
+    W = _c(W, np.float32)
+    n, k = W.shape
+    q = np.empty((n, k), np.uint8)
+    s16 = np.empty((n, k // group), np.uint16)
+    z = np.empty((n, k // group), np.uint8)
+    lib().oracle_quantize_compact(W, n, k, bits, group, int(symmetric), q, s16, z)
+    return q, s16, z
+
+
+def pack_zeros(zeros, bits: int):
+    """Compact zero points: nibbles (b <= 4, low nibble first) or bytes."""
+    z = _c(zeros, np.uint8).ravel()
+    out = np.empty(len(z), np.uint8)
+    nb = lib().oracle_pack_zeros(z, len(z), bits, out)
+    return out[:nb].copy()
+
+
+def dequantize_compact(q, scales16, zpacked, bits: int, group: int = 128):
+    q = _c(q, np.uint8)
+    n, k = q.shape
+    out = np.empty((n, k), np.float32)
+    lib().oracle_dequantize_compact(q, _c(scales16, np.uint16).ravel(), _c(zpacked, np.uint8),
+                                    n, k, group, bits, out)
+    return out

@@ -22,6 +22,9 @@
  *               its base).
  *  [SLQ-blog-en] "SLQ: Bridging the Gap ..." : The Motivation (next-token
  *               probability distribution), The Math of Asymmetry.
+ *  [SLQ-readme] Search: the bit-width map adds 0.156 bits per parameter of
+ *               scale and zero point (20 bits per 128-group); Evaluation:
+ *               Uniform-4 at 4.16 bpp.
  *  [SLQ-summary] gist.science summary, "3. The SLQ Pipeline": bit-width
  *               allocation as a multiple-choice knapsack problem solved exactly
  *               (ILP) under a bit budget; [SLQ-readme] Pipeline paragraph: the
@@ -466,4 +469,127 @@ int oracle_mckp_search(int64_t L, int nb, const int64_t *sizes, const double *co
   free(cur);
   free(pick);
   return status;
+}
+
+/*
+ * Compact group metadata ([SLQ-readme] Search: 0.156 bits per parameter of
+ * metadata, i.e. 20 bits per 128-group; Evaluation: Uniform-4 at 4.16 bpp).
+ * Readings R24-R27: the scale is stored in IEEE binary16, rounded UP from the
+ * fp32 scale so the grid still spans [lo, hi] and the half-step bound holds;
+ * the zero point and codes are computed with the stored scale; the zero point
+ * takes 4 bits for b <= 4 (16 + 4 = 20 bits) and 8 bits above.
+ */
+
+/* Value of binary16 bits (positive, finite), from the format's definition:
+ * exponent field e, fraction f: e == 0 -> f * 2^-24, else (1 + f/1024) 2^(e-15). */
+double oracle_f16_value(uint16_t bits) {
+  const int e = (bits >> 10) & 31, f = bits & 1023;
+  if (e == 0) return ldexp((double)f, -24);
+  return ldexp(1.0 + (double)f / 1024.0, e - 15);
+}
+
+/* The smallest binary16 value >= s (s > 0, finite), as bits; values above
+ * 65504 saturate at 65504.  The spacing of binary16 around s is 2^(E - 10)
+ * for 2^E <= s < 2^(E+1), E >= -14, and 2^-24 below 2^-14; s / spacing is
+ * exact in fp64, so ceil() gives the round-up exactly. */
+uint16_t oracle_f16_round_up(float s) {
+  const double v = (double)s;
+  if (v >= 65504.0) return 0x7BFF;
+  int e2;
+  frexp(v, &e2);   /* v = f * 2^e2, f in [0.5, 1): 2^(e2-1) <= v < 2^e2 */
+  const int E = e2 - 1;
+  const double spacing = E < -14 ? ldexp(1.0, -24) : ldexp(1.0, E - 10);
+  const double r = ceil(v / spacing) * spacing;
+  if (r < ldexp(1.0, -14)) return (uint16_t)(r / ldexp(1.0, -24));   /* subnormal */
+  int er;
+  frexp(r, &er);
+  const int Er = er - 1;
+  const int frac = (int)((r / ldexp(1.0, Er) - 1.0) * 1024.0);
+  return (uint16_t)(((Er + 15) << 10) | frac);
+}
+
+/* Zero-point bits of the compact layout: 4 for b <= 4, else 8. */
+int oracle_compact_zero_bits(int bits) { return bits <= 4 ? 4 : 8; }
+
+/*
+ * Asymmetric (or symmetric) group quantization with compact metadata: the
+ * steps of oracle_quantize, except that s is replaced by the binary16 value
+ * rounded up from it before z and q are computed.  scales16[i] holds its
+ * bits and zeros[i] the zero point (one byte per group, unpacked; see
+ * oracle_pack_zeros), i = row * G + g.
+ */
+void oracle_quantize_compact(const float *W, int64_t n, int64_t k, int bits, int group,
+                             int symmetric, uint8_t *q, uint16_t *scales16, uint8_t *zeros) {
+  const int maxq = (1 << bits) - 1;
+  const int64_t G = k / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t g = 0; g < G; ++g) {
+      const float *w = W + r * k + g * group;
+      float s, lo = 0.0f;
+      int z;
+      if (!symmetric) {
+        float hi = 0.0f;
+        for (int i = 0; i < group; ++i) {
+          if (w[i] < lo) lo = w[i];
+          if (w[i] > hi) hi = w[i];
+        }
+        s = (hi - lo) / (float)maxq;
+      } else {
+        float m = 0.0f;
+        for (int i = 0; i < group; ++i) {
+          float a = fabsf(w[i]);
+          if (a > m) m = a;
+        }
+        s = (2.0f * m) / (float)maxq;
+      }
+      uint16_t h;
+      if (s == 0.0f) {
+        h = 0x3C00; /* 1.0 */
+        s = 1.0f;
+        z = symmetric ? 1 << (bits - 1) : 0;
+      } else {
+        h = oracle_f16_round_up(s);
+        s = (float)oracle_f16_value(h);
+        z = symmetric ? 1 << (bits - 1) : (int)clamp_code(rintf(-lo / s), maxq);
+      }
+      scales16[r * G + g] = h;
+      zeros[r * G + g] = (uint8_t)z;
+      for (int i = 0; i < group; ++i) {
+        const float tq = rintf(w[i] / s);
+        q[r * k + g * group + i] = (uint8_t)(int)clamp_code(tq + (float)z, maxq);
+      }
+    }
+  }
+}
+
+/* Zero points of `count` groups in the compact layout: nibble i of the byte
+ * stream (low nibble first) for b <= 4, else byte i.  Returns bytes written. */
+int64_t oracle_pack_zeros(const uint8_t *zeros, int64_t count, int bits, uint8_t *out) {
+  if (oracle_compact_zero_bits(bits) == 8) {
+    for (int64_t i = 0; i < count; ++i) out[i] = zeros[i];
+    return count;
+  }
+  const int64_t nb = (count + 1) / 2;
+  for (int64_t i = 0; i < nb; ++i) out[i] = 0;
+  for (int64_t i = 0; i < count; ++i) out[i / 2] |= (uint8_t)((zeros[i] & 15) << (4 * (i % 2)));
+  return nb;
+}
+
+/* Reconstruction from compact metadata: w_hat = fl32((q - z) * s), s the
+ * binary16 scale's value, z read from the packed zero points. */
+void oracle_dequantize_compact(const uint8_t *q, const uint16_t *scales16, const uint8_t *zpacked,
+                               int64_t n, int64_t k, int group, int bits, float *w_hat) {
+  const int64_t G = k / group;
+  const int zb = oracle_compact_zero_bits(bits);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t i = r * G + j / group;
+      const int z = zb == 8 ? zpacked[i] : (zpacked[i / 2] >> (4 * (i % 2))) & 15;
+      const float s = (float)oracle_f16_value(scales16[i]);
+      float d = (float)((int)q[r * k + j] - z);
+      w_hat[r * k + j] = d * s;
+    }
+  }
 }

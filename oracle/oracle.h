@@ -27,6 +27,14 @@ void oracle_ear_kl_topk(const float *a, const float *b, int64_t rows, int64_t vo
 void oracle_quant_error(const float *W, const float *w_hat, const float *scales,
                         int64_t n, int64_t k, int group, double *out);
 double oracle_bits_per_param(int bits, int meta_bits, int group);
+double oracle_f16_value(uint16_t bits);
+uint16_t oracle_f16_round_up(float s);
+int oracle_compact_zero_bits(int bits);
+void oracle_quantize_compact(const float *W, int64_t n, int64_t k, int bits, int group,
+                             int symmetric, uint8_t *q, uint16_t *scales16, uint8_t *zeros);
+int64_t oracle_pack_zeros(const uint8_t *zeros, int64_t count, int bits, uint8_t *out);
+void oracle_dequantize_compact(const uint8_t *q, const uint16_t *scales16, const uint8_t *zpacked,
+                               int64_t n, int64_t k, int group, int bits, float *w_hat);
 int oracle_mckp_search(int64_t L, int nb, const int64_t *sizes, const double *costs, int64_t W,
                        double tau, int32_t *choice, int64_t *budget_out, int64_t *size_out,
                        double *cost_out, double *best_out);

@@ -14,8 +14,8 @@ import tempfile
 import pytest
 
 import oracle
-from tests import (test_oracle_fidelity, test_oracle_gamma, test_oracle_gemm, test_oracle_mckp,
-                   test_oracle_pack, test_oracle_quant, test_oracle_topk)
+from tests import (test_oracle_compact, test_oracle_fidelity, test_oracle_gamma, test_oracle_gemm,
+                   test_oracle_mckp, test_oracle_pack, test_oracle_quant, test_oracle_topk)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 HDR_DIR = os.path.dirname(SRC)
@@ -61,6 +61,16 @@ MUTANTS = {
     "mckp_ties_to_higher": ("        if (v < b) {\n          b = v;", "        if (v <= b) {\n          b = v;"),
     "mckp_search_off_by_one": ("      else lo = mid + 1;", "      else lo = mid + 2;"),
     "mckp_readback_wrong_row": ("const int j = pick[l * NW + w];", "const int j = pick[(L - 1 - l) * NW + w];"),
+    "f16_round_to_nearest": ("const double r = ceil(v / spacing) * spacing;",
+                             "const double r = rint(v / spacing) * spacing;"),
+    "f16_spacing_off_by_one": ("ldexp(1.0, E - 10);\n", "ldexp(1.0, E - 9);\n"),
+    "f16_value_bias": ("return ldexp(1.0 + (double)f / 1024.0, e - 15);", "return ldexp(1.0 + (double)f / 1024.0, e - 14);"),
+    "compact_zero_from_fp32_scale": ("        s = (float)oracle_f16_value(h);\n        z =",
+                                     "        z ="),
+    "compact_nibble_high_first": ("out[i / 2] |= (uint8_t)((zeros[i] & 15) << (4 * (i % 2)));",
+                                  "out[i / 2] |= (uint8_t)((zeros[i] & 15) << (4 * (1 - i % 2)));"),
+    "compact_zero_bits_always_4": ("int oracle_compact_zero_bits(int bits) { return bits <= 4 ? 4 : 8; }",
+                                   "int oracle_compact_zero_bits(int bits) { return 4; }"),
 }
 
 
@@ -68,7 +78,8 @@ def _pin_calls():
     """Every pin with every parameter value, as zero-argument callables."""
     calls = []
     for mod in (test_oracle_quant, test_oracle_pack, test_oracle_gemm,
-                test_oracle_fidelity, test_oracle_gamma, test_oracle_topk, test_oracle_mckp):
+                test_oracle_fidelity, test_oracle_gamma, test_oracle_topk, test_oracle_mckp,
+                test_oracle_compact):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
