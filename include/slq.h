@@ -51,6 +51,12 @@ typedef enum {
   SLQ_SYM = 1       /* symmetric grid (comparison only): center 2^(b-1)      */
 } slq_grid;
 
+typedef enum {
+  SLQ_META_F32 = 0,     /* fp32 scale + uint8 zero point per group (40 bits)      */
+  SLQ_META_COMPACT = 1  /* binary16 scale rounded up + 4-bit zero point (b <= 4,
+                           20 bits per group) or 8-bit zero point (b >= 5)       */
+} slq_meta;
+
 typedef void *slq_stream; /* a hipStream_t */
 
 /*
@@ -61,10 +67,22 @@ typedef void *slq_stream; /* a hipStream_t */
  *            integer sum_i codes[row][i] * 2^(32 i); group g starts at word
  *            4*bits*g.  For bits = 4 this is 8 codes per word, nibble j = code
  *            j; 3/5/6/7-bit codes straddle word boundaries with no padding.
- *   scales : fp32 [n][G], > 0.
- *   zeros  : uint8 [n][G], in [0, 2^bits - 1].
- * Reconstruction: w_hat[n][k] = fl32((q[n][k] - zeros[n][g]) * scales[n][g]).
- * Storage: bits + 40/group bits per parameter (fp32 scale + u8 zero point).
+ *   scales, zeros: group metadata, flat group index i = row * G + g, in one of
+ *   two layouts (`meta`):
+ *   SLQ_META_F32     scales fp32 [n*G] (> 0), zeros uint8 [n*G] in
+ *                    [0, 2^bits - 1]: bits + 40/group bits per parameter.
+ *   SLQ_META_COMPACT scales binary16 [n*G]: the fp32 scale rounded up to the
+ *                    next binary16 value (so the half-step error bound still
+ *                    holds), and the zero point and codes are computed with that
+ *                    scale; zeros: 4-bit nibbles for bits <= 4 (nibble i of the
+ *                    byte stream, low nibble first: ceil(n*G/2) bytes), bytes
+ *                    for bits >= 5.  bits + 20/group bits per parameter for
+ *                    bits <= 4, the README's 0.156 bpp of metadata (Search:
+ *                    bit-width map; Evaluation: Uniform-4 at 4.16 bpp), and
+ *                    bits + 24/group above.  Scales beyond the binary16 range
+ *                    (65504) saturate; no weight of a real model comes near.
+ * Reconstruction: w_hat[n][k] = fl32((q[n][k] - z[i]) * s[i]), s in fp32.
+ * Alignment: codes and scales 16 bytes, zeros 4 bytes.
  */
 typedef struct {
   int32_t bits;   /* 2..8                                   */
@@ -72,12 +90,18 @@ typedef struct {
   int64_t n;      /* rows (outputs)                         */
   int64_t k;      /* columns (inputs), a multiple of group  */
   uint32_t *codes;
-  float *scales;
+  void *scales;   /* fp32 or binary16, per `meta`           */
   uint8_t *zeros;
+  int32_t meta;   /* slq_meta                               */
+  int32_t reserved;
 } slq_packed;
 
 /* Bytes of the codes array: n*k*bits/8 (0 on invalid arguments). */
 size_t slq_codes_bytes(int64_t n, int64_t k, int bits);
+/* Bytes of the scales and zeros arrays for a metadata layout (0 on invalid
+ * arguments; group 128). */
+size_t slq_scales_bytes(int64_t n, int64_t k, int32_t meta);
+size_t slq_zeros_bytes(int64_t n, int64_t k, int bits, int32_t meta);
 
 /*
  * Group quantization and dense packing of an fp32 weight (gist.science
@@ -91,13 +115,15 @@ size_t slq_codes_bytes(int64_t n, int64_t k, int bits);
  *             (the comparison grid of Methodology 1).
  *   q = clamp(rint(fl32(w / s)) + z, 0, maxq); rint rounds half to even and
  *   every fp32 operation is IEEE correctly rounded, so the result is exact
- *   and reproducible bit for bit.
+ *   and reproducible bit for bit.  With out->meta = SLQ_META_COMPACT, s is
+ *   rounded up to binary16 before z and q are computed.
  * In : W fp32 [n][k] (device, 16-byte aligned), n >= 0, k % group == 0,
  *      bits in 2..8, group == 128 (else SLQ_ENOTSUP).
- * Out: out->codes/scales/zeros must point to caller-owned device buffers of
- *      slq_codes_bytes(n,k,bits), 4*n*(k/group) and n*(k/group) bytes, codes
- *      16-byte aligned, none overlapping W.  The call fills out->bits, group,
- *      n and k and writes the three arrays.
+ * Out: out->meta selects the metadata layout; out->codes/scales/zeros must
+ *      point to caller-owned device buffers of slq_codes_bytes(n,k,bits),
+ *      slq_scales_bytes(n,k,meta) and slq_zeros_bytes(n,k,bits,meta) bytes,
+ *      aligned as above, none overlapping W.  The call fills out->bits,
+ *      group, n and k and writes the three arrays.
  */
 slq_status slq_quantize_pack(const float *W, int64_t n, int64_t k, int bits, int group,
                              slq_grid grid, slq_packed *out, slq_stream stream);

@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for name in names:
         assert hasattr(L, name), name
 
@@ -134,6 +134,13 @@ def test_fidelity_and_error_validation():
     assert L.slq_mckp_workspace_bytes(0, 10) == 0
     assert L.slq_row_lse(A, 4, 0, C, E, None) == slq.SLQ_EINVAL
     assert L.slq_row_lse(A, 4, 10, A, E, None) == slq.SLQ_EINVAL                   # lse aliases input
+    bad_meta = packed()
+    bad_meta.meta = 2
+    assert L.slq_dequantize(ctypes.byref(bad_meta), E, None) == slq.SLQ_EINVAL            # layout
+    assert L.slq_dequantize(ctypes.byref(packed(scales=C + 4)), E, None) == slq.SLQ_EINVAL  # align
+    assert L.slq_scales_bytes(10, 1024, 1) == 160 and L.slq_scales_bytes(10, 1024, 0) == 320
+    assert L.slq_zeros_bytes(7, 384, 3, 1) == 11 and L.slq_zeros_bytes(7, 384, 5, 1) == 21
+    assert L.slq_zeros_bytes(7, 384, 3, 2) == 0 and L.slq_scales_bytes(7, 100, 0) == 0
     assert L.slq_quant_error(A, ctypes.byref(packed(bits=1)), C, E, None) == slq.SLQ_EINVAL
     assert L.slq_quant_error(A, ctypes.byref(packed()), None, E, None) == slq.SLQ_EINVAL
     assert L.slq_quant_error(A, ctypes.byref(packed()), C, None, None) == slq.SLQ_EINVAL
@@ -152,7 +159,7 @@ def test_sizes_and_strings():
     assert L.slq_quant_error_workspace_bytes(ctypes.byref(packed())) > 0
     name = L.slq_dequant_gemm_kernel_name(1, ctypes.byref(packed(n=4096, k=4096)))
     assert name.startswith(b"slq::gemv_kernel<4, 1,")
-    assert L.slq_dequant_gemm_kernel_name(100, ctypes.byref(packed())) == b"slq::gemm_kernel<4>"
+    assert L.slq_dequant_gemm_kernel_name(100, ctypes.byref(packed())) == b"slq::gemm_kernel<4, false>"
     assert L.slq_dequant_gemm_kernel_name(1, ctypes.byref(packed(bits=9))) == b""
     for s in range(4):
         assert L.slq_strerror(s)

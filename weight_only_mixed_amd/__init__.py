@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libslq.so")
 
 SLQ_OK, SLQ_EINVAL, SLQ_ENOTSUP, SLQ_EHIP = 0, 1, 2, 3
 SLQ_ASYM, SLQ_SYM = 0, 1
+SLQ_META_F32, SLQ_META_COMPACT = 0, 1
 GROUP = 128
 
 
@@ -30,7 +31,8 @@ class SlqPacked(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("zeros", ctypes.c_void_p)]
+                ("zeros", ctypes.c_void_p), ("meta", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _LIB = None
@@ -47,6 +49,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.slq_codes_bytes.argtypes = [_i64, _i64, _int]
         L.slq_codes_bytes.restype = _sz
+        L.slq_scales_bytes.argtypes = [_i64, _i64, ctypes.c_int32]
+        L.slq_scales_bytes.restype = _sz
+        L.slq_zeros_bytes.argtypes = [_i64, _i64, _int, ctypes.c_int32]
+        L.slq_zeros_bytes.restype = _sz
         L.slq_quantize_pack.argtypes = [_vp, _i64, _i64, _int, _int, _int, _pp, _vp]
         L.slq_dequantize.argtypes = [_pp, _vp, _vp]
         L.slq_gemm_workspace_bytes.argtypes = [_i64, _pp]
@@ -91,7 +97,9 @@ def _ptr(t):
 
 @dataclass
 class PackedWeight:
-    """A packed weight: codes uint32 [n][k*bits/32], scales fp32 [n][G], zeros uint8 [n][G]."""
+    """A packed weight: codes uint32 [n][k*bits/32]; metadata SLQ_META_F32:
+    scales fp32 [n][G], zeros uint8 [n][G]; SLQ_META_COMPACT: scales binary16
+    bits int16 [n*G], zeros nibbles (bits <= 4) uint8 [ceil(n*G/2)] or bytes."""
     bits: int
     n: int
     k: int
@@ -99,30 +107,40 @@ class PackedWeight:
     scales: torch.Tensor
     zeros: torch.Tensor
     group: int = GROUP
+    meta: int = SLQ_META_F32
 
     def c(self) -> SlqPacked:
         return SlqPacked(self.bits, self.group, self.n, self.k, _ptr(self.codes),
-                         _ptr(self.scales), _ptr(self.zeros))
+                         _ptr(self.scales), _ptr(self.zeros), self.meta, 0)
 
     @property
     def nbytes(self) -> int:
-        return self.codes.numel() * 4 + self.scales.numel() * 4 + self.zeros.numel()
+        return (self.codes.numel() * 4 + self.scales.numel() * self.scales.element_size() +
+                self.zeros.numel())
 
 
-def alloc_packed(n: int, k: int, bits: int, device, group: int = GROUP) -> PackedWeight:
+def alloc_packed(n: int, k: int, bits: int, device, group: int = GROUP,
+                 meta: int = SLQ_META_F32) -> PackedWeight:
     G = k // group
+    if meta == SLQ_META_COMPACT:
+        scales = torch.empty((n * G,), dtype=torch.int16, device=device)
+        zeros = torch.empty(((n * G + 1) // 2 if bits <= 4 else n * G,), dtype=torch.uint8,
+                            device=device)
+    else:
+        scales = torch.empty((n, G), dtype=torch.float32, device=device)
+        zeros = torch.empty((n, G), dtype=torch.uint8, device=device)
     return PackedWeight(bits, n, k,
                         torch.empty((n, k * bits // 32), dtype=torch.int32, device=device),
-                        torch.empty((n, G), dtype=torch.float32, device=device),
-                        torch.empty((n, G), dtype=torch.uint8, device=device), group)
+                        scales, zeros, group, meta)
 
 
 def slq_quantize_pack(W: torch.Tensor, bits: int, group: int = GROUP, grid: int = SLQ_ASYM,
-                      out: PackedWeight | None = None) -> PackedWeight:
-    """Quantize fp32 W[n][k] to `bits` (asymmetric by default) and pack it."""
+                      out: PackedWeight | None = None, meta: int = SLQ_META_F32) -> PackedWeight:
+    """Quantize fp32 W[n][k] to `bits` (asymmetric by default) and pack it, with
+    fp32 (SLQ_META_F32) or 20-bit (SLQ_META_COMPACT) group metadata."""
     assert W.dtype == torch.float32 and W.is_cuda and W.is_contiguous()
     n, k = W.shape
-    pw = out if out is not None else alloc_packed(n, k, bits, W.device, group)
+    pw = out if out is not None else alloc_packed(n, k, bits, W.device, group, meta)
     desc = pw.c()
     _check(lib().slq_quantize_pack(_ptr(W), n, k, bits, group, grid, ctypes.byref(desc),
                                    _stream(W)), "slq_quantize_pack")
@@ -259,4 +277,5 @@ def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
 
 __all__ = ["lib", "SlqError", "SlqPacked", "PackedWeight", "alloc_packed", "workspace",
            "gemm_workspace_bytes", "kernel_name", "slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm",
-           "slq_row_lse", "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_quant_error", "SLQ_ASYM", "SLQ_SYM", "GROUP"]
+           "slq_row_lse", "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_quant_error",
+           "SLQ_META_F32", "SLQ_META_COMPACT", "SLQ_ASYM", "SLQ_SYM", "GROUP"]

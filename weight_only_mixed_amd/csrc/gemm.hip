@@ -172,11 +172,12 @@ __device__ __forceinline__ u32x4_t dequant_slice(const Chunk<BITS> &c, const Deq
   return u32x4_t{p[0], p[1], p[2], p[3]};
 }
 
-template <int BITS>
+template <int BITS, bool CM>
 __global__ __launch_bounds__(kThreads, kMT * kNTW > 8 ? 1 : 2) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
-    const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     float *__restrict__ y) {
+  const MetaRd<BITS, CM> md{scales, zeros};
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_x[];
   uint16_t *As[2] = {lds_x, lds_x + kBM * kPitch};
 
@@ -215,14 +216,12 @@ __global__ __launch_bounds__(kThreads, kMT * kNTW > 8 ? 1 : 2) void gemm_kernel(
   // weights: column n = n0 + 32t + c32 (rows past N are read, never stored);
   // the lane's chunk of step st is chunk 2*st + h of the row
   const uint32_t *crow[kNTW];
-  const float *srow[kNTW];
-  const uint8_t *zrow[kNTW];
+  int64_t mrow[kNTW];   // flat group index of the row's first group
 #pragma unroll
   for (int t = 0; t < kNTW; ++t) {
     const int n = min(n0 + 32 * t + c32, N - 1);
     crow[t] = codes + (int64_t)n * wpr + h * BITS;
-    srow[t] = scales + (int64_t)n * G;
-    zrow[t] = zeros + (int64_t)n * G;
+    mrow[t] = (int64_t)n * G;
   }
   // chunks, scale and zero point of step st (a step is half a 128-group)
   auto load_w = [&](int st, Chunk<BITS> (&c)[kNTW], float (&sv)[kNTW], uint32_t (&zv)[kNTW]) {
@@ -230,8 +229,8 @@ __global__ __launch_bounds__(kThreads, kMT * kNTW > 8 ? 1 : 2) void gemm_kernel(
 #pragma unroll
     for (int t = 0; t < kNTW; ++t) {
       c[t] = load_chunk<BITS>(crow[t] + (int64_t)st * 2 * BITS);
-      sv[t] = srow[t][g];
-      zv[t] = zrow[t][g];
+      sv[t] = md.scale(mrow[t] + g);
+      zv[t] = md.zero(mrow[t] + g);
     }
   };
 
@@ -317,19 +316,19 @@ __global__ __launch_bounds__(kThreads, kMT * kNTW > 8 ? 1 : 2) void gemm_kernel(
   }
 }
 
-template <int BITS>
-hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const float *scales,
+template <int BITS, bool CM>
+hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
                      hipStream_t st) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS, CM>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) {
     (void)hipGetLastError();   // leave no sticky error behind for later calls
     return attr;
   }
   const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gemm_kernel<BITS>), grid, dim3(kThreads), kLdsBytes, st, x, codes, scales,
+  hipLaunchKernelGGL((gemm_kernel<BITS, CM>), grid, dim3(kThreads), kLdsBytes, st, x, codes, scales,
                      zeros, (int)m, (int)n, (int)k, y);
   return hipGetLastError();
 }
@@ -338,19 +337,24 @@ hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const float *scal
 
 size_t gemm_workspace(int64_t, int64_t, int64_t, int) { return 0; }
 
-hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const float *scales,
-                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, int bits, float *y,
-                       void *, hipStream_t s) {
+hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const void *scales,
+                       const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,
+                       int bits, float *y, void *, hipStream_t s) {
+#define SLQ_GEMM_BITS(B_)                                                        \
+  case B_:                                                                       \
+    return compact ? gemm_bits<B_, true>(x, codes, scales, zeros, m, n, k, y, s) \
+                   : gemm_bits<B_, false>(x, codes, scales, zeros, m, n, k, y, s);
   switch (bits) {
-    case 2: return gemm_bits<2>(x, codes, scales, zeros, m, n, k, y, s);
-    case 3: return gemm_bits<3>(x, codes, scales, zeros, m, n, k, y, s);
-    case 4: return gemm_bits<4>(x, codes, scales, zeros, m, n, k, y, s);
-    case 5: return gemm_bits<5>(x, codes, scales, zeros, m, n, k, y, s);
-    case 6: return gemm_bits<6>(x, codes, scales, zeros, m, n, k, y, s);
-    case 7: return gemm_bits<7>(x, codes, scales, zeros, m, n, k, y, s);
-    case 8: return gemm_bits<8>(x, codes, scales, zeros, m, n, k, y, s);
+    SLQ_GEMM_BITS(2)
+    SLQ_GEMM_BITS(3)
+    SLQ_GEMM_BITS(4)
+    SLQ_GEMM_BITS(5)
+    SLQ_GEMM_BITS(6)
+    SLQ_GEMM_BITS(7)
+    SLQ_GEMM_BITS(8)
     default: return hipErrorInvalidValue;
   }
+#undef SLQ_GEMM_BITS
 }
 
 }  // namespace slq

@@ -209,15 +209,16 @@ __device__ __forceinline__ float meta_zero(uint32_t z) {
 // 16*NT rows x [ga, gz) groups.
 constexpr int kMetaRounds = 2;
 
-template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV>
+template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV, bool CM>
 __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
-    const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
     unsigned *__restrict__ tickets) {
   // One m-tile: the zero point is folded into a per-row S' chain (see
   // zero_pair); several m-tiles share one S chain per m-tile instead.
   constexpr bool ZS = (MT == 1);
+  const MetaRd<BITS, CM> md{scales, zeros};
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -275,8 +276,7 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
         const int e = min(lane + r * kWave, munits - 1);
         const int n = min(n0 + e / q4, N - 1);
         const int64_t o = (int64_t)n * G + gbase + ga + 4 * (e % q4);
-        msv[r] = *reinterpret_cast<const float4 *>(scales + o);
-        mzv[r] = *reinterpret_cast<const uint32_t *>(zeros + o);
+        md.load4(o, msv[r], mzv[r]);
       }
     }
   } else {
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
       const int n = min(n0 + i / cnt, N - 1);
       const int gl = ga + i % cnt;
       const int64_t o = (int64_t)n * G + gbase + gl;
-      meta[gl * mrows + i / cnt] = make_float2(scales[o], meta_zero<BITS, ZS>(zeros[o]));
+      meta[gl * mrows + i / cnt] = make_float2(md.scale(o), meta_zero<BITS, ZS>(md.zero(o)));
     }
   }
 
@@ -509,12 +509,13 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
 constexpr int kRowsDepth = 4;
 constexpr int kRowsXPitch = 68;   // words per activation row and group (64 + 4 vs bank conflicts)
 
-template <int BITS, int MT>
+template <int BITS, int MT, bool CM>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
-    const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
     int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
     unsigned *__restrict__ tickets) {
+  const MetaRd<BITS, CM> md{scales, zeros};
   static_assert(kThreads == 256, "four wavefronts of 16 rows");
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & (kWave - 1);
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
   for (int i = lane; i < 16 * gcount; i += kWave) {
     const int r = i / gcount, gl = i % gcount;
     const int64_t o = (int64_t)min(nw + r, N - 1) * G + gbase + gl;
-    meta[gl * 16 + r] = make_float2(scales[o], (float)zeros[o]);
+    meta[gl * 16 + r] = make_float2(md.scale(o), (float)md.zero(o));
   }
   xstore(xbuf[0], xr0);
   __syncthreads();
@@ -731,8 +732,8 @@ constexpr int64_t kWvBlocks = SLQ_GEMV_WV_BLOCKS;
 // plus scales/zero points (<= 32 KiB), or the reduction area (<= 64 KiB).
 constexpr size_t kMaxDynLds = 128 * 1024;
 
-template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV>
-hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *scales,
+template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV, bool CM>
+hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const void *scales,
                        const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                        const GemvPlan &plan, hipStream_t st) {
   float *partial = nullptr;
@@ -744,13 +745,13 @@ hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *sc
   const size_t lds = gemv_lds_bytes(m, MT, NT, plan.gw, XD, WV);
   if (lds > kMaxDynLds) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B, MV, XD, WV>),
+      reinterpret_cast<const void *>(&gemv_kernel<BITS, MT, NT, B, MV, XD, WV, CM>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
   if (attr != hipSuccess) {
     (void)hipGetLastError();   // leave no sticky error behind for later calls
     return attr;
   }
-  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B, MV, XD, WV>), dim3(plan.nblocks, plan.ksplits),
+  hipLaunchKernelGGL((gemv_kernel<BITS, MT, NT, B, MV, XD, WV, CM>), dim3(plan.nblocks, plan.ksplits),
                      dim3(WV * kWave), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
                      plan.gw, plan.ksplits, y, partial, tickets);
   return hipGetLastError();
@@ -758,14 +759,14 @@ hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const float *sc
 
 // Groups per load batch: kBatchNt* (NT * B = 4 chunk loads per batch per
 // lane by default), two batches in flight.
-template <int BITS, int MT>
-hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const float *scales,
+template <int BITS, int MT, bool CM>
+hipError_t gemv_shape(const uint16_t *x, const uint32_t *codes, const void *scales,
                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                       const GemvPlan &plan, hipStream_t st) {
 // One m-tile may use 8 waves per workgroup, or 16 with LDS-staged activations
 // (more waves on the same rows for occupancy); several m-tiles use 4.
 #define SLQ_GEMV_LAUNCH_WV(NT_, B_, MV_, XD_, WV_) \
-  gemv_launch<BITS, MT, NT_, B_, MV_, XD_, WV_>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
+  gemv_launch<BITS, MT, NT_, B_, MV_, XD_, WV_, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
 #define SLQ_GEMV_LAUNCH(NT_, B_, MV_, XD_)                                                  \
   (MT == 1 && !XD_ && plan.wv == 16                                                         \
        ? SLQ_GEMV_LAUNCH_WV(NT_, B_, MV_, XD_, (MT == 1 && !XD_ ? 16 : 4))                 \
@@ -801,8 +802,8 @@ size_t gemv_rows_lds_bytes(int64_t m, int gw) {
   return (size_t)2 * m * kRowsXPitch * 4 + (size_t)kWaves * gw * 16 * 8 + 16;
 }
 
-template <int BITS, int MT>
-hipError_t gemv_rows_launch(const uint16_t *x, const uint32_t *codes, const float *scales,
+template <int BITS, int MT, bool CM>
+hipError_t gemv_rows_launch(const uint16_t *x, const uint32_t *codes, const void *scales,
                             const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
                             void *ws, const GemvPlan &plan, hipStream_t st) {
   float *partial = nullptr;
@@ -814,36 +815,36 @@ hipError_t gemv_rows_launch(const uint16_t *x, const uint32_t *codes, const floa
   const size_t lds = gemv_rows_lds_bytes(m, plan.gw);
   if (lds > kMaxDynLds) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&gemv_rows_kernel<BITS, MT>),
+      reinterpret_cast<const void *>(&gemv_rows_kernel<BITS, MT, CM>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
   if (attr != hipSuccess) {
     (void)hipGetLastError();
     return attr;
   }
-  hipLaunchKernelGGL((gemv_rows_kernel<BITS, MT>), dim3(plan.nblocks, plan.ksplits),
+  hipLaunchKernelGGL((gemv_rows_kernel<BITS, MT, CM>), dim3(plan.nblocks, plan.ksplits),
                      dim3(kThreads), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
                      plan.gw, plan.ksplits, y, partial, tickets);
   return hipGetLastError();
 }
 
-template <int BITS>
-hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const float *scales,
+template <int BITS, bool CM>
+hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      const GemvPlan &plan, hipStream_t st) {
   if (plan.rows) {
     switch (plan.mt) {
-      case 1: return gemv_rows_launch<BITS, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-      case 2: return gemv_rows_launch<BITS, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-      case 3: return gemv_rows_launch<BITS, 3>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-      case 4: return gemv_rows_launch<BITS, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      case 1: return gemv_rows_launch<BITS, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      case 2: return gemv_rows_launch<BITS, 2, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      case 3: return gemv_rows_launch<BITS, 3, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      case 4: return gemv_rows_launch<BITS, 4, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
       default: return hipErrorInvalidValue;
     }
   }
   switch (plan.mt) {
-    case 1: return gemv_shape<BITS, 1>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 2: return gemv_shape<BITS, 2>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 3: return gemv_shape<BITS, 3>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
-    case 4: return gemv_shape<BITS, 4>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 1: return gemv_shape<BITS, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 2: return gemv_shape<BITS, 2, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 3: return gemv_shape<BITS, 3, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    case 4: return gemv_shape<BITS, 4, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -951,19 +952,24 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   return p;
 }
 
-hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const float *scales,
-                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, int bits, float *y,
-                       void *ws, const GemvPlan &plan, hipStream_t s) {
+hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const void *scales,
+                       const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,
+                       int bits, float *y, void *ws, const GemvPlan &plan, hipStream_t s) {
+#define SLQ_GEMV_BITS(B_)                                                                   \
+  case B_:                                                                                  \
+    return compact ? gemv_bits<B_, true>(x, codes, scales, zeros, m, n, k, y, ws, plan, s) \
+                   : gemv_bits<B_, false>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
   switch (bits) {
-    case 2: return gemv_bits<2>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
-    case 3: return gemv_bits<3>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
-    case 4: return gemv_bits<4>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
-    case 5: return gemv_bits<5>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
-    case 6: return gemv_bits<6>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
-    case 7: return gemv_bits<7>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
-    case 8: return gemv_bits<8>(x, codes, scales, zeros, m, n, k, y, ws, plan, s);
+    SLQ_GEMV_BITS(2)
+    SLQ_GEMV_BITS(3)
+    SLQ_GEMV_BITS(4)
+    SLQ_GEMV_BITS(5)
+    SLQ_GEMV_BITS(6)
+    SLQ_GEMV_BITS(7)
+    SLQ_GEMV_BITS(8)
     default: return hipErrorInvalidValue;
   }
+#undef SLQ_GEMV_BITS
 }
 
 }  // namespace slq

@@ -7,14 +7,18 @@
 namespace slq {
 
 // quantize.hip
+// `compact`: binary16 scales and nibble (b <= 4) or byte zero points; else
+// fp32 scales and byte zero points.
 hipError_t launch_quantize_pack(const float *W, int64_t n, int64_t k, int bits, bool symmetric,
-                                uint32_t *codes, float *scales, uint8_t *zeros, hipStream_t s);
-hipError_t launch_dequantize(const uint32_t *codes, const float *scales, const uint8_t *zeros,
-                             int64_t n, int64_t k, int bits, float *out, hipStream_t s);
+                                bool compact, uint32_t *codes, void *scales, uint8_t *zeros,
+                                hipStream_t s);
+hipError_t launch_dequantize(const uint32_t *codes, const void *scales, const uint8_t *zeros,
+                             bool compact, int64_t n, int64_t k, int bits, float *out,
+                             hipStream_t s);
 size_t quant_error_workspace(int64_t n, int64_t k);
-hipError_t launch_quant_error(const float *W, const uint32_t *codes, const float *scales,
-                              const uint8_t *zeros, int64_t n, int64_t k, int bits, double *out,
-                              void *ws, hipStream_t s);
+hipError_t launch_quant_error(const float *W, const uint32_t *codes, const void *scales,
+                              const uint8_t *zeros, bool compact, int64_t n, int64_t k, int bits,
+                              double *out, void *ws, hipStream_t s);
 
 // gemv.hip (decode, m <= 64)
 struct GemvPlan {
@@ -31,15 +35,15 @@ struct GemvPlan {
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);
-hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const float *scales,
-                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, int bits, float *y,
-                       void *ws, const GemvPlan &plan, hipStream_t s);
+hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const void *scales,
+                       const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,
+                       int bits, float *y, void *ws, const GemvPlan &plan, hipStream_t s);
 
 // gemm.hip (prefill, m > 64)
 size_t gemm_workspace(int64_t m, int64_t n, int64_t k, int bits);
-hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const float *scales,
-                       const uint8_t *zeros, int64_t m, int64_t n, int64_t k, int bits, float *y,
-                       void *ws, hipStream_t s);
+hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const void *scales,
+                       const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,
+                       int bits, float *y, void *ws, hipStream_t s);
 
 // fidelity.hip
 size_t fidelity_workspace(int64_t rows, int64_t vocab);

@@ -59,10 +59,12 @@ __device__ __forceinline__ void load_words(const uint32_t *__restrict__ p, uint3
   for (int i = 0; i < BITS; ++i) w[i] = p[i];
 }
 
-template <int BITS, bool SYM>
+// CM: compact metadata (see MetaRd): the fp32 scale is rounded up to binary16
+// and the zero point and codes are computed with the rounded scale.
+template <int BITS, bool SYM, bool CM>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const float *__restrict__ W, int64_t chunks, uint32_t *__restrict__ codes,
-    float *__restrict__ scales, uint8_t *__restrict__ zeros) {
+    void *__restrict__ scales, uint8_t *__restrict__ zeros) {
   constexpr int maxq_i = (1 << BITS) - 1;
   const float maxq = (float)maxq_i;
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
       s = 1.0f;
       zf = 0.0f;
     } else {
+      if constexpr (CM) s = f16_bits_to_f32(f16_bits_round_up(s));
       zf = clamp_code(rintf((-lo) / s), maxq);
     }
   } else {
@@ -118,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
     const float two_m = 2.0f * m;
     s = two_m / maxq;
     if (s == 0.0f) s = 1.0f;
+    if constexpr (CM) s = f16_bits_to_f32(f16_bits_round_up(s));
     zf = (float)(1 << (BITS - 1));
   }
 
@@ -130,28 +134,46 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(
   uint32_t packed[BITS];
   pack32<BITS>(q, packed);
 
+  // nibble zero points: the first lane of an even group also takes the odd
+  // group's zero point (4 lanes on; 0 past the last group)
+  uint32_t zodd = 0;
+  if constexpr (CM && BITS <= 4) {
+    zodd = (uint32_t)(int)__shfl_down(zf, 4, kWave);
+    if (c + 4 >= chunks) zodd = 0;
+  }
   if (c < chunks) {
     uint32_t *dst = codes + c * BITS;
 #pragma unroll
     for (int i = 0; i < BITS; ++i) dst[i] = packed[i];
     if ((c & 3) == 0) {
-      scales[c >> 2] = s;
-      zeros[c >> 2] = (uint8_t)(int)zf;
+      if constexpr (CM) {
+        // s is already a binary16 value: rounding it up returns its own bits
+        static_cast<uint16_t *>(scales)[c >> 2] = (uint16_t)f16_bits_round_up(s);
+        if constexpr (BITS <= 4) {
+          if ((c & 7) == 0) zeros[c >> 3] = (uint8_t)((uint32_t)(int)zf | (zodd << 4));
+        } else {
+          zeros[c >> 2] = (uint8_t)(int)zf;
+        }
+      } else {
+        static_cast<float *>(scales)[c >> 2] = s;
+        zeros[c >> 2] = (uint8_t)(int)zf;
+      }
     }
   }
 }
 
-template <int BITS>
+template <int BITS, bool CM>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
-    const uint32_t *__restrict__ codes, const float *__restrict__ scales,
+    const uint32_t *__restrict__ codes, const void *__restrict__ scales,
     const uint8_t *__restrict__ zeros, int64_t chunks, float *__restrict__ out) {
+  const MetaRd<BITS, CM> meta{scales, zeros};
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (c >= chunks) return;
   uint32_t words[BITS], q[32];
   load_words<BITS>(codes + c * BITS, words);
   unpack32<BITS>(words, q);
-  const float s = scales[c >> 2];
-  const int z = zeros[c >> 2];
+  const float s = meta.scale(c >> 2);
+  const int z = (int)meta.zero(c >> 2);
   float4 *dst = reinterpret_cast<float4 *>(out + c * 32);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -178,20 +200,21 @@ __device__ __forceinline__ double block_sum_f64(double v, double *lds) {
 }
 
 // Per block: sum (w - w_hat)^2 over its chunks and sum s^2 over its groups.
-template <int BITS>
+template <int BITS, bool CM>
 __global__ __launch_bounds__(kThreads) void quant_error_kernel(
     const float *__restrict__ W, const uint32_t *__restrict__ codes,
-    const float *__restrict__ scales, const uint8_t *__restrict__ zeros, int64_t chunks,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int64_t chunks,
     double *__restrict__ partial) {
   __shared__ double lds[kThreads / kWave];
+  const MetaRd<BITS, CM> meta{scales, zeros};
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   double sse = 0.0, s2 = 0.0;
   if (c < chunks) {
     uint32_t words[BITS], q[32];
     load_words<BITS>(codes + c * BITS, words);
     unpack32<BITS>(words, q);
-    const float s = scales[c >> 2];
-    const int z = zeros[c >> 2];
+    const float s = meta.scale(c >> 2);
+    const int z = (int)meta.zero(c >> 2);
     const float4 *src = reinterpret_cast<const float4 *>(W + c * 32);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -233,35 +256,48 @@ __global__ __launch_bounds__(kThreads) void sum_pairs_kernel(const double *__res
 }
 
 template <int BITS>
-hipError_t quantize_bits(const float *W, int64_t chunks, bool sym, uint32_t *codes, float *scales,
-                         uint8_t *zeros, hipStream_t st) {
+hipError_t quantize_bits(const float *W, int64_t chunks, bool sym, bool cm, uint32_t *codes,
+                         void *scales, uint8_t *zeros, hipStream_t st) {
   const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads));
-  if (sym)
-    hipLaunchKernelGGL((quantize_pack_kernel<BITS, true>), grid, dim3(kThreads), 0, st, W,
-                       chunks, codes, scales, zeros);
+#define SLQ_Q(SYM_, CM_)                                                                       \
+  hipLaunchKernelGGL((quantize_pack_kernel<BITS, SYM_, CM_>), grid, dim3(kThreads), 0, st, W, \
+                     chunks, codes, scales, zeros)
+  if (sym) {
+    if (cm) SLQ_Q(true, true);
+    else SLQ_Q(true, false);
+  } else {
+    if (cm) SLQ_Q(false, true);
+    else SLQ_Q(false, false);
+  }
+#undef SLQ_Q
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t dequantize_bits(const uint32_t *codes, const void *scales, const uint8_t *zeros,
+                           bool cm, int64_t chunks, float *out, hipStream_t st) {
+  const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads));
+  if (cm)
+    hipLaunchKernelGGL((dequantize_kernel<BITS, true>), grid, dim3(kThreads), 0, st, codes,
+                       scales, zeros, chunks, out);
   else
-    hipLaunchKernelGGL((quantize_pack_kernel<BITS, false>), grid, dim3(kThreads), 0, st, W,
-                       chunks, codes, scales, zeros);
+    hipLaunchKernelGGL((dequantize_kernel<BITS, false>), grid, dim3(kThreads), 0, st, codes,
+                       scales, zeros, chunks, out);
   return hipGetLastError();
 }
 
 template <int BITS>
-hipError_t dequantize_bits(const uint32_t *codes, const float *scales, const uint8_t *zeros,
-                           int64_t chunks, float *out, hipStream_t st) {
-  const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL((dequantize_kernel<BITS>), grid, dim3(kThreads), 0, st, codes, scales, zeros,
-                     chunks, out);
-  return hipGetLastError();
-}
-
-template <int BITS>
-hipError_t quant_error_bits(const float *W, const uint32_t *codes, const float *scales,
-                            const uint8_t *zeros, int64_t chunks, double *out, double *partial,
-                            hipStream_t st) {
+hipError_t quant_error_bits(const float *W, const uint32_t *codes, const void *scales,
+                            const uint8_t *zeros, bool cm, int64_t chunks, double *out,
+                            double *partial, hipStream_t st) {
   const int64_t nblocks = (chunks + kThreads - 1) / kThreads;
   if (nblocks > 0) {
-    hipLaunchKernelGGL((quant_error_kernel<BITS>), dim3((unsigned)nblocks), dim3(kThreads), 0, st,
-                       W, codes, scales, zeros, chunks, partial);
+    if (cm)
+      hipLaunchKernelGGL((quant_error_kernel<BITS, true>), dim3((unsigned)nblocks), dim3(kThreads),
+                         0, st, W, codes, scales, zeros, chunks, partial);
+    else
+      hipLaunchKernelGGL((quant_error_kernel<BITS, false>), dim3((unsigned)nblocks),
+                         dim3(kThreads), 0, st, W, codes, scales, zeros, chunks, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -284,17 +320,19 @@ hipError_t quant_error_bits(const float *W, const uint32_t *codes, const float *
   }
 
 hipError_t launch_quantize_pack(const float *W, int64_t n, int64_t k, int bits, bool symmetric,
-                                uint32_t *codes, float *scales, uint8_t *zeros, hipStream_t s) {
+                                bool compact, uint32_t *codes, void *scales, uint8_t *zeros,
+                                hipStream_t s) {
   const int64_t chunks = n * (k / 32);
   if (chunks == 0) return hipSuccess;
-  SLQ_DISPATCH_BITS(bits, quantize_bits, W, chunks, symmetric, codes, scales, zeros, s);
+  SLQ_DISPATCH_BITS(bits, quantize_bits, W, chunks, symmetric, compact, codes, scales, zeros, s);
 }
 
-hipError_t launch_dequantize(const uint32_t *codes, const float *scales, const uint8_t *zeros,
-                             int64_t n, int64_t k, int bits, float *out, hipStream_t s) {
+hipError_t launch_dequantize(const uint32_t *codes, const void *scales, const uint8_t *zeros,
+                             bool compact, int64_t n, int64_t k, int bits, float *out,
+                             hipStream_t s) {
   const int64_t chunks = n * (k / 32);
   if (chunks == 0) return hipSuccess;
-  SLQ_DISPATCH_BITS(bits, dequantize_bits, codes, scales, zeros, chunks, out, s);
+  SLQ_DISPATCH_BITS(bits, dequantize_bits, codes, scales, zeros, compact, chunks, out, s);
 }
 
 size_t quant_error_workspace(int64_t n, int64_t k) {
@@ -302,11 +340,11 @@ size_t quant_error_workspace(int64_t n, int64_t k) {
   return (size_t)((chunks + kThreads - 1) / kThreads) * 2 * sizeof(double);
 }
 
-hipError_t launch_quant_error(const float *W, const uint32_t *codes, const float *scales,
-                              const uint8_t *zeros, int64_t n, int64_t k, int bits, double *out,
-                              void *ws, hipStream_t s) {
+hipError_t launch_quant_error(const float *W, const uint32_t *codes, const void *scales,
+                              const uint8_t *zeros, bool compact, int64_t n, int64_t k, int bits,
+                              double *out, void *ws, hipStream_t s) {
   const int64_t chunks = n * (k / 32);
-  SLQ_DISPATCH_BITS(bits, quant_error_bits, W, codes, scales, zeros, chunks, out,
+  SLQ_DISPATCH_BITS(bits, quant_error_bits, W, codes, scales, zeros, compact, chunks, out,
                     static_cast<double *>(ws), s);
 }
 

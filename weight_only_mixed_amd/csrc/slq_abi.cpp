@@ -33,13 +33,16 @@ struct PackedSizes {
   size_t codes, scales, zeros;
 };
 
-PackedSizes sizes_of(int64_t n, int64_t k, int bits, int group) {
+PackedSizes sizes_of(int64_t n, int64_t k, int bits, int group, int32_t meta) {
   PackedSizes s;
+  const size_t groups = (size_t)(n * (k / group));
   s.codes = (size_t)(n * k / 8 * bits);
-  s.scales = (size_t)(n * (k / group)) * sizeof(float);
-  s.zeros = (size_t)(n * (k / group));
+  s.scales = groups * (meta == SLQ_META_COMPACT ? 2 : 4);
+  s.zeros = meta == SLQ_META_COMPACT && bits <= 4 ? (groups + 1) / 2 : groups;
   return s;
 }
+
+bool meta_ok(int32_t meta) { return meta == SLQ_META_F32 || meta == SLQ_META_COMPACT; }
 
 // Shape, bit-width, group, pointers and alignment of a packed weight.
 slq_status check_packed(const slq_packed *w, PackedSizes *sz) {
@@ -47,11 +50,12 @@ slq_status check_packed(const slq_packed *w, PackedSizes *sz) {
   if (w->bits < 2 || w->bits > 8) return SLQ_EINVAL;
   if (w->group <= 0) return SLQ_EINVAL;
   if (w->group != kGroupSize) return SLQ_ENOTSUP;
-  if (!dims_ok(w->n, w->k) || w->k % w->group != 0) return SLQ_EINVAL;
-  *sz = sizes_of(w->n, w->k, w->bits, w->group);
+  if (!dims_ok(w->n, w->k) || w->k % w->group != 0 || !meta_ok(w->meta)) return SLQ_EINVAL;
+  *sz = sizes_of(w->n, w->k, w->bits, w->group, w->meta);
   if (w->n * w->k > 0) {
     if (!w->codes || !w->scales || !w->zeros) return SLQ_EINVAL;
-    if (!aligned(w->codes, 16) || !aligned(w->scales, 4)) return SLQ_EINVAL;
+    if (!aligned(w->codes, 16) || !aligned(w->scales, 16) || !aligned(w->zeros, 4))
+      return SLQ_EINVAL;
     if (overlap(w->codes, sz->codes, w->scales, sz->scales) ||
         overlap(w->codes, sz->codes, w->zeros, sz->zeros) ||
         overlap(w->scales, sz->scales, w->zeros, sz->zeros))
@@ -69,6 +73,16 @@ size_t slq_codes_bytes(int64_t n, int64_t k, int bits) {
   return (size_t)(n * k / 8 * bits);
 }
 
+size_t slq_scales_bytes(int64_t n, int64_t k, int32_t meta) {
+  if (!dims_ok(n, k) || k % kGroupSize != 0 || !meta_ok(meta)) return 0;
+  return sizes_of(n, k, 8, kGroupSize, meta).scales;
+}
+
+size_t slq_zeros_bytes(int64_t n, int64_t k, int bits, int32_t meta) {
+  if (bits < 2 || bits > 8 || !dims_ok(n, k) || k % kGroupSize != 0 || !meta_ok(meta)) return 0;
+  return sizes_of(n, k, bits, kGroupSize, meta).zeros;
+}
+
 slq_status slq_quantize_pack(const float *W, int64_t n, int64_t k, int bits, int group,
                              slq_grid grid, slq_packed *out, slq_stream stream) {
   if (!out) return SLQ_EINVAL;
@@ -77,10 +91,13 @@ slq_status slq_quantize_pack(const float *W, int64_t n, int64_t k, int bits, int
   if (group != kGroupSize) return SLQ_ENOTSUP;
   if (grid != SLQ_ASYM && grid != SLQ_SYM) return SLQ_EINVAL;
   if (!dims_ok(n, k) || k % group != 0) return SLQ_EINVAL;
-  const PackedSizes sz = sizes_of(n, k, bits, group);
+  if (!meta_ok(out->meta)) return SLQ_EINVAL;
+  const PackedSizes sz = sizes_of(n, k, bits, group, out->meta);
   if (n * k > 0) {
     if (!W || !out->codes || !out->scales || !out->zeros) return SLQ_EINVAL;
-    if (!aligned(W, 16) || !aligned(out->codes, 16) || !aligned(out->scales, 4)) return SLQ_EINVAL;
+    if (!aligned(W, 16) || !aligned(out->codes, 16) || !aligned(out->scales, 16) ||
+        !aligned(out->zeros, 4))
+      return SLQ_EINVAL;
     const size_t wb = (size_t)(n * k) * sizeof(float);
     if (overlap(W, wb, out->codes, sz.codes) || overlap(W, wb, out->scales, sz.scales) ||
         overlap(W, wb, out->zeros, sz.zeros) || overlap(out->codes, sz.codes, out->scales, sz.scales) ||
@@ -93,7 +110,8 @@ slq_status slq_quantize_pack(const float *W, int64_t n, int64_t k, int bits, int
   out->n = n;
   out->k = k;
   if (n * k == 0) return SLQ_OK;
-  return from_hip(slq::launch_quantize_pack(W, n, k, bits, grid == SLQ_SYM, out->codes,
+  return from_hip(slq::launch_quantize_pack(W, n, k, bits, grid == SLQ_SYM,
+                                            out->meta == SLQ_META_COMPACT, out->codes,
                                             out->scales, out->zeros,
                                             static_cast<hipStream_t>(stream)));
 }
@@ -108,8 +126,9 @@ slq_status slq_dequantize(const slq_packed *w, float *W_deq, slq_stream stream) 
   if (overlap(W_deq, ob, w->codes, sz.codes) || overlap(W_deq, ob, w->scales, sz.scales) ||
       overlap(W_deq, ob, w->zeros, sz.zeros))
     return SLQ_EINVAL;
-  return from_hip(slq::launch_dequantize(w->codes, w->scales, w->zeros, w->n, w->k, w->bits,
-                                         W_deq, static_cast<hipStream_t>(stream)));
+  return from_hip(slq::launch_dequantize(w->codes, w->scales, w->zeros,
+                                         w->meta == SLQ_META_COMPACT, w->n, w->k, w->bits, W_deq,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w) {
@@ -142,27 +161,31 @@ slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t
   if (m <= 64) {
     const slq::GemvPlan plan = slq::gemv_plan(m, w->n, w->k, w->bits);
     if (plan.ksplits == 0) return SLQ_ENOTSUP;
-    return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros, m, w->n, w->k,
-                                     w->bits, y, workspace, plan, s));
+    return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros,
+                                     w->meta == SLQ_META_COMPACT, m, w->n, w->k, w->bits, y,
+                                     workspace, plan, s));
   }
-  return from_hip(slq::launch_gemm(x_bf16, w->codes, w->scales, w->zeros, m, w->n, w->k, w->bits,
-                                   y, workspace, s));
+  return from_hip(slq::launch_gemm(x_bf16, w->codes, w->scales, w->zeros,
+                                   w->meta == SLQ_META_COMPACT, m, w->n, w->k, w->bits, y,
+                                   workspace, s));
 }
 
 const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
-  static thread_local char buf[64];
+  static thread_local char buf[96];
   PackedSizes sz;
   buf[0] = '\0';
   if (m <= 0 || m >= kMaxDim || check_packed(w, &sz) != SLQ_OK) return buf;
   if (m <= 64) {
     const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
+    const char *cm = w->meta == SLQ_META_COMPACT ? "true" : "false";
     if (p.rows)
-      snprintf(buf, sizeof buf, "slq::gemv_rows_kernel<%d, %d>", w->bits, p.mt);
+      snprintf(buf, sizeof buf, "slq::gemv_rows_kernel<%d, %d, %s>", w->bits, p.mt, cm);
     else
-      snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s, %d>", w->bits, p.mt,
-               p.nt, p.b, p.mv ? "true" : "false", p.xd ? "true" : "false", p.wv);
+      snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s, %d, %s>", w->bits, p.mt,
+               p.nt, p.b, p.mv ? "true" : "false", p.xd ? "true" : "false", p.wv, cm);
   } else {
-    snprintf(buf, sizeof buf, "slq::gemm_kernel<%d>", w->bits);
+    snprintf(buf, sizeof buf, "slq::gemm_kernel<%d, %s>", w->bits,
+             w->meta == SLQ_META_COMPACT ? "true" : "false");
   }
   return buf;
 }
@@ -299,8 +322,9 @@ slq_status slq_quant_error(const float *W, const slq_packed *w, double *out, voi
       overlap(workspace, wsb, w->codes, sz.codes) || overlap(workspace, wsb, w->scales, sz.scales) ||
       overlap(workspace, wsb, w->zeros, sz.zeros))
     return SLQ_EINVAL;
-  return from_hip(slq::launch_quant_error(W, w->codes, w->scales, w->zeros, w->n, w->k, w->bits,
-                                          out, workspace, static_cast<hipStream_t>(stream)));
+  return from_hip(slq::launch_quant_error(W, w->codes, w->scales, w->zeros,
+                                          w->meta == SLQ_META_COMPACT, w->n, w->k, w->bits, out,
+                                          workspace, static_cast<hipStream_t>(stream)));
 }
 
 const char *slq_strerror(slq_status s) {

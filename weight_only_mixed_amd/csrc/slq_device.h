@@ -48,6 +48,56 @@ __device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
   return v;
 }
 
+// IEEE binary16 bits -> fp32 (exact).
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// The smallest binary16 value >= s (s > 0, finite), as bits: a scale rounded up
+// keeps the half-step error bound of the grid it spans.  Values above the
+// binary16 range saturate at 65504.
+__device__ __forceinline__ uint32_t f16_bits_round_up(float s) {
+  uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)s);   // nearest, ties to even
+  if (f16_bits_to_f32(b) < s) b += 1u;                       // next value up
+  return b >= 0x7C00u ? 0x7BFFu : b;
+}
+
+// Group metadata, in one of two layouts (flat group index i = row * G + g):
+//  CM = false: fp32 scales[i], zero points as bytes zeros[i];
+//  CM = true (20 bits per group for b <= 4): binary16 scales[i] rounded up from
+//    the fp32 scale; zero points as 4-bit nibbles (b <= 4: nibble i of the byte
+//    stream, low nibble first) or bytes (b >= 5).
+template <int BITS, bool CM>
+struct MetaRd {
+  const void *s;
+  const uint8_t *z;
+  __device__ __forceinline__ float scale(int64_t i) const {
+    if constexpr (CM) return f16_bits_to_f32(static_cast<const uint16_t *>(s)[i]);
+    else return static_cast<const float *>(s)[i];
+  }
+  __device__ __forceinline__ uint32_t zero(int64_t i) const {
+    if constexpr (CM && BITS <= 4) return (uint32_t)(z[i >> 1] >> ((i & 1) * 4)) & 15u;
+    else return z[i];
+  }
+  // groups i..i+3 (i % 4 == 0): scales, and zero points as the bytes of one word
+  __device__ __forceinline__ void load4(int64_t i, float4 &sv, uint32_t &zv) const {
+    if constexpr (CM) {
+      const u32x2_t h = *reinterpret_cast<const u32x2_t *>(static_cast<const uint16_t *>(s) + i);
+      sv = make_float4(f16_bits_to_f32(h[0] & 0xFFFFu), f16_bits_to_f32(h[0] >> 16),
+                       f16_bits_to_f32(h[1] & 0xFFFFu), f16_bits_to_f32(h[1] >> 16));
+      if constexpr (BITS <= 4) {
+        const uint32_t v = *reinterpret_cast<const uint16_t *>(z + (i >> 1));
+        zv = (v & 0xFu) | ((v & 0xF0u) << 4) | ((v & 0xF00u) << 8) | ((v & 0xF000u) << 12);
+      } else {
+        zv = *reinterpret_cast<const uint32_t *>(z + i);
+      }
+    } else {
+      sv = *reinterpret_cast<const float4 *>(static_cast<const float *>(s) + i);
+      zv = *reinterpret_cast<const uint32_t *>(z + i);
+    }
+  }
+};
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
