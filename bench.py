@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default="all", help="extra rows: all, none, or a comma list of "
-                    "quantize,gemm,stack,fidelity,allocation,gamma")
+                    "quantize,gemm,stack,fidelity,allocation,gamma,compact")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--pmc", default=None, metavar="KERNEL",
@@ -128,7 +128,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     torch.manual_seed(0)
-    rows_sel = {"quantize", "gemm", "stack", "fidelity", "allocation", "gamma"} if args.rows == "all" else (
+    rows_sel = {"quantize", "gemm", "stack", "fidelity", "allocation", "gamma", "compact"} if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
 
     def to_dev(a):
@@ -215,6 +215,33 @@ def main():
     value = sweep_bytes / (step_ms * 1e-3) / 1e9
     log(f"bench: sweep step {step_ms * 1e3:.1f} us, {value:.1f} GB/s packed weights")
 
+    # the same sweep with compact metadata (binary16 scale + 4/8-bit zero point)
+    compact_row = None
+    if "compact" in rows_sel:
+        cpacks = [[slq.slq_quantize_pack(W_dev[name], bits, meta=slq.SLQ_META_COMPACT)
+                   for (name, n, k, bits, m) in points] for _ in range(R)]
+        cgraphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for pi, (name, n, k, bits, m) in enumerate(points):
+                    slq.slq_dequant_gemm(xs[(m, k)], cpacks[r][pi], y=ys[pi], ws=ws)
+            cgraphs.append(g)
+        for i in range(args.warmup):
+            cgraphs[i % R].replay()
+        torch.cuda.synchronize()
+        with Timer(torch) as T:
+            for i in range(args.steps):
+                cgraphs[i % R].replay()
+        c_ms = T.ms / max(1, args.steps)
+        c_bytes = sum(p.nbytes for p in cpacks[0])
+        compact_row = {"ms_per_step": round(c_ms, 4), "packed_MB_per_step": round(c_bytes / 1e6, 1),
+                       "GBps_packed_step": round(c_bytes / (c_ms * 1e-3) / 1e9, 1),
+                       "step_time_vs_fp32_metadata": round(c_ms / step_ms, 4)}
+        log(f"bench: compact-metadata sweep step {c_ms * 1e3:.1f} us ({c_bytes / 1e6:.0f} MB)")
+        del cgraphs, cpacks
+        torch.cuda.empty_cache()
+
     # per-point event pairs (include ~2-4 us of dispatch latency per launch)
     per_point_ms = [[] for _ in points]
     for rep in range(3):
@@ -278,6 +305,8 @@ def main():
         "GBps_packed_step": round(value, 1),
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "points": point_rows}}
+    if compact_row is not None:
+        rows["decode_sweep_compact_metadata"] = compact_row
 
     # free sweep copies beyond slot 0 before the other rows
     del graphs
