@@ -162,6 +162,19 @@ def allocation_table(layers: int = 32, shapes=None, bits=tuple(range(2, 9)),
     return np.array(sizes, np.int64), np.array(costs, np.float64), tau, names
 
 
+def gptq_hessian(k: int, seed: int, tokens: int | None = None, rank: int = 8) -> np.ndarray:
+    """Synthetic layer Hessian H = 2 X X^T / T (float32 [k][k]) from T seeded
+    activation vectors with correlated channels: a rank-`rank` shared
+    component plus independent noise, and lognormal per-channel scales (a few
+    strong channels, as in transformer activations)."""
+    g = rng(seed)
+    T = tokens if tokens is not None else 2 * k
+    scale = np.exp(0.5 * g.standard_normal(k))
+    B = g.standard_normal((k, rank)) / np.sqrt(rank)
+    X = (B @ g.standard_normal((rank, T)) + 0.5 * g.standard_normal((k, T))) * scale[:, None]
+    return (2.0 * (X @ X.T) / T).astype(np.float32)
+
+
 def uniform_group_weights(n_groups: int, lo: float, hi: float, seed: int,
                           group: int = 128) -> np.ndarray:
     """Rows of uniform[lo, hi] samples with both endpoints pinned in every group.
