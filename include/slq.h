@@ -219,6 +219,33 @@ slq_status slq_ear_kl_topk(const float *logits_p, const float *logits_q, int64_t
                            int64_t vocab, int64_t K, double temperature, float *ear_rows,
                            float *kl_rows, double *means, void *workspace, slq_stream stream);
 
+/* Workspace bytes slq_gptq_quantize needs for W[n][k]. */
+size_t slq_gptq_workspace_bytes(int64_t n, int64_t k);
+
+/*
+ * GPTQ code selection (named by the README, Pipeline, as the code-choice step:
+ * layer-wise GPTQ at every bit-width, asymmetric INT, group size 128; steps of
+ * the published algorithm, Frantar et al., ICLR 2023, Algorithm 1 with the
+ * Cholesky form of the inverse Hessian):
+ *   dead inputs (H_ii = 0) get H_ii = 1 and a zeroed weight column;
+ *   H += damp * mean(diag H) * I;  U upper with U^T U = H^-1 (fp64);
+ *   for each column i: at a group's first column its scale and zero point come
+ *   from the group's current weights (the slq_quantize_pack steps), the column
+ *   is quantized, and the later columns move by -err_i * U[i][j] with
+ *   err_i = (w_i - w_hat_i) / U[i][i]  (weights updated in fp32).
+ * In : W fp32 [n][k], H fp32 [k][k] symmetric positive semi-definite (the
+ *      layer Hessian 2 X X^T; device, 16-byte aligned), 1 <= n, 128 <= k <=
+ *      32768, k % 128 == 0, bits 2..8, group 128, damp > 0 and finite.
+ * Out: out as for slq_quantize_pack with out->meta = SLQ_META_F32 (the
+ *      compact layout: SLQ_ENOTSUP); u_out fp64 [k][k] or NULL: U.
+ * workspace: slq_gptq_workspace_bytes(n, k) bytes, 256-byte aligned.
+ * If H + damping is not positive definite the factor holds NaN and so do the
+ * scales; nothing else is reported.
+ */
+slq_status slq_gptq_quantize(const float *W, const float *H, int64_t n, int64_t k, int bits,
+                             int group, double damp, slq_packed *out, double *u_out,
+                             void *workspace, slq_stream stream);
+
 /* Workspace bytes slq_mckp_search needs for L items and budgets 0..W. */
 size_t slq_mckp_workspace_bytes(int64_t L, int64_t W);
 

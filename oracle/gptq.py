@@ -86,4 +86,4 @@ def proxy_loss(W, w_hat, H):
     """tr((W - W_hat) H (W - W_hat)^T): the layer-output error the algorithm
     minimizes greedily (H = 2 X X^T)."""
     D = np.asarray(W, np.float64) - np.asarray(w_hat, np.float64)
-    return float(np.einsum("ij,jk,ik->", D, np.asarray(H, np.float64), D))
+    return float(((D @ np.asarray(H, np.float64)) * D).sum())

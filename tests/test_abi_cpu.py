@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for name in names:
         assert hasattr(L, name), name
 
@@ -120,6 +120,18 @@ def test_fidelity_and_error_validation():
     assert T(A + 4, B, 4, 100, 10, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL  # misaligned
     assert T(A, B, 4, 0, 1, 1.0, C, C + 64, D, E, None) == slq.SLQ_EINVAL        # empty vocab
     assert T(A, B, 0, 10, 5, 1.0, None, None, None, None, None) == slq.SLQ_OK
+    Q = L.slq_gptq_quantize
+    assert Q(A, B, 64, 200, 4, 128, 0.01, ctypes.byref(packed()), None, E, None) == slq.SLQ_EINVAL
+    assert Q(A, B, 64, 256, 9, 128, 0.01, ctypes.byref(packed()), None, E, None) == slq.SLQ_EINVAL
+    assert Q(A, B, 64, 256, 4, 64, 0.01, ctypes.byref(packed()), None, E, None) == slq.SLQ_ENOTSUP
+    assert Q(A, B, 64, 256, 4, 128, 0.0, ctypes.byref(packed()), None, E, None) == slq.SLQ_EINVAL
+    assert Q(A, B, 64, 256, 4, 128, 0.01, ctypes.byref(packed()), None, None, None) == slq.SLQ_EINVAL
+    cp = packed()
+    cp.meta = 1
+    assert Q(A, B, 64, 256, 4, 128, 0.01, ctypes.byref(cp), None, E, None) == slq.SLQ_ENOTSUP
+    assert Q(A, A, 64, 256, 4, 128, 0.01, ctypes.byref(packed(codes=A)), None, E, None) == slq.SLQ_EINVAL
+    assert L.slq_gptq_workspace_bytes(64, 256) > 2 * 256 * 256 * 8
+    assert L.slq_gptq_workspace_bytes(64, 200) == 0
     M = L.slq_mckp_search
     assert M(A, B, 0, 7, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL   # L = 0
     assert M(A, B, 4, 0, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL   # nb = 0

@@ -64,6 +64,10 @@ def lib():
         L.slq_ear_kl.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
         L.slq_ear_kl_topk.argtypes = [_vp, _vp, _i64, _i64, _i64, ctypes.c_double, _vp, _vp, _vp,
                                       _vp, _vp]
+        L.slq_gptq_workspace_bytes.argtypes = [_i64, _i64]
+        L.slq_gptq_workspace_bytes.restype = _sz
+        L.slq_gptq_quantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, ctypes.c_double, _pp, _vp,
+                                        _vp, _vp]
         L.slq_mckp_workspace_bytes.argtypes = [_i64, _i64]
         L.slq_mckp_workspace_bytes.restype = _sz
         L.slq_mckp_search.argtypes = [_vp, _vp, _i64, ctypes.c_int32, _i64, ctypes.c_double, _vp,
@@ -76,7 +80,8 @@ def lib():
         L.slq_strerror.argtypes = [_int]
         L.slq_strerror.restype = ctypes.c_char_p
         for f in ("slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm", "slq_row_lse",
-                  "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_quant_error"):
+                  "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_gptq_quantize",
+                  "slq_quant_error"):
             getattr(L, f).restype = _int
         _LIB = L
     return _LIB
@@ -243,6 +248,23 @@ def slq_ear_kl_topk(logits_p: torch.Tensor, logits_q: torch.Tensor, k: int,
     return ear, kl, means
 
 
+def slq_gptq_quantize(W: torch.Tensor, H: torch.Tensor, bits: int, damp: float = 0.01,
+                      with_u: bool = False):
+    """GPTQ codes for fp32 W[n][k] against the layer Hessian H[k][k] (fp32,
+    device): a PackedWeight (fp32 metadata), and U (fp64 [k][k]) on request."""
+    assert W.dtype == torch.float32 and H.dtype == torch.float32
+    assert W.is_contiguous() and H.is_contiguous()
+    n, k = W.shape
+    pw = alloc_packed(n, k, bits, W.device)
+    desc = pw.c()
+    U = torch.empty((k, k), dtype=torch.float64, device=W.device) if with_u else None
+    ws = workspace(lib().slq_gptq_workspace_bytes(n, k), W.device, "gptq")
+    _check(lib().slq_gptq_quantize(_ptr(W), _ptr(H), n, k, bits, GROUP, float(damp),
+                                   ctypes.byref(desc), _ptr(U), _ptr(ws), _stream(W)),
+           "slq_gptq_quantize")
+    return pw, U
+
+
 def slq_mckp_search(sizes: torch.Tensor, costs: torch.Tensor, W: int, tau: float,
                     with_best: bool = False):
     """Bit-width allocation on the device: exact multiple-choice knapsack for
@@ -277,5 +299,5 @@ def slq_quant_error(W: torch.Tensor, pw: PackedWeight) -> torch.Tensor:
 
 __all__ = ["lib", "SlqError", "SlqPacked", "PackedWeight", "alloc_packed", "workspace",
            "gemm_workspace_bytes", "kernel_name", "slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm",
-           "slq_row_lse", "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_quant_error",
+           "slq_row_lse", "slq_ear_kl", "slq_ear_kl_topk", "slq_mckp_search", "slq_gptq_quantize", "slq_quant_error",
            "SLQ_META_F32", "SLQ_META_COMPACT", "SLQ_ASYM", "SLQ_SYM", "GROUP"]

@@ -19,7 +19,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 EXTRA = {"quantize.hip": ["-ffp-contract=off"],
          # MFMA results in VGPRs: the decode epilogue reads them with plain VALU ops
          "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
-SOURCES = ["quantize.hip", "gemv.hip", "gemm.hip", "fidelity.hip", "mckp.hip", "slq_abi.cpp"]
+SOURCES = ["quantize.hip", "gemv.hip", "gemm.hip", "fidelity.hip", "mckp.hip", "gptq.hip", "slq_abi.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -1,0 +1,451 @@
+// GPTQ code selection for gfx950 (named by the SLQ README, Pipeline, as the
+// code-choice step: layer-wise GPTQ at every bit-width, asymmetric INT, group
+// size 128; the steps follow the published algorithm: Frantar et al., "GPTQ:
+// Accurate Post-Training Quantization for Generative Pre-trained
+// Transformers", Algorithm 1 with the Cholesky form of the inverse Hessian and
+// lazy batched updates).
+//
+//  1. Dead inputs (H_ii = 0) get H_ii = 1 and a zeroed weight column; then
+//     H += damp * mean(diag H) * I.
+//  2. The upper factor U with U^T U = H^-1: with J the index reversal and
+//     J H J = L L^T (lower Cholesky factor), H^-1 = (J L^-1 J)^T (J L^-1 J), so
+//     U = J L^-1 J.  The reversed matrix is factored in fp64 by a blocked
+//     right-looking Cholesky (64 x 64 diagonal blocks in LDS, a panel solve and
+//     a tiled trailing update), and L is inverted by block rows.
+//  3. Columns in groups of 128 (the lazy batch is the group): per weight row,
+//     one lane takes the group's 128 current weights into registers, computes
+//     the group's scale and zero point from them (the plain quantizer's fp32
+//     steps), and for each column quantizes it, divides the error by U_ii and
+//     moves the group's later columns by err * U_ij (U read as wave-uniform
+//     scalars).  A tiled GEMM then moves every later column of the layer by
+//     the group's errors times the matching block of U.
+#include <cmath>
+
+#include "launch.h"
+#include "slq_device.h"
+
+namespace slq {
+namespace {
+
+constexpr int kThr = 256;
+constexpr int kNb = 64;   // Cholesky / inverse block
+constexpr int kLdp = kNb + 1;
+
+__device__ __forceinline__ double block_sum(double v, double *lds) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[w] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kThr / kWave; ++i) t += lds[i];
+  return t;
+}
+
+// mean of the diagonal after dead inputs get 1 (one workgroup, fixed order)
+__global__ __launch_bounds__(kThr) void diag_mean_kernel(const float *__restrict__ H, int64_t k,
+                                                         double *__restrict__ stat) {
+  __shared__ double lds[kThr / kWave];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < k; i += kThr) {
+    const float h = H[i * k + i];
+    s += h == 0.0f ? 1.0 : (double)h;
+  }
+  const double t = block_sum(s, lds);
+  if (threadIdx.x == 0) stat[0] = t / (double)k;
+}
+
+// A = J H' J in fp64 (H' = H with dead diagonals 1 and the damping added)
+__global__ __launch_bounds__(kThr) void prep_kernel(const float *__restrict__ H, int64_t k,
+                                                    double damp, const double *__restrict__ stat,
+                                                    double *__restrict__ A) {
+  const int64_t e = (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (e >= k * k) return;
+  const int64_t i = e / k, j = e % k;
+  const int64_t si = k - 1 - i, sj = k - 1 - j;
+  double h = (double)H[si * k + sj];
+  if (si == sj) {
+    if (h == 0.0) h = 1.0;
+    h += damp * stat[0];
+  }
+  A[e] = h;
+}
+
+// working weights: dead input columns zeroed
+__global__ __launch_bounds__(kThr) void wcopy_kernel(const float *__restrict__ W,
+                                                     const float *__restrict__ H, int64_t n,
+                                                     int64_t k, float *__restrict__ Wk) {
+  const int64_t e = (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (e >= n * k) return;
+  const int64_t c = e % k;
+  Wk[e] = H[c * k + c] == 0.0f ? 0.0f : W[e];
+}
+
+// Cholesky of the diagonal block at j0 (one workgroup, block in LDS)
+__global__ __launch_bounds__(kThr) void potf2_kernel(double *__restrict__ A, int64_t k,
+                                                     int64_t j0) {
+  __shared__ double a[kNb][kLdp];
+  for (int e = threadIdx.x; e < kNb * kNb; e += kThr)
+    a[e / kNb][e % kNb] = A[(j0 + e / kNb) * k + j0 + e % kNb];
+  for (int c = 0; c < kNb; ++c) {
+    __syncthreads();
+    if (threadIdx.x == 0) a[c][c] = sqrt(a[c][c]);
+    __syncthreads();
+    for (int i = c + 1 + threadIdx.x; i < kNb; i += kThr) a[i][c] /= a[c][c];
+    __syncthreads();
+    const int m = kNb - 1 - c;
+    for (int e = threadIdx.x; e < m * m; e += kThr) {
+      const int i = c + 1 + e / m, j = c + 1 + e % m;
+      if (j <= i) a[i][j] -= a[i][c] * a[j][c];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kNb * kNb; e += kThr) {
+    const int i = e / kNb, j = e % kNb;
+    A[(j0 + i) * k + j0 + j] = j <= i ? a[i][j] : 0.0;
+  }
+}
+
+// panel below the diagonal block: rows solve x L11^T = a (one lane per row)
+__global__ __launch_bounds__(kThr) void trsm_kernel(double *__restrict__ A, int64_t k, int64_t j0) {
+  __shared__ double l[kNb][kLdp];
+  for (int e = threadIdx.x; e < kNb * kNb; e += kThr)
+    l[e / kNb][e % kNb] = A[(j0 + e / kNb) * k + j0 + e % kNb];
+  __syncthreads();
+  const int64_t r = j0 + kNb + (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (r >= k) return;
+  double x[kNb];
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) x[c] = A[r * k + j0 + c];
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) {
+    double s = x[c];
+#pragma unroll
+    for (int p = 0; p < c; ++p) s -= x[p] * l[c][p];
+    x[c] = s / l[c][c];
+  }
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) A[r * k + j0 + c] = x[c];
+}
+
+// C -= P_i P_j^T on the trailing lower tiles, P = A[r0:, j0:j0+64]
+__global__ __launch_bounds__(kThr) void syrk_kernel(double *__restrict__ A, int64_t k, int64_t j0) {
+  const int ti = blockIdx.y, tj = blockIdx.x;
+  if (tj > ti) return;
+  constexpr int H = kNb / 2;   // the 64 inner terms in two LDS halves
+  __shared__ double pi[kNb][H + 1], pj[kNb][H + 1];
+  const int64_t r0 = j0 + kNb;
+  const int64_t i0 = r0 + (int64_t)ti * kNb, c0 = r0 + (int64_t)tj * kNb;
+  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  double acc[4][4] = {};
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kNb * H; e += kThr) {
+      pi[e / H][e % H] = A[(i0 + e / H) * k + j0 + h * H + e % H];
+      pj[e / H][e % H] = A[(c0 + e / H) * k + j0 + h * H + e % H];
+    }
+    __syncthreads();
+    for (int p = 0; p < H; ++p) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) av[u] = pi[ty * 4 + u][p];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) bv[v] = pj[tx * 4 + v][p];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) A[(i0 + ty * 4 + u) * k + c0 + tx * 4 + v] -= acc[u][v];
+}
+
+// inverse of every 64 x 64 lower diagonal block of L (one workgroup each; lane
+// c solves L y = e_c by forward substitution)
+__global__ __launch_bounds__(kNb) void diag_inv_kernel(const double *__restrict__ L, int64_t k,
+                                                       double *__restrict__ X) {
+  __shared__ double l[kNb][kNb], y[kNb][kNb];
+  const int64_t b0 = (int64_t)blockIdx.x * kNb;
+  for (int e = threadIdx.x; e < kNb * kNb; e += kNb)
+    l[e / kNb][e % kNb] = L[(b0 + e / kNb) * k + b0 + e % kNb];
+  __syncthreads();
+  const int c = threadIdx.x;
+  for (int r = 0; r < kNb; ++r) {
+    if (r < c) {
+      y[r][c] = 0.0;
+      continue;
+    }
+    double s = r == c ? 1.0 : 0.0;
+    for (int p = c; p < r; ++p) s -= l[r][p] * y[p][c];
+    y[r][c] = s / l[r][r];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kNb * kNb; e += kNb)
+    X[(b0 + e / kNb) * k + b0 + e % kNb] = y[e / kNb][e % kNb];
+}
+
+// block row ib of L^-1: workgroup jb (< ib) forms S = sum_{p=jb}^{ib-1} L[ib][p] X[p][jb]
+// and writes X[ib][jb] = -X[ib][ib] S
+__global__ __launch_bounds__(kThr) void inv_row_kernel(const double *__restrict__ L,
+                                                       double *__restrict__ X, int64_t k,
+                                                       int64_t ib) {
+  constexpr int H = kNb / 2;   // inner terms in two LDS halves
+  __shared__ double ta[kNb][H + 1], tb[H][kNb + 1];
+  const int64_t jb = blockIdx.x;
+  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  double acc[4][4] = {};
+  const int64_t r0 = ib * kNb, c0 = jb * kNb;
+  auto mac = [&](double (&out)[4][4]) {
+    for (int q = 0; q < H; ++q) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) av[u] = ta[ty * 4 + u][q];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) bv[v] = tb[q][tx * 4 + v];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) out[u][v] = fma(av[u], bv[v], out[u][v]);
+    }
+  };
+  for (int64_t p = jb; p < ib; ++p) {
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+      for (int e = threadIdx.x; e < kNb * H; e += kThr) {
+        ta[e / H][e % H] = L[(r0 + e / H) * k + p * kNb + h * H + e % H];
+        tb[e / kNb][e % kNb] = X[(p * kNb + h * H + e / kNb) * k + c0 + e % kNb];
+      }
+      __syncthreads();
+      mac(acc);
+    }
+  }
+  // X[ib][jb] = -X[ib][ib] S: S goes through global memory (this workgroup's
+  // own output block, read back after a barrier) in the same two halves
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) X[(r0 + ty * 4 + u) * k + c0 + tx * 4 + v] = acc[u][v];
+  __threadfence_block();
+  double out[4][4] = {};
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kNb * H; e += kThr) {
+      ta[e / H][e % H] = X[(r0 + e / H) * k + r0 + h * H + e % H];
+      tb[e / kNb][e % kNb] = X[(r0 + h * H + e / kNb) * k + c0 + e % kNb];
+    }
+    __syncthreads();
+    mac(out);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) X[(r0 + ty * 4 + u) * k + c0 + tx * 4 + v] = -out[u][v];
+}
+
+// U[i][j] = X[k-1-i][k-1-j] for j >= i (fp32 for the column loop; fp64 copy on request)
+__global__ __launch_bounds__(kThr) void u_kernel(const double *__restrict__ X, int64_t k,
+                                                 float *__restrict__ Uf, double *__restrict__ Ud) {
+  const int64_t e = (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (e >= k * k) return;
+  const int64_t i = e / k, j = e % k;
+  const double u = j >= i ? X[(k - 1 - i) * k + (k - 1 - j)] : 0.0;
+  Uf[e] = (float)u;
+  if (Ud) Ud[e] = u;
+}
+
+__device__ __forceinline__ float clampq(float v, float maxq) {
+  v = v < 0.0f ? 0.0f : v;
+  return v > maxq ? maxq : v;
+}
+
+template <int BITS>
+__device__ __forceinline__ void pack_group(const float (&w)[kGroup], uint32_t *__restrict__ dst) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t out[BITS];
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) out[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t q = (uint32_t)w[32 * c + j];
+      const int bit = j * BITS, wd = bit / 32, o = bit % 32;
+      out[wd] |= q << o;
+      if (o + BITS > 32) out[wd + 1] |= q >> (32 - o);
+    }
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) dst[c * BITS + i] = out[i];
+  }
+}
+
+// Group g (columns i1 = 128 g ...): one lane per weight row.
+template <int BITS>
+__global__ __launch_bounds__(kThr) void gptq_group_kernel(
+    float *__restrict__ Wk, const float *__restrict__ Uf, int64_t n, int64_t k, int64_t g,
+    uint32_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros,
+    float *__restrict__ err) {
+  const int64_t r = (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (r >= n) return;
+  const float maxq = (float)((1 << BITS) - 1);
+  const int64_t i1 = g * kGroup;
+  float w[kGroup];
+  const float4 *src = reinterpret_cast<const float4 *>(Wk + r * k + i1);
+#pragma unroll
+  for (int i = 0; i < kGroup / 4; ++i) {
+    const float4 v = src[i];
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+  // the plain quantizer's steps on the group's current weights
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    lo = w[i] < lo ? w[i] : lo;
+    hi = w[i] > hi ? w[i] : hi;
+  }
+  float s = (hi - lo) / maxq, zf;
+  if (s == 0.0f) {
+    s = 1.0f;
+    zf = 0.0f;
+  } else {
+    zf = clampq(rintf((-lo) / s), maxq);
+  }
+  const float *ub = Uf + i1 * k + i1;   // U block of the group (wave-uniform reads)
+  float *er = err + r * kGroup;
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    const float q = clampq(rintf(w[i] / s) + zf, maxq);
+    const float what = (float)((int)q - (int)zf) * s;
+    const float e = (w[i] - what) / ub[i * k + i];
+    er[i] = e;
+#pragma unroll
+    for (int j = i + 1; j < kGroup; ++j) w[j] = fmaf(-e, ub[i * k + j], w[j]);
+    w[i] = q;
+  }
+  const int64_t G = k / kGroup;
+  pack_group<BITS>(w, codes + r * (k * BITS / 32) + g * 4 * BITS);
+  scales[r * G + g] = s;
+  zeros[r * G + g] = (uint8_t)(int)zf;
+}
+
+// Wk[:, c] -= sum_p err[:, p] U[i1 + p][c] for the columns after group g
+__global__ __launch_bounds__(kThr) void gptq_update_kernel(float *__restrict__ Wk,
+                                                           const float *__restrict__ Uf,
+                                                           const float *__restrict__ err,
+                                                           int64_t n, int64_t k, int64_t g) {
+  __shared__ float te[64][kGroup + 1];
+  __shared__ float tu[kGroup][64 + 1];
+  const int64_t i1 = g * kGroup, c0 = i1 + kGroup + (int64_t)blockIdx.y * 64;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  for (int e = threadIdx.x; e < 64 * kGroup; e += kThr) {
+    const int64_t rr = r0 + e / kGroup;
+    te[e / kGroup][e % kGroup] = rr < n ? err[rr * kGroup + e % kGroup] : 0.0f;
+  }
+  for (int e = threadIdx.x; e < kGroup * 64; e += kThr)
+    tu[e / 64][e % 64] = Uf[(i1 + e / 64) * k + c0 + e % 64];
+  __syncthreads();
+  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  float acc[4][4] = {};
+  for (int p = 0; p < kGroup; ++p) {
+    float av[4], bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) av[u] = te[ty * 4 + u][p];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) bv[v] = tu[p][tx * 4 + v];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t rr = r0 + ty * 4 + u;
+    if (rr >= n) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Wk[rr * k + c0 + tx * 4 + v] -= acc[u][v];
+  }
+}
+
+template <int BITS>
+hipError_t group_launch(float *Wk, const float *Uf, int64_t n, int64_t k, int64_t g,
+                        uint32_t *codes, float *scales, uint8_t *zeros, float *err,
+                        hipStream_t s) {
+  hipLaunchKernelGGL((gptq_group_kernel<BITS>), dim3((unsigned)((n + kThr - 1) / kThr)),
+                     dim3(kThr), 0, s, Wk, Uf, n, k, g, codes, scales, zeros, err);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Workspace: A, X fp64 [k][k] | Uf fp32 [k][k] | Wk fp32 [n][k] | err fp32 [n][128] | stat
+size_t gptq_workspace(int64_t n, int64_t k) {
+  const size_t b = (size_t)k * k * 8 * 2 + (size_t)k * k * 4 + (size_t)n * k * 4 +
+                   (size_t)n * kGroup * 4 + 256;
+  return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int bits, double damp,
+                       uint32_t *codes, float *scales, uint8_t *zeros, double *u_out, void *ws,
+                       hipStream_t s) {
+  double *A = static_cast<double *>(ws);
+  double *X = A + k * k;
+  float *Uf = reinterpret_cast<float *>(X + k * k);
+  float *Wk = Uf + k * k;
+  float *err = Wk + n * k;
+  double *stat = reinterpret_cast<double *>(err + n * kGroup + 64);   // 256-byte gap
+  hipError_t e;
+  const unsigned kk = (unsigned)((k * k + kThr - 1) / kThr);
+  hipLaunchKernelGGL(diag_mean_kernel, dim3(1), dim3(kThr), 0, s, H, k, stat);
+  hipLaunchKernelGGL(prep_kernel, dim3(kk), dim3(kThr), 0, s, H, k, damp, stat, A);
+  hipLaunchKernelGGL(wcopy_kernel, dim3((unsigned)((n * k + kThr - 1) / kThr)), dim3(kThr), 0, s,
+                     W, H, n, k, Wk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nbk = k / kNb;
+  for (int64_t b = 0; b < nbk; ++b) {
+    const int64_t j0 = b * kNb;
+    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(kThr), 0, s, A, k, j0);
+    const int64_t rest = k - j0 - kNb;
+    if (rest > 0) {
+      hipLaunchKernelGGL(trsm_kernel, dim3((unsigned)((rest + kThr - 1) / kThr)), dim3(kThr), 0,
+                         s, A, k, j0);
+      const unsigned t = (unsigned)(rest / kNb);
+      hipLaunchKernelGGL(syrk_kernel, dim3(t, t), dim3(kThr), 0, s, A, k, j0);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)nbk), dim3(kNb), 0, s, A, k, X);
+  for (int64_t ib = 1; ib < nbk; ++ib)
+    hipLaunchKernelGGL(inv_row_kernel, dim3((unsigned)ib), dim3(kThr), 0, s, A, X, k, ib);
+  hipLaunchKernelGGL(u_kernel, dim3(kk), dim3(kThr), 0, s, X, k, Uf, u_out);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t G = k / kGroup;
+  for (int64_t g = 0; g < G; ++g) {
+    switch (bits) {
+      case 2: e = group_launch<2>(Wk, Uf, n, k, g, codes, scales, zeros, err, s); break;
+      case 3: e = group_launch<3>(Wk, Uf, n, k, g, codes, scales, zeros, err, s); break;
+      case 4: e = group_launch<4>(Wk, Uf, n, k, g, codes, scales, zeros, err, s); break;
+      case 5: e = group_launch<5>(Wk, Uf, n, k, g, codes, scales, zeros, err, s); break;
+      case 6: e = group_launch<6>(Wk, Uf, n, k, g, codes, scales, zeros, err, s); break;
+      case 7: e = group_launch<7>(Wk, Uf, n, k, g, codes, scales, zeros, err, s); break;
+      case 8: e = group_launch<8>(Wk, Uf, n, k, g, codes, scales, zeros, err, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t later = k - (g + 1) * kGroup;
+    if (later > 0) {
+      hipLaunchKernelGGL(gptq_update_kernel,
+                         dim3((unsigned)((n + 63) / 64), (unsigned)(later / 64)), dim3(kThr), 0, s,
+                         Wk, Uf, err, n, k, g);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace slq

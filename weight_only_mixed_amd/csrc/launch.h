@@ -51,6 +51,10 @@ hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *l
                           hipStream_t s);
 hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab, float *ear,
                          float *kl, double *means, void *ws, hipStream_t s);
+size_t gptq_workspace(int64_t n, int64_t k);
+hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int bits, double damp,
+                       uint32_t *codes, float *scales, uint8_t *zeros, double *u_out, void *ws,
+                       hipStream_t s);
 size_t mckp_workspace(int64_t L, int64_t W);
 hipError_t launch_mckp(const int64_t *sizes, const double *costs, int64_t L, int nb, int64_t W,
                        double tau, int32_t *choice, int64_t *result, double *cost, double *best,

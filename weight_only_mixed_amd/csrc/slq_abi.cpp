@@ -270,6 +270,49 @@ slq_status slq_ear_kl_topk(const float *logits_p, const float *logits_q, int64_t
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t slq_gptq_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 1 || n >= kMaxDim || k < kGroupSize || k > 32768 || k % kGroupSize != 0) return 0;
+  return slq::gptq_workspace(n, k);
+}
+
+slq_status slq_gptq_quantize(const float *W, const float *H, int64_t n, int64_t k, int bits,
+                             int group, double damp, slq_packed *out, double *u_out,
+                             void *workspace, slq_stream stream) {
+  if (!out || bits < 2 || bits > 8 || group <= 0) return SLQ_EINVAL;
+  if (group != kGroupSize) return SLQ_ENOTSUP;
+  if (n < 1 || n >= kMaxDim || k < kGroupSize || k > 32768 || k % kGroupSize != 0 ||
+      n * k >= kMaxDim * 64)
+    return SLQ_EINVAL;
+  if (!(damp > 0.0) || !std::isfinite(damp)) return SLQ_EINVAL;
+  if (!meta_ok(out->meta)) return SLQ_EINVAL;
+  if (out->meta != SLQ_META_F32) return SLQ_ENOTSUP;
+  const PackedSizes sz = sizes_of(n, k, bits, group, out->meta);
+  const size_t wsb = slq_gptq_workspace_bytes(n, k);
+  if (!W || !H || !workspace || !out->codes || !out->scales || !out->zeros) return SLQ_EINVAL;
+  if (!aligned(W, 16) || !aligned(H, 16) || !aligned(workspace, 256) || !aligned(out->codes, 16) ||
+      !aligned(out->scales, 16) || !aligned(out->zeros, 4) || (u_out && !aligned(u_out, 8)))
+    return SLQ_EINVAL;
+  const size_t wb = (size_t)(n * k) * 4, hb = (size_t)(k * k) * 4, ub = (size_t)(k * k) * 8;
+  const void *in[2] = {W, H};
+  const size_t inb[2] = {wb, hb};
+  const void *outs[5] = {out->codes, out->scales, out->zeros, workspace, u_out};
+  const size_t outb[5] = {sz.codes, sz.scales, sz.zeros, wsb, u_out ? ub : 0};
+  for (int i = 0; i < 5; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 2; ++j)
+      if (overlap(outs[i], outb[i], in[j], inb[j])) return SLQ_EINVAL;
+    for (int j = i + 1; j < 5; ++j)
+      if (outs[j] && overlap(outs[i], outb[i], outs[j], outb[j])) return SLQ_EINVAL;
+  }
+  out->bits = bits;
+  out->group = group;
+  out->n = n;
+  out->k = k;
+  return from_hip(slq::launch_gptq(W, H, n, k, bits, damp, out->codes,
+                                   static_cast<float *>(out->scales), out->zeros, u_out, workspace,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 size_t slq_mckp_workspace_bytes(int64_t L, int64_t W) {
   if (L < 1 || L >= kMaxDim || W < 0 || W >= kMaxDim - 1) return 0;
   return slq::mckp_workspace(L, W);
