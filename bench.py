@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default="all", help="extra rows: all, none, or a comma list of "
-                    "quantize,gemm,stack,fidelity,allocation,gamma,compact")
+                    "quantize,gemm,stack,fidelity,allocation,gptq,gamma,compact")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--pmc", default=None, metavar="KERNEL",
@@ -128,7 +128,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     torch.manual_seed(0)
-    rows_sel = {"quantize", "gemm", "stack", "fidelity", "allocation", "gamma", "compact"} if args.rows == "all" else (
+    rows_sel = {"quantize", "gemm", "stack", "fidelity", "allocation", "gptq", "gamma", "compact"} if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
 
     def to_dev(a):
@@ -476,6 +476,32 @@ def main():
                               "status": int(r[0]), "budget_units": int(r[1]),
                               "mean_bits": round(float((bits * sz[:, 0]).sum() / sz[:, 0].sum()), 3)}
         log(f"bench: allocation {ms:.3f} ms")
+
+    # ---------------- GPTQ code selection ----------------
+    if "gptq" in rows_sel:
+        log("bench: GPTQ, Llama-3-8B q (4096x4096) and gate (14336x4096) at 4 bits")
+        kq = 4096
+        g = np.random.Generator(np.random.PCG64(S.seed_for(6)))
+        # synthetic Hessian 2 X X^T / T from correlated seeded activations (T = 2k);
+        # the product is input synthesis on the device
+        Xa = torch.from_numpy((g.standard_normal((kq, 8)) @ g.standard_normal((8, 2 * kq))
+                               + 0.5 * g.standard_normal((kq, 2 * kq))).astype(np.float32)).to(dev)
+        Hd = (2.0 / (2 * kq)) * (Xa @ Xa.T)
+        Hd = 0.5 * (Hd + Hd.T).contiguous()
+        del Xa
+        res = {}
+        for (shape, n_) in (("q", 4096), ("gate", 14336)):
+            Wg = to_dev(S.skewed_weights(n_, kq, S.seed_for(6, 1)))
+            slq.slq_gptq_quantize(Wg, Hd, 4)
+            torch.cuda.synchronize()
+            with Timer(torch) as T:
+                slq.slq_gptq_quantize(Wg, Hd, 4)
+            res[shape] = {"n": n_, "k": kq, "ms": round(T.ms, 2)}
+            log(f"bench: GPTQ {shape} {n_}x{kq}: {T.ms:.1f} ms")
+            del Wg
+        rows["gptq"] = res
+        del Hd
+        torch.cuda.empty_cache()
 
     # ---------------- gamma-squared ----------------
     if "gamma" in rows_sel:

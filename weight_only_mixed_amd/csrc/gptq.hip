@@ -11,7 +11,8 @@
 //     J H J = L L^T (lower Cholesky factor), H^-1 = (J L^-1 J)^T (J L^-1 J), so
 //     U = J L^-1 J.  The reversed matrix is factored in fp64 by a blocked
 //     right-looking Cholesky (64 x 64 diagonal blocks in LDS, a panel solve and
-//     a tiled trailing update), and L is inverted by block rows.
+//     a tiled trailing update), and L is inverted by right-looking block
+//     substitution (every step a grid of tile updates).
 //  3. Columns in groups of 128 (the lazy batch is the group): per weight row,
 //     one lane takes the group's 128 current weights into registers, computes
 //     the group's scale and zero point from them (the plain quantizer's fp32
@@ -82,29 +83,35 @@ __global__ __launch_bounds__(kThr) void wcopy_kernel(const float *__restrict__ W
   Wk[e] = H[c * k + c] == 0.0f ? 0.0f : W[e];
 }
 
-// Cholesky of the diagonal block at j0 (one workgroup, block in LDS)
-__global__ __launch_bounds__(kThr) void potf2_kernel(double *__restrict__ A, int64_t k,
-                                                     int64_t j0) {
-  __shared__ double a[kNb][kLdp];
-  for (int e = threadIdx.x; e < kNb * kNb; e += kThr)
-    a[e / kNb][e % kNb] = A[(j0 + e / kNb) * k + j0 + e % kNb];
+// Cholesky of the diagonal block at j0: one wavefront, lane i holds row i of
+// the block in registers.  Column c: the pivot and then each scaled entry of
+// column c are broadcast from their lanes (readlane), and every lane updates
+// its own row.  Entries right of a lane's diagonal receive junk and are never
+// stored.
+__device__ __forceinline__ double lane_bcast(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(kNb) void potf2_kernel(double *__restrict__ A, int64_t k, int64_t j0) {
+  const int i = threadIdx.x;
+  double r[kNb];
+  const double *src = A + (j0 + i) * k + j0;
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) r[c] = src[c];
+#pragma unroll
   for (int c = 0; c < kNb; ++c) {
-    __syncthreads();
-    if (threadIdx.x == 0) a[c][c] = sqrt(a[c][c]);
-    __syncthreads();
-    for (int i = c + 1 + threadIdx.x; i < kNb; i += kThr) a[i][c] /= a[c][c];
-    __syncthreads();
-    const int m = kNb - 1 - c;
-    for (int e = threadIdx.x; e < m * m; e += kThr) {
-      const int i = c + 1 + e / m, j = c + 1 + e % m;
-      if (j <= i) a[i][j] -= a[i][c] * a[j][c];
-    }
+    const double d = sqrt(lane_bcast(r[c], c));
+    const double l = i > c ? r[c] / d : (i == c ? d : 0.0);
+    r[c] = l;
+#pragma unroll
+    for (int jj = c + 1; jj < kNb; ++jj) r[jj] = fma(-l, lane_bcast(l, jj), r[jj]);
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < kNb * kNb; e += kThr) {
-    const int i = e / kNb, j = e % kNb;
-    A[(j0 + i) * k + j0 + j] = j <= i ? a[i][j] : 0.0;
-  }
+  double *dst = A + (j0 + i) * k + j0;
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) dst[c] = c <= i ? r[c] : 0.0;
 }
 
 // panel below the diagonal block: rows solve x L11^T = a (one lane per row)
@@ -164,10 +171,10 @@ __global__ __launch_bounds__(kThr) void syrk_kernel(double *__restrict__ A, int6
     for (int v = 0; v < 4; ++v) A[(i0 + ty * 4 + u) * k + c0 + tx * 4 + v] -= acc[u][v];
 }
 
-// inverse of every 64 x 64 lower diagonal block of L (one workgroup each; lane
-// c solves L y = e_c by forward substitution)
+// inverse of every 64 x 64 lower diagonal block of L into Dinv[b] (one
+// workgroup each; lane c solves L y = e_c by forward substitution)
 __global__ __launch_bounds__(kNb) void diag_inv_kernel(const double *__restrict__ L, int64_t k,
-                                                       double *__restrict__ X) {
+                                                       double *__restrict__ Dinv) {
   __shared__ double l[kNb][kNb], y[kNb][kNb];
   const int64_t b0 = (int64_t)blockIdx.x * kNb;
   for (int e = threadIdx.x; e < kNb * kNb; e += kNb)
@@ -185,21 +192,29 @@ __global__ __launch_bounds__(kNb) void diag_inv_kernel(const double *__restrict_
   }
   __syncthreads();
   for (int e = threadIdx.x; e < kNb * kNb; e += kNb)
-    X[(b0 + e / kNb) * k + b0 + e % kNb] = y[e / kNb][e % kNb];
+    Dinv[(int64_t)blockIdx.x * kNb * kNb + e] = y[e / kNb][e % kNb];
 }
 
-// block row ib of L^-1: workgroup jb (< ib) forms S = sum_{p=jb}^{ib-1} L[ib][p] X[p][jb]
-// and writes X[ib][jb] = -X[ib][ib] S
-__global__ __launch_bounds__(kThr) void inv_row_kernel(const double *__restrict__ L,
-                                                       double *__restrict__ X, int64_t k,
-                                                       int64_t ib) {
-  constexpr int H = kNb / 2;   // inner terms in two LDS halves
-  __shared__ double ta[kNb][H + 1], tb[H][kNb + 1];
-  const int64_t jb = blockIdx.x;
+// L^-1 by right-looking block substitution of L X = I, in place in X (which
+// holds the running right-hand side, zero below the diagonal at the start).
+// Step b: X[b][c] = Dinv_b X[b][c] for c < b and X[b][b] = Dinv_b (inv_scale),
+// then X[i][c] -= L[i][b] X[b][c] for every i > b, c <= b (inv_update).
+
+// 64 x 64 tile product acc += P Q, P and Q row-major with leading dimensions,
+// through LDS in two halves of the inner dimension (4 x 4 outputs per lane).
+__device__ __forceinline__ void tile_mac(const double *__restrict__ P, int64_t ldp,
+                                         const double *__restrict__ Q, int64_t ldq,
+                                         double (&acc)[4][4], double (*ta)[kNb / 2 + 1],
+                                         double (*tb)[kNb + 1]) {
+  constexpr int H = kNb / 2;
   const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
-  double acc[4][4] = {};
-  const int64_t r0 = ib * kNb, c0 = jb * kNb;
-  auto mac = [&](double (&out)[4][4]) {
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kNb * H; e += kThr) {
+      ta[e / H][e % H] = P[(int64_t)(e / H) * ldp + h * H + e % H];
+      tb[e / kNb][e % kNb] = Q[(int64_t)(h * H + e / kNb) * ldq + e % kNb];
+    }
+    __syncthreads();
     for (int q = 0; q < H; ++q) {
       double av[4], bv[4];
 #pragma unroll
@@ -209,42 +224,50 @@ __global__ __launch_bounds__(kThr) void inv_row_kernel(const double *__restrict_
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) out[u][v] = fma(av[u], bv[v], out[u][v]);
-    }
-  };
-  for (int64_t p = jb; p < ib; ++p) {
-    for (int h = 0; h < 2; ++h) {
-      __syncthreads();
-      for (int e = threadIdx.x; e < kNb * H; e += kThr) {
-        ta[e / H][e % H] = L[(r0 + e / H) * k + p * kNb + h * H + e % H];
-        tb[e / kNb][e % kNb] = X[(p * kNb + h * H + e / kNb) * k + c0 + e % kNb];
-      }
-      __syncthreads();
-      mac(acc);
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
     }
   }
-  // X[ib][jb] = -X[ib][ib] S: S goes through global memory (this workgroup's
-  // own output block, read back after a barrier) in the same two halves
+}
+
+__global__ __launch_bounds__(kThr) void inv_scale_kernel(const double *__restrict__ Dinv,
+                                                         double *__restrict__ X, int64_t k,
+                                                         int64_t b) {
+  __shared__ double ta[kNb][kNb / 2 + 1], tb[kNb / 2][kNb + 1];
+  const int64_t c = blockIdx.x;
+  const double *D = Dinv + b * kNb * kNb;
+  double *out = X + b * kNb * k + c * kNb;
+  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  if (c == b) {
+    for (int e = threadIdx.x; e < kNb * kNb; e += kThr) out[(e / kNb) * k + e % kNb] = D[e];
+    return;
+  }
+  double acc[4][4] = {};
+  tile_mac(D, kNb, out, k, acc, ta, tb);
+  __syncthreads();   // every lane has read the block before it is overwritten
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) X[(r0 + ty * 4 + u) * k + c0 + tx * 4 + v] = acc[u][v];
-  __threadfence_block();
-  double out[4][4] = {};
-  for (int h = 0; h < 2; ++h) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < kNb * H; e += kThr) {
-      ta[e / H][e % H] = X[(r0 + e / H) * k + r0 + h * H + e % H];
-      tb[e / kNb][e % kNb] = X[(r0 + h * H + e / kNb) * k + c0 + e % kNb];
-    }
-    __syncthreads();
-    mac(out);
-  }
-  __syncthreads();
+    for (int v = 0; v < 4; ++v) out[(ty * 4 + u) * k + tx * 4 + v] = acc[u][v];
+}
+
+__global__ __launch_bounds__(kThr) void inv_update_kernel(const double *__restrict__ L,
+                                                          double *__restrict__ X, int64_t k,
+                                                          int64_t b) {
+  __shared__ double ta[kNb][kNb / 2 + 1], tb[kNb / 2][kNb + 1];
+  const int64_t c = blockIdx.x, i = b + 1 + blockIdx.y;
+  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  double acc[4][4] = {};
+  tile_mac(L + i * kNb * k + b * kNb, k, X + b * kNb * k + c * kNb, k, acc, ta, tb);
+  double *out = X + i * kNb * k + c * kNb;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) X[(r0 + ty * 4 + u) * k + c0 + tx * 4 + v] = -out[u][v];
+    for (int v = 0; v < 4; ++v) out[(ty * 4 + u) * k + tx * 4 + v] -= acc[u][v];
+}
+
+__global__ __launch_bounds__(kThr) void zero_kernel(double *__restrict__ p, int64_t n) {
+  const int64_t e = (int64_t)blockIdx.x * kThr + threadIdx.x;
+  if (e < n) p[e] = 0.0;
 }
 
 // U[i][j] = X[k-1-i][k-1-j] for j >= i (fp32 for the column loop; fp64 copy on request)
@@ -383,10 +406,11 @@ hipError_t group_launch(float *Wk, const float *Uf, int64_t n, int64_t k, int64_
 
 }  // namespace
 
-// Workspace: A, X fp64 [k][k] | Uf fp32 [k][k] | Wk fp32 [n][k] | err fp32 [n][128] | stat
+// Workspace: A, X fp64 [k][k] | Uf fp32 [k][k] | Wk fp32 [n][k] | err fp32 [n][128] |
+// gap | stat | Dinv fp64 [k/64][64][64]
 size_t gptq_workspace(int64_t n, int64_t k) {
   const size_t b = (size_t)k * k * 8 * 2 + (size_t)k * k * 4 + (size_t)n * k * 4 +
-                   (size_t)n * kGroup * 4 + 256;
+                   (size_t)n * kGroup * 4 + 256 + 256 + (size_t)k * kNb * 8;
   return (b + 255) / 256 * 256;
 }
 
@@ -399,6 +423,7 @@ hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int
   float *Wk = Uf + k * k;
   float *err = Wk + n * k;
   double *stat = reinterpret_cast<double *>(err + n * kGroup + 64);   // 256-byte gap
+  double *Dinv = stat + 32;                                            // [k / 64][64][64]
   hipError_t e;
   const unsigned kk = (unsigned)((k * k + kThr - 1) / kThr);
   hipLaunchKernelGGL(diag_mean_kernel, dim3(1), dim3(kThr), 0, s, H, k, stat);
@@ -409,7 +434,7 @@ hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int
   const int64_t nbk = k / kNb;
   for (int64_t b = 0; b < nbk; ++b) {
     const int64_t j0 = b * kNb;
-    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(kThr), 0, s, A, k, j0);
+    hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(kNb), 0, s, A, k, j0);
     const int64_t rest = k - j0 - kNb;
     if (rest > 0) {
       hipLaunchKernelGGL(trsm_kernel, dim3((unsigned)((rest + kThr - 1) / kThr)), dim3(kThr), 0,
@@ -419,9 +444,15 @@ hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)nbk), dim3(kNb), 0, s, A, k, X);
-  for (int64_t ib = 1; ib < nbk; ++ib)
-    hipLaunchKernelGGL(inv_row_kernel, dim3((unsigned)ib), dim3(kThr), 0, s, A, X, k, ib);
+  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)nbk), dim3(kNb), 0, s, A, k, Dinv);
+  hipLaunchKernelGGL(zero_kernel, dim3(kk), dim3(kThr), 0, s, X, k * k);
+  for (int64_t b = 0; b < nbk; ++b) {
+    hipLaunchKernelGGL(inv_scale_kernel, dim3((unsigned)(b + 1)), dim3(kThr), 0, s, Dinv, X, k, b);
+    if (b + 1 < nbk)
+      hipLaunchKernelGGL(inv_update_kernel, dim3((unsigned)(b + 1), (unsigned)(nbk - b - 1)),
+                         dim3(kThr), 0, s, A, X, k, b);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(u_kernel, dim3(kk), dim3(kThr), 0, s, X, k, Uf, u_out);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t G = k / kGroup;
