@@ -932,6 +932,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
     return std::min<int64_t>((g + unit - 1) / unit * unit, cap);
   };
   int wv = kWaves;
+  int64_t gw_wide = 0;
   if (p.mt == 1) {
     int w = p.xd ? 8 : 16;
     int64_t g = k_block(w);
@@ -940,9 +941,24 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
       g = k_block(w);
     }
     if (w > kWaves && nb * std::max<int64_t>(1, (G + g - 1) / g) <= kWvBlocks) wv = w;
+    if (wv == kWaves && !p.xd) {
+      // Small grids whose k-blocks hold too few 4-group metadata units for
+      // wide workgroups: wide workgroups on fewer (or no) k splits instead,
+      // with metadata staged per group (the split tails cost more than the
+      // vector staging saves).
+      for (int w2 : {16, 8}) {
+        const int64_t ks2 = std::max<int64_t>(ks_min, (target * kWaves / w2 + nb - 1) / nb);
+        const int64_t g2 = std::max<int64_t>(1, (G + ks2 - 1) / ks2);
+        if (g2 > gw_max || g2 < w2 || nb * ((G + g2 - 1) / g2) > kWvBlocks) continue;
+        wv = w2;
+        gw_wide = g2;
+        p.mv = false;
+        break;
+      }
+    }
   }
   p.wv = wv;
-  const int64_t gw = k_block(wv);
+  const int64_t gw = gw_wide ? gw_wide : k_block(wv);
   p.gw = (int)gw;
   p.b = (p.xd && p.mt > 1) ? 1 : p.nt == 1 ? kBatchNt1 : p.nt == 2 ? kBatchNt2 : kBatchNt4;
   p.ksplits = (int)std::max<int64_t>(1, (G + p.gw - 1) / p.gw);
