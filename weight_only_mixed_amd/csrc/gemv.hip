@@ -506,7 +506,10 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
 // Each wavefront keeps kRowsDepth groups of its codes in flight and stages
 // its rows' scales and zero points for the k-block in LDS.  Zero points use
 // one shared S chain per m-tile (t = (C - S) - z * S / 128, or C - z * S).
-constexpr int kRowsDepth = 4;
+#ifndef SLQ_GEMV_ROWS_DEPTH
+#define SLQ_GEMV_ROWS_DEPTH 4
+#endif
+constexpr int kRowsDepth = SLQ_GEMV_ROWS_DEPTH;
 constexpr int kRowsXPitch = 68;   // words per activation row and group (64 + 4 vs bank conflicts)
 
 template <int BITS, int MT, bool CM>

@@ -14,6 +14,10 @@ namespace {
 
 constexpr int kGroupSize = 128;                 // group size the kernels are built for
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // kernels index rows/cols with int
+#ifndef SLQ_DECODE_MAX_M
+#define SLQ_DECODE_MAX_M 64
+#endif
+constexpr int64_t kDecodeMaxM = SLQ_DECODE_MAX_M;   // activation rows served by the decode kernels
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -135,7 +139,7 @@ size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w) {
   PackedSizes sz;
   if (m < 0 || m >= kMaxDim || check_packed(w, &sz) != SLQ_OK) return 0;
   if (m == 0 || w->n == 0) return 0;
-  if (m <= 64) return slq::gemv_plan(m, w->n, w->k, w->bits).ws_bytes;
+  if (m <= kDecodeMaxM) return slq::gemv_plan(m, w->n, w->k, w->bits).ws_bytes;
   return slq::gemm_workspace(m, w->n, w->k, w->bits);
 }
 
@@ -158,7 +162,7 @@ slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t
       overlap(workspace, wsb, w->scales, sz.scales) || overlap(workspace, wsb, w->zeros, sz.zeros))
     return SLQ_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (m <= 64) {
+  if (m <= kDecodeMaxM) {
     const slq::GemvPlan plan = slq::gemv_plan(m, w->n, w->k, w->bits);
     if (plan.ksplits == 0) return SLQ_ENOTSUP;
     return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros,
@@ -175,7 +179,7 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
   PackedSizes sz;
   buf[0] = '\0';
   if (m <= 0 || m >= kMaxDim || check_packed(w, &sz) != SLQ_OK) return buf;
-  if (m <= 64) {
+  if (m <= kDecodeMaxM) {
     const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
     const char *cm = w->meta == SLQ_META_COMPACT ? "true" : "false";
     if (p.rows)
