@@ -101,3 +101,15 @@ def test_quant_error_compact():
         sv = np.vectorize(oracle.f16_value)(s16).astype(np.float32)
         sse, s2 = oracle.quant_error(W, wh, sv)
         assert abs(out[0] - sse) <= 1e-9 * sse and abs(out[1] - s2) <= 1e-12 * s2
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_full_sweep_shapes_bit_exact(bits):
+    """Compact quantize/pack at the decode sweep's gate/up and down shapes."""
+    for (n, k) in [(14336, 4096), (4096, 14336)]:
+        W = S.skewed_weights(n, k, 500 + bits, row_offset_std=0.005)
+        pw = pack_compact(W, bits)
+        q, s16, zp = oracle_compact(W, bits)
+        assert np.array_equal(pw.codes.cpu().numpy().view(np.uint32), oracle.pack(q, bits))
+        assert np.array_equal(pw.scales.cpu().numpy().view(np.uint16), s16.ravel())
+        assert np.array_equal(pw.zeros.cpu().numpy(), zp)

@@ -82,3 +82,20 @@ def test_dead_input_and_full_layer():
     l_rtn = G.proxy_loss(W, oracle.dequantize(q0, s0, z0), H)
     say(f"gptq 512x4096: loss {l_gpu:.4g} vs rtn {l_rtn:.4g}")
     assert l_gpu < 0.6 * l_rtn
+
+
+def test_full_q_layer_sampled_rows():
+    """Llama-3-8B q projection (4096 x 4096) with a 4096^2 Hessian: rows are
+    independent given H, so the oracle runs on 24 sampled rows of the layer
+    the GPU quantized whole."""
+    k = 4096
+    H = S.gptq_hessian(k, 91, tokens=2 * k)
+    W = S.skewed_weights(4096, k, 92, row_offset_std=0.005)
+    q, s, z, _ = gpu_gptq(W, H, 4)
+    rows = np.random.default_rng(93).choice(4096, 24, replace=False)
+    qr, sr, zr, _ = G.gptq(W[rows], H, 4)
+    agree = (q[rows] == qr).mean()
+    l_gpu = G.proxy_loss(W[rows], oracle.dequantize(q[rows], s[rows], z[rows]), H)
+    l_ref = G.proxy_loss(W[rows], oracle.dequantize(qr, sr, zr), H)
+    say(f"gptq 4096x4096 sampled: codes agree {agree:.4f}, loss {l_gpu:.4g} vs {l_ref:.4g}")
+    assert agree >= 0.99 and abs(l_gpu - l_ref) <= 0.01 * l_ref
