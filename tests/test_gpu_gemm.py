@@ -56,6 +56,28 @@ def test_prefill_small_shapes(bits):
 
 
 @pytest.mark.parametrize("bits", BITS)
+def test_prefill_wide_tiles_ragged(bits):
+    """Grids of at least 256 tiles of 256 x 256 (the wide-tile kernel) with
+    ragged m and n edges; k = 128 is the shortest pipeline (two k steps).
+    Sampled outputs plus the whole last row and the whole last column."""
+    for (m, n, k) in [(4000, 16000, 128), (4095, 16130, 640)]:
+        say(f"prefill wide bits={bits} m={m} n={n} k={k}")
+        W = S.skewed_weights(n, k, 11 * bits + k, row_offset_std=0.005)
+        x = S.activations_bf16(m, k, m + bits + k)
+        pw = slq.slq_quantize_pack(gpu(W), bits)
+        assert slq.kernel_name(m, pw).startswith("slq::gemm_wide_kernel")
+        y = slq.slq_dequant_gemm(x_gpu(x), pw)
+        mi, ni = sample_pairs(m, n, 3000, seed=bits + k)
+        mi = np.concatenate([mi, np.full(n, m - 1), np.arange(m)])
+        ni = np.concatenate([ni, np.arange(n), np.full(m, n - 1)])
+        ys = y[torch.from_numpy(mi).to(DEV), torch.from_numpy(ni).to(DEV)].cpu().numpy()
+        yr, br = oracle_sampled(W, bits, x, mi, ni)
+        assert_gemm_close(ys, yr, br, what=f"wide b{bits} {m}x{n}x{k}")
+        del y, pw
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bits", BITS)
 def test_exact_pins(bits):
     """One-hot activations give w_hat exactly (decode path); zero rows give 0;
     identical activation rows give identical outputs."""

@@ -316,17 +316,233 @@ __global__ __launch_bounds__(kThreads, kMT * kNTW > 8 ? 1 : 2) void gemm_kernel(
   }
 }
 
+// ---- Wide tiles: 256 (m) x 256 (n), one wavefront per SIMD ----
+//
+// Wavefront w owns columns [64w, 64w + 64) and all 256 rows (8 x 2 MFMA
+// tiles, 256 fp32 accumulators in the accumulation registers), so every
+// dequantized B operand feeds eight MFMAs: half the dequantization work per
+// MFMA of the 128-row tiles, which matters because the unpack, the fma and
+// the bf16 conversion run on the VALU at ~3 instructions per code.
+// With one wavefront per SIMD nothing else hides latency, so the operands of
+// slice s+1 (A from LDS, B dequantized from registers) are produced while the
+// 16 MFMAs of slice s run, including across step boundaries: the activation
+// tile goes through three LDS buffers (written two steps ahead), so the A
+// operands of the next step's first slice can be read before the step's
+// closing barrier.
+constexpr int kWideMT = 8;                  // 32-row MFMA tiles per wavefront
+constexpr int kWideBM = 32 * kWideMT;       // 256
+constexpr int kWideBN = 256;
+constexpr int kWideBuf = kWideBM * kPitch;  // bf16 elements per LDS buffer
+constexpr size_t kWideLdsBytes = (size_t)3 * kWideBuf * 2;
+
+// VALU instructions to place after each MFMA (the dequantization of one
+// 8-code B slice per 32-column tile, spread over the 16 MFMAs of a slice).
+template <int BITS>
+constexpr int wide_valu_per_mfma() {
+  return BITS == 4 ? 4 : BITS == 8 ? 4 : BITS == 2 ? 4 : 6;
+}
+
+template <int BITS, bool CM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    float *__restrict__ y) {
+  const MetaRd<BITS, CM> md{scales, zeros};
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_x[];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int c32 = lane & 31, h = lane >> 5;
+  const int m0 = blockIdx.y * kWideBM, n0 = blockIdx.x * kWideBN + 64 * wave;
+  const int G = K / kGroup;
+  const int64_t wpr = (int64_t)K * BITS / 32;
+  const int steps = K / kBK;
+
+  // activation staging: thread t copies rows t/2 and t/2 + 128, k half t%2
+  const int sr = threadIdx.x >> 1, sh = threadIdx.x & 1;
+  const u32x4_t *xsrc[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    xsrc[r] = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(m0 + sr + 128 * r, M - 1) * K + 32 * sh);
+  auto load_x = [&](int st, u32x4_t (&v)[2][4]) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[r][i] = xsrc[r][st * (kBK / 8) + i];
+  };
+  auto store_x = [&](int b, const u32x4_t (&v)[2][4]) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      u32x4_t *dst = reinterpret_cast<u32x4_t *>(&lds_x[b * kWideBuf + (sr + 128 * r) * kPitch + 32 * sh]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = v[r][i];
+    }
+  };
+
+  // weights: as in gemm_kernel, column n0 + 32t + c32, chunk 2*st + h of the row
+  const uint32_t *crow[2];
+  int64_t mrow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = min(n0 + 32 * t + c32, N - 1);
+    crow[t] = codes + (int64_t)n * wpr + h * BITS;
+    mrow[t] = (int64_t)n * G;
+  }
+  auto load_w = [&](int st, Chunk<BITS> (&c)[2], float (&sv)[2], uint32_t (&zv)[2]) {
+    const int g = (st * kBK) / kGroup;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      c[t] = load_chunk<BITS>(crow[t] + (int64_t)st * 2 * BITS);
+      sv[t] = md.scale(mrow[t] + g);
+      zv[t] = md.zero(mrow[t] + g);
+    }
+  };
+  // A operands of slice ks from LDS buffer b
+  auto read_a = [&](int b, int ks, u32x4_t (&a)[kWideMT]) {
+#pragma unroll
+    for (int i = 0; i < kWideMT; ++i)
+      a[i] = *reinterpret_cast<const u32x4_t *>(&lds_x[b * kWideBuf + (32 * i + c32) * kPitch + 32 * h + 8 * ks]);
+  };
+
+  f32x16_t acc[kWideMT][2];
+#pragma unroll
+  for (int i = 0; i < kWideMT; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
+
+  // Prologue: x(0), x(1) into buffers 0 and 1; weights of steps 0 and 1;
+  // the first slice's operands.
+  u32x4_t xr[2][4];
+  Chunk<BITS> wA[2], wB[2];
+  float sA[2], sB[2];
+  uint32_t zA[2], zB[2];
+  load_x(0, xr);
+  load_w(0, wA, sA, zA);
+  load_w(1, wB, sB, zB);   // steps = 2 * groups >= 2
+  store_x(0, xr);
+  load_x(1, xr);
+  store_x(1, xr);
+  __syncthreads();
+  u32x4_t a0[kWideMT], a1[kWideMT], b0[2], b1[2];
+  read_a(0, 0, a0);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) b0[t] = dequant_slice<BITS>(wA[t], make_deq(sA[t], zA[t]), 0);
+
+  auto mfma_slice = [&](const u32x4_t (&a)[kWideMT], const u32x4_t (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < kWideMT; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) acc[i][t] = mfma32(a[i], b[t], acc[i][t]);
+  };
+  // Ordering hints for one slice: each MFMA is followed by a few VALU
+  // instructions of the next slice's dequantization, and every other one by
+  // one of its LDS reads.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, wide_valu_per_mfma<BITS>(), 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, wide_valu_per_mfma<BITS>(), 0);
+    }
+  };
+
+  // Step st uses LDS buffer st % 3 and weight set w (wn for step st + 1).
+  // On entry a0 / b0 hold slice 0's operands; on exit they hold those of
+  // step st + 1 (past the last step: discarded reads of valid memory).
+  int bcur = 0;
+  auto step = [&](int st, Chunk<BITS> (&w)[2], float (&sw)[2], uint32_t (&zw)[2],
+                  const Chunk<BITS> (&wn)[2], const float (&swn)[2], const uint32_t (&zwn)[2]) {
+    const int bnext = bcur == 2 ? 0 : bcur + 1, bfill = bnext == 2 ? 0 : bnext + 1;
+    const int n2 = min(st + 2, steps - 1);   // past the end: reload the last step (discarded)
+    // Each slice is its own scheduling region (sched_barrier), so the
+    // interleaving hints see exactly one slice's MFMAs and the work that
+    // produces the next slice's operands, and nothing that waits on younger
+    // loads is hoisted into an earlier slice.
+    load_x(n2, xr);
+    Deq d[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) d[t] = make_deq(sw[t], zw[t]);
+    // slice 0: produce slice 1
+    read_a(bcur, 1, a1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) b1[t] = dequant_slice<BITS>(w[t], d[t], 1);
+    mfma_slice(a0, b0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 1: produce slice 2
+    read_a(bcur, 2, a0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) b0[t] = dequant_slice<BITS>(w[t], d[t], 2);
+    mfma_slice(a1, b1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 2: produce slice 3; then this step's chunks are free for step st + 2
+    read_a(bcur, 3, a1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) b1[t] = dequant_slice<BITS>(w[t], d[t], 3);
+    mfma_slice(a0, b0);
+    interleave();
+    load_w(n2, w, sw, zw);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice 3: produce slice 0 of step st + 1 (its buffer was filled two steps
+    // ago, its weights one step ago)
+    Deq dn[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) dn[t] = make_deq(swn[t], zwn[t]);
+    read_a(bnext, 0, a0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) b0[t] = dequant_slice<BITS>(wn[t], dn[t], 0);
+    mfma_slice(a1, b1);
+    interleave();
+    store_x(bfill, xr);
+    __syncthreads();
+    bcur = bnext;
+  };
+  for (int st = 0; st < steps; st += 2) {
+    step(st, wA, sA, zA, wB, sB, zB);
+    step(st + 1, wB, sB, zB, wA, sA, zA);
+  }
+
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = n0 + 32 * t + c32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < kWideMT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
+        if (m < M) y[(int64_t)m * N + n] = acc[i][t][e];
+      }
+  }
+}
+
+template <auto Kernel>
+hipError_t set_lds(size_t bytes) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (attr != hipSuccess) (void)hipGetLastError();   // leave no sticky error behind
+  return attr;
+}
+
 template <int BITS, bool CM>
 hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
                      hipStream_t st) {
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_kernel<BITS, CM>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-  if (attr != hipSuccess) {
-    (void)hipGetLastError();   // leave no sticky error behind for later calls
-    return attr;
+  if (gemm_wide(m, n)) {
+    const hipError_t attr = set_lds<&gemm_wide_kernel<BITS, CM>>(kWideLdsBytes);
+    if (attr != hipSuccess) return attr;
+    const dim3 grid((unsigned)((n + kWideBN - 1) / kWideBN), (unsigned)((m + kWideBM - 1) / kWideBM));
+    hipLaunchKernelGGL((gemm_wide_kernel<BITS, CM>), grid, dim3(kThreads), kWideLdsBytes, st, x,
+                       codes, scales, zeros, (int)m, (int)n, (int)k, y);
+    return hipGetLastError();
   }
+  const hipError_t attr = set_lds<&gemm_kernel<BITS, CM>>(kLdsBytes);
+  if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_kernel<BITS, CM>), grid, dim3(kThreads), kLdsBytes, st, x, codes, scales,
                      zeros, (int)m, (int)n, (int)k, y);
@@ -336,6 +552,15 @@ hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const void *scale
 }  // namespace
 
 size_t gemm_workspace(int64_t, int64_t, int64_t, int) { return 0; }
+
+#ifndef SLQ_GEMM_WIDE_MIN_TILES
+#define SLQ_GEMM_WIDE_MIN_TILES 256
+#endif
+// Wide tiles hold one workgroup per CU, so they need a grid that fills the
+// chip; smaller products keep the 128-row tiles (two workgroups per CU).
+bool gemm_wide(int64_t m, int64_t n) {
+  return ((n + kWideBN - 1) / kWideBN) * ((m + kWideBM - 1) / kWideBM) >= SLQ_GEMM_WIDE_MIN_TILES;
+}
 
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const void *scales,
                        const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,

@@ -41,6 +41,7 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const void *sca
 
 // gemm.hip (prefill, m > 64)
 size_t gemm_workspace(int64_t m, int64_t n, int64_t k, int bits);
+bool gemm_wide(int64_t m, int64_t n);   // true: gemm_wide_kernel serves (m, n)
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const void *scales,
                        const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,
                        int bits, float *y, void *ws, hipStream_t s);

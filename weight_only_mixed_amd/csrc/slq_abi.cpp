@@ -188,7 +188,8 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
       snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s, %d, %s>", w->bits, p.mt,
                p.nt, p.b, p.mv ? "true" : "false", p.xd ? "true" : "false", p.wv, cm);
   } else {
-    snprintf(buf, sizeof buf, "slq::gemm_kernel<%d, %s>", w->bits,
+    snprintf(buf, sizeof buf, "slq::%s<%d, %s>",
+             slq::gemm_wide(m, w->n) ? "gemm_wide_kernel" : "gemm_kernel", w->bits,
              w->meta == SLQ_META_COMPACT ? "true" : "false");
   }
   return buf;
