@@ -148,12 +148,15 @@ size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w);
  *      aligned, ZERO-FILLED before its first use.  Its first 64 KiB hold
  *      split-K tickets that every completed call leaves at zero, so one buffer
  *      (of the largest size needed) serves any sequence of calls on one
- *      stream; calls that overlap in time must not share it.  May be NULL when
- *      the size is 0.
+ *      stream; calls that overlap in time must not share it.  Split-K partial
+ *      sums (decode, and prefill grids too small to fill the chip) follow the
+ *      tickets and are overwritten by every call.  May be NULL when the size
+ *      is 0.
  * Accumulation is fp32.  m <= 64 runs the decode kernel (exact integer
  * (q - z), per-group scale in fp32); m > 64 runs the prefill kernel (w_hat
- * rounded to bf16 tiles in LDS, bf16 MFMA).  Both stay within
- * |y - y_exact| <= 1e-2 * sum_k |x||w_hat|.
+ * rounded to bf16 in registers, activations staged in LDS, bf16 MFMA).
+ * Both stay within |y - y_exact| <= 1e-2 * sum_k |x||w_hat|; split-K sums
+ * are taken in a fixed order, so repeated calls are bit-identical.
  */
 slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t m,
                             float *y, void *workspace, slq_stream stream);

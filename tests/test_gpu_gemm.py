@@ -78,6 +78,28 @@ def test_prefill_wide_tiles_ragged(bits):
 
 
 @pytest.mark.parametrize("bits", BITS)
+def test_prefill_split_k(bits):
+    """Grids of fewer than 256 wide tiles with m >= 1024 split k across
+    workgroups (partial tiles in the workspace, summed in split order):
+    m*n divisible by 4 and not, uneven last split (k = 640: 10 steps in
+    splits of 4, 4, 2), ragged edges.  Every output against the oracle, and
+    bit-identical results across calls."""
+    for (m, n, k) in [(1100, 700, 640), (1025, 301, 384), (2048, 96, 256)]:
+        say(f"prefill split bits={bits} m={m} n={n} k={k}")
+        W = S.skewed_weights(n, k, 13 * bits + n, row_offset_std=0.005)
+        x = S.activations_bf16(m, k, 3 * m + bits)
+        pw = slq.slq_quantize_pack(gpu(W), bits)
+        assert slq.kernel_name(m, pw).startswith("slq::gemm_wide_kernel")
+        assert slq.gemm_workspace_bytes(m, pw) > 65536
+        y = slq.slq_dequant_gemm(x_gpu(x), pw)
+        y2 = slq.slq_dequant_gemm(x_gpu(x), pw)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        yr, br, _ = full_ref(W, bits, x)
+        assert_gemm_close(y.cpu().numpy(), yr, br, what=f"split b{bits} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("bits", BITS)
 def test_exact_pins(bits):
     """One-hot activations give w_hat exactly (decode path); zero rows give 0;
     identical activation rows give identical outputs."""

@@ -22,6 +22,8 @@
 //    are assigned so that a lane's 8 slots of the 4 MFMA steps of a k step
 //    are its chunk's 32 consecutive codes; the A operands read the matching
 //    activations from LDS.
+#include <algorithm>
+
 #include "launch.h"
 #include "slq_device.h"
 
@@ -334,6 +336,9 @@ constexpr int kWideBM = 32 * kWideMT;       // 256
 constexpr int kWideBN = 256;
 constexpr int kWideBuf = kWideBM * kPitch;  // bf16 elements per LDS buffer
 constexpr size_t kWideLdsBytes = (size_t)3 * kWideBuf * 2;
+// Split-k partial tiles start past the workspace's first 64 KiB, which hold
+// the decode path's split-k tickets (kept zero between calls).
+constexpr size_t kGemmPartOffset = 65536;
 
 // VALU instructions to place after each MFMA (the dequantization of one
 // 8-code B slice per 32-column tile, spread over the 16 MFMAs of a slice).
@@ -346,7 +351,7 @@ template <int BITS, bool CM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
     const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    float *__restrict__ y) {
+    int ksteps, float *__restrict__ y, float *__restrict__ part) {
   const MetaRd<BITS, CM> md{scales, zeros};
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_x[];
 
@@ -356,14 +361,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
   const int m0 = blockIdx.y * kWideBM, n0 = blockIdx.x * kWideBN + 64 * wave;
   const int G = K / kGroup;
   const int64_t wpr = (int64_t)K * BITS / 32;
-  const int steps = K / kBK;
+  // split k: this workgroup's k steps [st0, st0 + steps) (an even count >= 2);
+  // with several splits the fp32 partial tile goes to part[blockIdx.z]
+  const int st0 = blockIdx.z * ksteps;
+  const int steps = min(ksteps, K / kBK - st0);
+  float *__restrict__ out = part ? part + (int64_t)blockIdx.z * M * N : y;
 
   // activation staging: thread t copies rows t/2 and t/2 + 128, k half t%2
   const int sr = threadIdx.x >> 1, sh = threadIdx.x & 1;
   const u32x4_t *xsrc[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
-    xsrc[r] = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(m0 + sr + 128 * r, M - 1) * K + 32 * sh);
+    xsrc[r] = reinterpret_cast<const u32x4_t *>(x + (int64_t)min(m0 + sr + 128 * r, M - 1) * K +
+                                                 (int64_t)st0 * kBK + 32 * sh);
   auto load_x = [&](int st, u32x4_t (&v)[2][4]) {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
@@ -379,14 +389,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
     }
   };
 
-  // weights: as in gemm_kernel, column n0 + 32t + c32, chunk 2*st + h of the row
+  // weights: as in gemm_kernel, column n0 + 32t + c32, chunk 2*(st0 + st) + h of the row
   const uint32_t *crow[2];
   int64_t mrow[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n = min(n0 + 32 * t + c32, N - 1);
-    crow[t] = codes + (int64_t)n * wpr + h * BITS;
-    mrow[t] = (int64_t)n * G;
+    crow[t] = codes + (int64_t)n * wpr + (int64_t)st0 * 2 * BITS + h * BITS;
+    mrow[t] = (int64_t)n * G + st0 * kBK / kGroup;
   }
   auto load_w = [&](int st, Chunk<BITS> (&c)[2], float (&sv)[2], uint32_t (&zv)[2]) {
     const int g = (st * kBK) / kGroup;
@@ -516,8 +526,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = m0 + 32 * i + 8 * (e / 4) + 4 * h + (e % 4);
-        if (m < M) y[(int64_t)m * N + n] = acc[i][t][e];
+        if (m < M) out[(int64_t)m * N + n] = acc[i][t][e];
       }
+  }
+}
+
+// y = sum of the split partial tiles, in split order (deterministic).
+template <bool VEC>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float *__restrict__ part,
+                                                               int64_t mn, int split,
+                                                               float *__restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC ? 4 : 1);
+  if (i >= mn) return;
+  if constexpr (VEC) {   // mn % 4 == 0: every split's partial is 16-byte aligned
+    float4 acc = *reinterpret_cast<const float4 *>(part + i);
+    for (int z = 1; z < split; ++z) {
+      const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)z * mn + i);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *reinterpret_cast<float4 *>(y + i) = acc;
+  } else {
+    float acc = part[i];
+    for (int z = 1; z < split; ++z) acc += part[(int64_t)z * mn + i];
+    y[i] = acc;
   }
 }
 
@@ -531,14 +565,26 @@ hipError_t set_lds(size_t bytes) {
 
 template <int BITS, bool CM>
 hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
-                     const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
+                     const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      hipStream_t st) {
-  if (gemm_wide(m, n)) {
+  const GemmPlan plan = gemm_plan(m, n, k);
+  if (plan.wide) {
     const hipError_t attr = set_lds<&gemm_wide_kernel<BITS, CM>>(kWideLdsBytes);
     if (attr != hipSuccess) return attr;
-    const dim3 grid((unsigned)((n + kWideBN - 1) / kWideBN), (unsigned)((m + kWideBM - 1) / kWideBM));
+    float *part = plan.split > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + kGemmPartOffset)
+                                 : nullptr;
+    const dim3 grid((unsigned)((n + kWideBN - 1) / kWideBN), (unsigned)((m + kWideBM - 1) / kWideBM),
+                    (unsigned)plan.split);
     hipLaunchKernelGGL((gemm_wide_kernel<BITS, CM>), grid, dim3(kThreads), kWideLdsBytes, st, x,
-                       codes, scales, zeros, (int)m, (int)n, (int)k, y);
+                       codes, scales, zeros, (int)m, (int)n, (int)k, plan.ksteps, y, part);
+    if (plan.split == 1) return hipGetLastError();
+    const int64_t mn = m * n;
+    if (mn % 4 == 0)
+      hipLaunchKernelGGL((gemm_split_reduce_kernel<true>), dim3((unsigned)((mn / 4 + 255) / 256)),
+                         dim3(256), 0, st, part, mn, plan.split, y);
+    else
+      hipLaunchKernelGGL((gemm_split_reduce_kernel<false>), dim3((unsigned)((mn + 255) / 256)),
+                         dim3(256), 0, st, part, mn, plan.split, y);
     return hipGetLastError();
   }
   const hipError_t attr = set_lds<&gemm_kernel<BITS, CM>>(kLdsBytes);
@@ -551,24 +597,52 @@ hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const void *scale
 
 }  // namespace
 
-size_t gemm_workspace(int64_t, int64_t, int64_t, int) { return 0; }
-
 #ifndef SLQ_GEMM_WIDE_MIN_TILES
 #define SLQ_GEMM_WIDE_MIN_TILES 256
 #endif
+#ifndef SLQ_GEMM_SPLIT_MIN_M
+#define SLQ_GEMM_SPLIT_MIN_M 1024
+#endif
+#ifndef SLQ_GEMM_MAX_SPLIT
+#define SLQ_GEMM_MAX_SPLIT 8
+#endif
 // Wide tiles hold one workgroup per CU, so they need a grid that fills the
-// chip; smaller products keep the 128-row tiles (two workgroups per CU).
-bool gemm_wide(int64_t m, int64_t n) {
-  return ((n + kWideBN - 1) / kWideBN) * ((m + kWideBM - 1) / kWideBM) >= SLQ_GEMM_WIDE_MIN_TILES;
+// chip.  Smaller grids with many rows split k over the grid's z dimension
+// (fp32 partial tiles in the workspace, then one in-order sum); the rest keep
+// the 128-row tiles (two workgroups per CU).
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k) {
+  GemmPlan p{false, 1, 0};
+  const int64_t tiles = ((n + kWideBN - 1) / kWideBN) * ((m + kWideBM - 1) / kWideBM);
+  const int64_t steps = k / kBK;
+  if (tiles >= SLQ_GEMM_WIDE_MIN_TILES) {
+    p.wide = true;
+    p.ksteps = (int)steps;
+    return p;
+  }
+  if (m < SLQ_GEMM_SPLIT_MIN_M || steps < 4) return p;
+  int64_t split = std::min<int64_t>({(int64_t)SLQ_GEMM_MAX_SPLIT,
+                                     (SLQ_GEMM_WIDE_MIN_TILES + tiles - 1) / tiles, steps / 2});
+  const int64_t ksteps = 2 * ((steps + 2 * split - 1) / (2 * split));   // even, >= 2
+  split = (steps + ksteps - 1) / ksteps;                                // no empty split
+  if (split < 2) return p;
+  p.wide = true;
+  p.split = (int)split;
+  p.ksteps = (int)ksteps;
+  return p;
+}
+
+size_t gemm_workspace(int64_t m, int64_t n, int64_t k, int) {
+  const GemmPlan p = gemm_plan(m, n, k);
+  return p.split > 1 ? kGemmPartOffset + (size_t)p.split * m * n * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const void *scales,
                        const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,
-                       int bits, float *y, void *, hipStream_t s) {
+                       int bits, float *y, void *ws, hipStream_t s) {
 #define SLQ_GEMM_BITS(B_)                                                        \
   case B_:                                                                       \
-    return compact ? gemm_bits<B_, true>(x, codes, scales, zeros, m, n, k, y, s) \
-                   : gemm_bits<B_, false>(x, codes, scales, zeros, m, n, k, y, s);
+    return compact ? gemm_bits<B_, true>(x, codes, scales, zeros, m, n, k, y, ws, s) \
+                   : gemm_bits<B_, false>(x, codes, scales, zeros, m, n, k, y, ws, s);
   switch (bits) {
     SLQ_GEMM_BITS(2)
     SLQ_GEMM_BITS(3)

@@ -41,7 +41,12 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *codes, const void *sca
 
 // gemm.hip (prefill, m > 64)
 size_t gemm_workspace(int64_t m, int64_t n, int64_t k, int bits);
-bool gemm_wide(int64_t m, int64_t n);   // true: gemm_wide_kernel serves (m, n)
+struct GemmPlan {
+  bool wide;    // gemm_wide_kernel (256 x 256 tiles) rather than gemm_kernel
+  int split;    // k splits (partial tiles in the workspace, summed in order)
+  int ksteps;   // 64-wide k steps per split
+};
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm(const uint16_t *x, const uint32_t *codes, const void *scales,
                        const uint8_t *zeros, bool compact, int64_t m, int64_t n, int64_t k,
                        int bits, float *y, void *ws, hipStream_t s);

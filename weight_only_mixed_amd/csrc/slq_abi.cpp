@@ -189,7 +189,7 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
                p.nt, p.b, p.mv ? "true" : "false", p.xd ? "true" : "false", p.wv, cm);
   } else {
     snprintf(buf, sizeof buf, "slq::%s<%d, %s>",
-             slq::gemm_wide(m, w->n) ? "gemm_wide_kernel" : "gemm_kernel", w->bits,
+             slq::gemm_plan(m, w->n, w->k).wide ? "gemm_wide_kernel" : "gemm_kernel", w->bits,
              w->meta == SLQ_META_COMPACT ? "true" : "false");
   }
   return buf;
