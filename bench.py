@@ -99,6 +99,10 @@ class Timer:
         self.ms = self.a.elapsed_time(self.b)
 
 
+# prefill GEMM points: (label, Llama-3.3-70B projection, weight seed index)
+PREFILL_SHAPES = [("q/o", "q", 1), ("k/v", "k", 2), ("gate/up", "gate", 4), ("down", "down", 6)]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +115,9 @@ def main():
     ap.add_argument("--pmc", default=None, metavar="KERNEL",
                     help="counter mode: 5 copies of 256 MiB (known bytes), then 10 passes over the "
                          "sweep points that launch KERNEL; prints what ran and exits")
+    ap.add_argument("--pmc-prefill", action="store_true",
+                    help="counter mode: 3 launches of each prefill GEMM point (M=4096, "
+                         "Llama-3.3-70B shapes, bits 4 and 6); prints what ran and exits")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -136,6 +143,27 @@ def main():
 
     def x_dev(bits16):
         return to_dev(bits16.view(np.int16)).view(torch.bfloat16)
+
+    if args.pmc_prefill:
+        x8 = x_dev(S.activations_bf16(4096, 8192, S.seed_for(4) + 1))
+        x28 = x_dev(S.activations_bf16(4096, 28672, S.seed_for(4) + 2))
+        ran = []
+        for label, pname, i in PREFILL_SHAPES:
+            n, k = S.LLAMA33_70B_PROJ[pname]
+            Wd = to_dev(S.skewed_weights(n, k, S.seed_for(4, 0, i), row_offset_std=0.005))
+            xx = x8 if k == 8192 else x28
+            y = torch.empty((4096, n), dtype=torch.float32, device=dev)
+            for bits in (4, 6):
+                pw = slq.slq_quantize_pack(Wd, bits)
+                for _ in range(3):
+                    slq.slq_dequant_gemm(xx, pw, y=y)
+                ran.append({"shape": label, "n": n, "k": k, "bits": bits,
+                            "kernel": slq.kernel_name(4096, pw), "flop_per_launch": 2 * 4096 * n * k})
+                del pw
+            del Wd, y
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_prefill": ran, "launches_each": 3}))
+        return
 
     # ---------------- headline: decode sweep ----------------
     log("bench: generating sweep weights")
@@ -336,9 +364,8 @@ def main():
         log("bench: prefill GEMM (Llama-3.3-70B shapes, M=4096)")
         x8 = x_dev(S.activations_bf16(4096, 8192, S.seed_for(4) + 1))
         x28 = x_dev(S.activations_bf16(4096, 28672, S.seed_for(4) + 2))
-        gshapes = [("q/o", "q", 1), ("k/v", "k", 2), ("gate/up", "gate", 4), ("down", "down", 6)]
         tot_f, tot_ms, per = 0, 0.0, []
-        for label, pname, i in gshapes:
+        for label, pname, i in PREFILL_SHAPES:
             n, k = S.LLAMA33_70B_PROJ[pname]
             Wd = to_dev(S.skewed_weights(n, k, S.seed_for(4, 0, i), row_offset_std=0.005))
             xx = x8 if k == 8192 else x28
