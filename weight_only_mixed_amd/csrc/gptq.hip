@@ -286,51 +286,59 @@ __device__ __forceinline__ float clampq(float v, float maxq) {
   return v > maxq ? maxq : v;
 }
 
-template <int BITS>
-__device__ __forceinline__ void pack_group(const float (&w)[kGroup], uint32_t *__restrict__ dst) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t out[BITS];
-#pragma unroll
-    for (int i = 0; i < BITS; ++i) out[i] = 0u;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t q = (uint32_t)w[32 * c + j];
-      const int bit = j * BITS, wd = bit / 32, o = bit % 32;
-      out[wd] |= q << o;
-      if (o + BITS > 32) out[wd + 1] |= q >> (32 - o);
-    }
-#pragma unroll
-    for (int i = 0; i < BITS; ++i) dst[c * BITS + i] = out[i];
-  }
-}
+// Group g (columns i1 = 128 g ...): a team of kTeam lanes per weight row,
+// lane t of a team holding the group's columns [kPer t, kPer t + kPer) in
+// registers; the group's block of U sits in LDS.  Step i: the owner of column
+// i quantizes it, its error e_i goes to the team in one cross-lane read, and
+// every later column j takes w_j = fma(-e_i, U[i][j], w_j), the same operations
+// in the same order as one lane doing the whole row.
+constexpr int kTeam = 16;
+constexpr int kPer = kGroup / kTeam;   // columns per lane
+constexpr int kRowsPerBlock = kThr / kTeam;
 
-// Group g (columns i1 = 128 g ...): one lane per weight row.
 template <int BITS>
 __global__ __launch_bounds__(kThr) void gptq_group_kernel(
     float *__restrict__ Wk, const float *__restrict__ Uf, int64_t n, int64_t k, int64_t g,
     uint32_t *__restrict__ codes, float *__restrict__ scales, uint8_t *__restrict__ zeros,
     float *__restrict__ err) {
-  const int64_t r = (int64_t)blockIdx.x * kThr + threadIdx.x;
-  if (r >= n) return;
-  const float maxq = (float)((1 << BITS) - 1);
+  __shared__ __attribute__((aligned(16))) float ub[kGroup][kGroup];   // U block of the group
+  __shared__ uint8_t qs[kRowsPerBlock][kGroup];                       // codes, for packing
   const int64_t i1 = g * kGroup;
-  float w[kGroup];
-  const float4 *src = reinterpret_cast<const float4 *>(Wk + r * k + i1);
-#pragma unroll
-  for (int i = 0; i < kGroup / 4; ++i) {
-    const float4 v = src[i];
-    w[4 * i] = v.x;
-    w[4 * i + 1] = v.y;
-    w[4 * i + 2] = v.z;
-    w[4 * i + 3] = v.w;
+  for (int e = threadIdx.x; e < kGroup * kGroup / 4; e += kThr) {
+    const int row = e / (kGroup / 4), c4 = e % (kGroup / 4);
+    reinterpret_cast<float4 *>(&ub[row][0])[c4] =
+        reinterpret_cast<const float4 *>(Uf + (i1 + row) * k + i1)[c4];
   }
-  // the plain quantizer's steps on the group's current weights
+  const int t = threadIdx.x % kTeam, tr = threadIdx.x / kTeam;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + tr;
+  const bool live = r < n;
+  const int64_t rr = live ? r : n - 1;   // a team past the last row works on a valid row, stores nothing
+  const float maxq = (float)((1 << BITS) - 1);
+  float w[kPer];
+  {
+    const float4 *src = reinterpret_cast<const float4 *>(Wk + rr * k + i1 + kPer * t);
+#pragma unroll
+    for (int i = 0; i < kPer / 4; ++i) {
+      const float4 v = src[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  }
+  // the plain quantizer's steps on the group's current weights (min and max
+  // over the team: exact in any order)
   float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kGroup; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     lo = w[i] < lo ? w[i] : lo;
     hi = w[i] > hi ? w[i] : hi;
+  }
+#pragma unroll
+  for (int o = kTeam / 2; o > 0; o /= 2) {
+    const float l2 = __shfl_xor(lo, o, kTeam), h2 = __shfl_xor(hi, o, kTeam);
+    lo = l2 < lo ? l2 : lo;
+    hi = h2 > hi ? h2 : hi;
   }
   float s = (hi - lo) / maxq, zf;
   if (s == 0.0f) {
@@ -339,22 +347,65 @@ __global__ __launch_bounds__(kThr) void gptq_group_kernel(
   } else {
     zf = clampq(rintf((-lo) / s), maxq);
   }
-  const float *ub = Uf + i1 * k + i1;   // U block of the group (wave-uniform reads)
-  float *er = err + r * kGroup;
+  __syncthreads();   // U block staged
+  float ev[kPer], qv[kPer];
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) {
-    const float q = clampq(rintf(w[i] / s) + zf, maxq);
+    const int owner = i / kPer, li = i % kPer;
+    // every lane evaluates its own column li; the owner's value is the one used
+    const float wi = w[li];
+    const float q = clampq(rintf(wi / s) + zf, maxq);
     const float what = (float)((int)q - (int)zf) * s;
-    const float e = (w[i] - what) / ub[i * k + i];
-    er[i] = e;
+    const float ei = (wi - what) / ub[i][i];
+    const float e = __shfl(ei, owner, kTeam);
+    if (t == owner) {
+      ev[li] = ei;
+      qv[li] = q;
+    }
+    if (i + 1 < kGroup) {
+      const float4 u0 = *reinterpret_cast<const float4 *>(&ub[i][kPer * t]);
+      const float4 u1 = *reinterpret_cast<const float4 *>(&ub[i][kPer * t + 4]);
+      const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-    for (int j = i + 1; j < kGroup; ++j) w[j] = fmaf(-e, ub[i * k + j], w[j]);
-    w[i] = q;
+      for (int jj = 0; jj < kPer; ++jj)
+        if (kPer * t + jj > i) w[jj] = fmaf(-e, u[jj], w[jj]);
+    }
   }
-  const int64_t G = k / kGroup;
-  pack_group<BITS>(w, codes + r * (k * BITS / 32) + g * 4 * BITS);
-  scales[r * G + g] = s;
-  zeros[r * G + g] = (uint8_t)(int)zf;
+  static_assert(kPer == 8, "the U row slice is read as two float4");
+  // errors and codes of this lane's columns
+  if (live) {
+    float4 *er = reinterpret_cast<float4 *>(err + rr * kGroup + kPer * t);
+    er[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
+    er[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < kPer; ++jj) qs[tr][kPer * t + jj] = (uint8_t)(int)qv[jj];
+  __syncthreads();
+  // pack: lane t writes words t and t + kTeam of the row's 4 * BITS words
+  // (32-code chunks of BITS words, code j of a chunk at bit j * BITS)
+  if (live) {
+    uint32_t *dst = codes + rr * (k * BITS / 32) + g * 4 * BITS;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int W = t + kTeam * h;
+      if (W >= 4 * BITS) continue;
+      const int c = W / BITS, wd = W % BITS;
+      uint32_t out = 0u;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int lo_bit = j * BITS - 32 * wd;
+        if (lo_bit <= -BITS || lo_bit >= 32) continue;
+        const uint32_t q = qs[tr][32 * c + j];
+        out |= lo_bit >= 0 ? q << lo_bit : q >> (-lo_bit);
+      }
+      dst[W] = out;
+    }
+    if (t == 0) {
+      const int64_t G = k / kGroup;
+      scales[rr * G + g] = s;
+      zeros[rr * G + g] = (uint8_t)(int)zf;
+    }
+  }
 }
 
 // Wk[:, c] -= sum_p err[:, p] U[i1 + p][c] for the columns after group g
@@ -399,7 +450,7 @@ template <int BITS>
 hipError_t group_launch(float *Wk, const float *Uf, int64_t n, int64_t k, int64_t g,
                         uint32_t *codes, float *scales, uint8_t *zeros, float *err,
                         hipStream_t s) {
-  hipLaunchKernelGGL((gptq_group_kernel<BITS>), dim3((unsigned)((n + kThr - 1) / kThr)),
+  hipLaunchKernelGGL((gptq_group_kernel<BITS>), dim3((unsigned)((n + kRowsPerBlock - 1) / kRowsPerBlock)),
                      dim3(kThr), 0, s, Wk, Uf, n, k, g, codes, scales, zeros, err);
   return hipGetLastError();
 }
