@@ -114,26 +114,38 @@ __global__ __launch_bounds__(kNb) void potf2_kernel(double *__restrict__ A, int6
   for (int c = 0; c < kNb; ++c) dst[c] = c <= i ? r[c] : 0.0;
 }
 
-// panel below the diagonal block: rows solve x L11^T = a (one lane per row)
+// panel below the diagonal block: rows solve x L11^T = a.  A team of kTeamT
+// lanes per row, lane t holding columns [kPerT t, kPerT t + kPerT): step c, the
+// owner of column c divides by l_cc and the team takes x_c in one cross-lane
+// read; every later column subtracts x_c l[c'][c].  Each x_c' sees the same
+// operations in the same order as a lane solving its row alone.
+constexpr int kTeamT = 16;
+constexpr int kPerT = kNb / kTeamT;
 __global__ __launch_bounds__(kThr) void trsm_kernel(double *__restrict__ A, int64_t k, int64_t j0) {
   __shared__ double l[kNb][kLdp];
   for (int e = threadIdx.x; e < kNb * kNb; e += kThr)
     l[e / kNb][e % kNb] = A[(j0 + e / kNb) * k + j0 + e % kNb];
   __syncthreads();
-  const int64_t r = j0 + kNb + (int64_t)blockIdx.x * kThr + threadIdx.x;
-  if (r >= k) return;
-  double x[kNb];
+  const int t = threadIdx.x % kTeamT;
+  const int64_t r = j0 + kNb + (int64_t)blockIdx.x * (kThr / kTeamT) + threadIdx.x / kTeamT;
+  const bool live = r < k;
+  const int64_t rr = live ? r : k - 1;   // a row below the block (launched only when rows remain)
+  double x[kPerT];
 #pragma unroll
-  for (int c = 0; c < kNb; ++c) x[c] = A[r * k + j0 + c];
+  for (int c = 0; c < kPerT; ++c) x[c] = A[rr * k + j0 + kPerT * t + c];
 #pragma unroll
   for (int c = 0; c < kNb; ++c) {
-    double s = x[c];
+    const int owner = c / kPerT, lc = c % kPerT;
+    const double xc = __shfl(x[lc] / l[c][c], owner, kTeamT);
+    if (t == owner) x[lc] = xc;
 #pragma unroll
-    for (int p = 0; p < c; ++p) s -= x[p] * l[c][p];
-    x[c] = s / l[c][c];
+    for (int jj = 0; jj < kPerT; ++jj)
+      if (kPerT * t + jj > c) x[jj] = fma(-xc, l[kPerT * t + jj][c], x[jj]);
   }
+  if (live) {
 #pragma unroll
-  for (int c = 0; c < kNb; ++c) A[r * k + j0 + c] = x[c];
+    for (int c = 0; c < kPerT; ++c) A[rr * k + j0 + kPerT * t + c] = x[c];
+  }
 }
 
 // C -= P_i P_j^T on the trailing lower tiles, P = A[r0:, j0:j0+64]
@@ -488,8 +500,8 @@ hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int
     hipLaunchKernelGGL(potf2_kernel, dim3(1), dim3(kNb), 0, s, A, k, j0);
     const int64_t rest = k - j0 - kNb;
     if (rest > 0) {
-      hipLaunchKernelGGL(trsm_kernel, dim3((unsigned)((rest + kThr - 1) / kThr)), dim3(kThr), 0,
-                         s, A, k, j0);
+      hipLaunchKernelGGL(trsm_kernel, dim3((unsigned)((rest + kThr / kTeamT - 1) / (kThr / kTeamT))),
+                         dim3(kThr), 0, s, A, k, j0);
       const unsigned t = (unsigned)(rest / kNb);
       hipLaunchKernelGGL(syrk_kernel, dim3(t, t), dim3(kThr), 0, s, A, k, j0);
     }
