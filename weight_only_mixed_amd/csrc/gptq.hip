@@ -420,41 +420,73 @@ __global__ __launch_bounds__(kThr) void gptq_group_kernel(
   }
 }
 
-// Wk[:, c] -= sum_p err[:, p] U[i1 + p][c] for the columns after group g
+// Wk[:, c] -= sum_p err[:, p] U[i1 + p][c] for the columns after group g:
+// 128 x 128 output tiles, 8 x 8 per thread, the 128 inner terms in two LDS
+// halves (errors transposed to [p][row]); each output accumulates its terms in
+// p order.
+constexpr int kUpT = 128, kUpP = 64;
 __global__ __launch_bounds__(kThr) void gptq_update_kernel(float *__restrict__ Wk,
                                                            const float *__restrict__ Uf,
                                                            const float *__restrict__ err,
                                                            int64_t n, int64_t k, int64_t g) {
-  __shared__ float te[64][kGroup + 1];
-  __shared__ float tu[kGroup][64 + 1];
-  const int64_t i1 = g * kGroup, c0 = i1 + kGroup + (int64_t)blockIdx.y * 64;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  for (int e = threadIdx.x; e < 64 * kGroup; e += kThr) {
-    const int64_t rr = r0 + e / kGroup;
-    te[e / kGroup][e % kGroup] = rr < n ? err[rr * kGroup + e % kGroup] : 0.0f;
-  }
-  for (int e = threadIdx.x; e < kGroup * 64; e += kThr)
-    tu[e / 64][e % 64] = Uf[(i1 + e / 64) * k + c0 + e % 64];
-  __syncthreads();
+  __shared__ __attribute__((aligned(16))) float ta[kUpP][kUpT];   // err^T half: [p][row]
+  __shared__ __attribute__((aligned(16))) float tb[kUpP][kUpT];   // U half: [p][column]
+  const int64_t i1 = g * kGroup, c0 = i1 + kGroup + (int64_t)blockIdx.y * kUpT;
+  const int64_t r0 = (int64_t)blockIdx.x * kUpT;
   const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
-  float acc[4][4] = {};
-  for (int p = 0; p < kGroup; ++p) {
-    float av[4], bv[4];
+  float acc[8][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) av[u] = te[ty * 4 + u][p];
+  for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) bv[v] = tu[p][tx * 4 + v];
+    for (int v = 0; v < 8; ++v) acc[u][v] = 0.0f;
+  for (int h = 0; h < kGroup / kUpP; ++h) {
+    if (h) __syncthreads();   // the previous half is consumed
+    // errors: thread e takes row e % 128 and terms 4 (e / 128) .. + 3
+    for (int e = threadIdx.x; e < kUpT * kUpP / 4; e += kThr) {
+      const int rr = e % kUpT, p4 = e / kUpT;
+      const int64_t row = r0 + rr;
+      const float4 v = row < n ? *reinterpret_cast<const float4 *>(err + row * kGroup + h * kUpP + 4 * p4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      ta[4 * p4 + 0][rr] = v.x;
+      ta[4 * p4 + 1][rr] = v.y;
+      ta[4 * p4 + 2][rr] = v.z;
+      ta[4 * p4 + 3][rr] = v.w;
+    }
+    // U rows i1 + 64 h + p, columns c0 .. c0 + 127 (the later columns come in whole tiles)
+    for (int e = threadIdx.x; e < kUpP * kUpT / 4; e += kThr) {
+      const int pp = e / (kUpT / 4), c4 = e % (kUpT / 4);
+      *reinterpret_cast<float4 *>(&tb[pp][4 * c4]) =
+          *reinterpret_cast<const float4 *>(Uf + (i1 + h * kUpP + pp) * k + c0 + 4 * c4);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int pp = 0; pp < kUpP; ++pp) {
+      const float4 a0 = *reinterpret_cast<const float4 *>(&ta[pp][8 * ty]);
+      const float4 a1 = *reinterpret_cast<const float4 *>(&ta[pp][8 * ty + 4]);
+      const float4 b0 = *reinterpret_cast<const float4 *>(&tb[pp][8 * tx]);
+      const float4 b1 = *reinterpret_cast<const float4 *>(&tb[pp][8 * tx + 4]);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+        for (int v = 0; v < 8; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+    }
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t rr = r0 + ty * 4 + u;
-    if (rr >= n) continue;
+  for (int u = 0; u < 8; ++u) {
+    const int64_t row = r0 + 8 * ty + u;
+    if (row >= n) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) Wk[rr * k + c0 + tx * 4 + v] -= acc[u][v];
+    for (int q = 0; q < 2; ++q) {
+      float4 *dst = reinterpret_cast<float4 *>(Wk + row * k + c0 + 8 * tx + 4 * q);
+      float4 w = *dst;
+      w.x -= acc[u][4 * q];
+      w.y -= acc[u][4 * q + 1];
+      w.z -= acc[u][4 * q + 2];
+      w.w -= acc[u][4 * q + 3];
+      *dst = w;
+    }
   }
 }
 
@@ -534,8 +566,8 @@ hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int
     const int64_t later = k - (g + 1) * kGroup;
     if (later > 0) {
       hipLaunchKernelGGL(gptq_update_kernel,
-                         dim3((unsigned)((n + 63) / 64), (unsigned)(later / 64)), dim3(kThr), 0, s,
-                         Wk, Uf, err, n, k, g);
+                         dim3((unsigned)((n + kUpT - 1) / kUpT), (unsigned)(later / kUpT)), dim3(kThr),
+                         0, s, Wk, Uf, err, n, k, g);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
