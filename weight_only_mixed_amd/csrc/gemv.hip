@@ -944,6 +944,17 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
       g = k_block(w);
     }
     if (w > kWaves && nb * std::max<int64_t>(1, (G + g - 1) / g) <= kWvBlocks) wv = w;
+    if (wv == kWaves && p.xd) {
+      // Per-lane activation loads on k-blocks too short for 8 waves with
+      // 4-group metadata units: 8 waves on the same k-blocks with metadata
+      // staged per group (two waves per SIMD instead of one).
+      const int64_t g2 = std::max<int64_t>(1, (G + ks - 1) / ks);
+      if (g2 >= 8 && g2 <= gw_max) {
+        wv = 8;
+        gw_wide = g2;
+        p.mv = false;
+      }
+    }
     if (wv == kWaves && !p.xd) {
       // Small grids whose k-blocks hold too few 4-group metadata units for
       // wide workgroups: wide workgroups on fewer (or no) k splits instead,
