@@ -22,6 +22,8 @@
 // Every reduction has a fixed shape, so repeated calls are bit-identical.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "slq_device.h"
 
@@ -370,14 +372,9 @@ __device__ uint64_t kth_key(const uint64_t (&key)[PER], int k) {
   return prefix;
 }
 
-// Cuts one wave's candidate buffer (first `count` entries) back to its k
-// largest keys, stored at the front in lane order.  Returns the new count;
-// `kth` is the smallest key kept when the buffer held more than k, else 0.
-template <int CAP>
-__device__ int wave_keep(uint64_t *ck, float *cb, int count, int k, uint64_t &kth) {
-  kth = 0;
-  if (count <= k) return count;
-  constexpr int PER = CAP / kWave;
+// wave_keep with the buffer's first `count` entries in PER registers per lane.
+template <int PER>
+__device__ int keep_in_regs(uint64_t *ck, float *cb, int count, int k, uint64_t &kth) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t below = (1ull << lane) - 1;
   uint64_t key[PER];
@@ -402,6 +399,23 @@ __device__ int wave_keep(uint64_t *ck, float *cb, int count, int k, uint64_t &kt
     base += __popcll(m);
   }
   return k;
+}
+
+// Cuts one wave's candidate buffer (first `count` entries) back to its k
+// largest keys, stored at the front in lane order.  Returns the new count;
+// `kth` is the smallest key kept when the buffer held more than k, else 0.
+template <int CAP>
+__device__ int wave_keep(uint64_t *ck, float *cb, int count, int k, uint64_t &kth) {
+  kth = 0;
+  if (count <= k) return count;
+  // as few registers per lane as hold the entries: the selection costs one
+  // ballot per register and key bit
+  if (count <= kWave) return keep_in_regs<1>(ck, cb, count, k, kth);
+  if constexpr (CAP >= 2 * kWave)
+    if (count <= 2 * kWave) return keep_in_regs<2>(ck, cb, count, k, kth);
+  if constexpr (CAP >= 4 * kWave)
+    if (count <= 4 * kWave) return keep_in_regs<4>(ck, cb, count, k, kth);
+  return keep_in_regs<CAP / kWave>(ck, cb, count, k, kth);
 }
 
 // Pass 1 of the top-K metrics, per (chunk, row): the chunk's softmax partials
@@ -604,8 +618,10 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
       d += p * (lp - lq);
     };
     double e = 0.0, d = 0.0;
-    constexpr int kPer = 16;   // lists of up to 1024 entries stay in registers
-    if (ne <= (int64_t)kPer * kWave) {
+    // lists of up to 1024 entries stay in registers, as few per lane as fit
+    // (the selection costs one ballot per register and key bit)
+    auto in_regs = [&](auto per_tag) {
+      constexpr int kPer = decltype(per_tag)::value;
       uint64_t key[kPer];
 #pragma unroll
       for (int r = 0; r < kPer; ++r) {
@@ -616,6 +632,17 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
 #pragma unroll
       for (int r = 0; r < kPer; ++r)
         if (key[r] >= thr) term(key[r], rb[at((int64_t)r * kWave + lane)], e, d);
+    };
+    if (ne <= kWave) {
+      in_regs(std::integral_constant<int, 1>{});
+    } else if (ne <= 2 * kWave) {
+      in_regs(std::integral_constant<int, 2>{});
+    } else if (ne <= 4 * kWave) {
+      in_regs(std::integral_constant<int, 4>{});
+    } else if (ne <= 8 * kWave) {
+      in_regs(std::integral_constant<int, 8>{});
+    } else if (ne <= 16 * kWave) {
+      in_regs(std::integral_constant<int, 16>{});
     } else {   // long lists (few rows, long vocabulary): count from memory
       uint64_t prefix = 0;
       for (int bit = 63; bit >= 0; --bit) {
