@@ -22,6 +22,12 @@
 //    are assigned so that a lane's 8 slots of the 4 MFMA steps of a k step
 //    are its chunk's 32 consecutive codes; the A operands read the matching
 //    activations from LDS.
+//
+// Two kernels share this scheme.  gemm_wide_kernel (256 x 256 tiles, one
+// wavefront per SIMD, each dequantized operand feeding 8 MFMAs) serves grids
+// that fill the chip, and smaller grids with m >= 1024 by splitting k over the
+// grid's z dimension (partial tiles summed in order by a second kernel);
+// gemm_kernel (128 x 256 tiles, two wavefronts per SIMD) serves the rest.
 #include <algorithm>
 
 #include "launch.h"
