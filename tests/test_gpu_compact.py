@@ -73,6 +73,37 @@ def test_matmul_paths(bits):
             assert_gemm_close(y, yr, br, what=f"compact b{bits} m{m} {n}x{k}")
 
 
+@pytest.mark.parametrize("bits", BITS)
+def test_prefill_wide_and_split_compact(bits):
+    """The wide-tile prefill kernel and its split-k form reading the compact
+    layout: split k compared in full, the wide grid on sampled outputs plus its
+    whole last row and column."""
+    n, k, m = 300, 640, 1100
+    W = S.skewed_weights(n, k, 17 * bits, row_offset_std=0.005)
+    pw = pack_compact(W, bits)
+    assert slq.kernel_name(m, pw).startswith("slq::gemm_wide_kernel") and slq.gemm_workspace_bytes(m, pw) > 0
+    q, s16, zp = oracle_compact(W, bits)
+    wh = oracle.dequantize_compact(q, s16, zp, bits)
+    x = S.activations_bf16(m, k, 5 * bits)
+    y = slq.slq_dequant_gemm(x_gpu(x), pw).cpu().numpy()
+    yr, br = oracle.gemm(x, wh)
+    assert_gemm_close(y, yr, br, what=f"compact split b{bits}")
+    n, k, m = 16130, 256, 4095
+    W = S.skewed_weights(n, k, 19 * bits, row_offset_std=0.005)
+    pw = pack_compact(W, bits)
+    assert slq.kernel_name(m, pw).startswith("slq::gemm_wide_kernel") and slq.gemm_workspace_bytes(m, pw) == 0
+    q, s16, zp = oracle_compact(W, bits)
+    wh = oracle.dequantize_compact(q, s16, zp, bits)
+    x = S.activations_bf16(m, k, 7 * bits)
+    yd = slq.slq_dequant_gemm(x_gpu(x), pw)
+    g = np.random.default_rng(bits)
+    mi = np.concatenate([g.integers(0, m, 2000), np.full(n, m - 1), np.arange(m)]).astype(np.int64)
+    ni = np.concatenate([g.integers(0, n, 2000), np.arange(n), np.full(m, n - 1)]).astype(np.int64)
+    ys = yd[torch.from_numpy(mi).to(yd.device), torch.from_numpy(ni).to(yd.device)].cpu().numpy()
+    yr, br = oracle.gemm_pairs(x, wh, mi, ni)
+    assert_gemm_close(ys, yr, br, what=f"compact wide b{bits}")
+
+
 def test_one_hot_exact_and_zero_rows():
     n, k = 40, 512
     W = S.skewed_weights(n, k, 77)
