@@ -99,6 +99,32 @@ def test_prefill_split_k(bits):
         assert_gemm_close(y.cpu().numpy(), yr, br, what=f"split b{bits} {m}x{n}x{k}")
 
 
+def test_prefill_rows_beyond_one_grid():
+    """More activation rows than one launch grid holds (65535 tiles of 256
+    rows): the rows go in chunks; sampled rows on both sides of the chunk
+    boundary and the last row against the oracle."""
+    m, n, k, bits = 65535 * 256 + 300, 3, 128, 4
+    W = S.skewed_weights(n, k, 23, row_offset_std=0.005)
+    pw = slq.slq_quantize_pack(gpu(W), bits)
+    assert slq.kernel_name(m, pw).startswith("slq::gemm_wide_kernel")
+    g = torch.Generator(device=DEV).manual_seed(29)
+    x = torch.randn(m, k, device=DEV, generator=g).to(torch.bfloat16)
+    y = slq.slq_dequant_gemm(x, pw)
+    torch.cuda.synchronize()
+    edge = 65535 * 256
+    rows = np.concatenate([np.random.default_rng(31).integers(0, m, 500),
+                           np.arange(edge - 3, edge + 3), [m - 1]]).astype(np.int64)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    xs = x[rows_t].view(torch.int16).cpu().numpy().view(np.uint16)
+    ys = y[rows_t].cpu().numpy()
+    del x, y
+    torch.cuda.empty_cache()
+    mi = np.repeat(np.arange(len(rows)), n).astype(np.int64)
+    ni = np.tile(np.arange(n), len(rows)).astype(np.int64)
+    yr, br = oracle_sampled(W, bits, xs, mi, ni)
+    assert_gemm_close(ys[mi, ni], yr, br, what="prefill rows beyond one grid")
+
+
 @pytest.mark.parametrize("bits", BITS)
 def test_exact_pins(bits):
     """One-hot activations give w_hat exactly (decode path); zero rows give 0;

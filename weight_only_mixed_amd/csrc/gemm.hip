@@ -345,6 +345,7 @@ constexpr size_t kWideLdsBytes = (size_t)3 * kWideBuf * 2;
 // Split-k partial tiles start past the workspace's first 64 KiB, which hold
 // the decode path's split-k tickets (kept zero between calls).
 constexpr size_t kGemmPartOffset = 65536;
+constexpr int64_t kMaxGridY = 65535;   // workgroups along a grid's y dimension
 
 // VALU instructions to place after each MFMA (the dequantization of one
 // 8-code B slice per 32-column tile, spread over the 16 MFMAs of a slice).
@@ -577,13 +578,26 @@ hipError_t gemm_bits(const uint16_t *x, const uint32_t *codes, const void *scale
   if (plan.wide) {
     const hipError_t attr = set_lds<&gemm_wide_kernel<BITS, CM>>(kWideLdsBytes);
     if (attr != hipSuccess) return attr;
-    float *part = plan.split > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + kGemmPartOffset)
-                                 : nullptr;
+    if (plan.split == 1) {
+      // row chunks of at most kMaxGridY tiles (the grid's y limit)
+      for (int64_t r0 = 0; r0 < m; r0 += kMaxGridY * kWideBM) {
+        const int64_t mc = std::min<int64_t>(m - r0, kMaxGridY * kWideBM);
+        const dim3 grid((unsigned)((n + kWideBN - 1) / kWideBN), (unsigned)((mc + kWideBM - 1) / kWideBM));
+        hipLaunchKernelGGL((gemm_wide_kernel<BITS, CM>), grid, dim3(kThreads), kWideLdsBytes, st,
+                           x + r0 * k, codes, scales, zeros, (int)mc, (int)n, (int)k, plan.ksteps,
+                           y + r0 * n, nullptr);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+    // split k: fewer than 256 tiles, so far fewer than kMaxGridY row tiles
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + kGemmPartOffset);
     const dim3 grid((unsigned)((n + kWideBN - 1) / kWideBN), (unsigned)((m + kWideBM - 1) / kWideBM),
                     (unsigned)plan.split);
     hipLaunchKernelGGL((gemm_wide_kernel<BITS, CM>), grid, dim3(kThreads), kWideLdsBytes, st, x,
                        codes, scales, zeros, (int)m, (int)n, (int)k, plan.ksteps, y, part);
-    if (plan.split == 1) return hipGetLastError();
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     const int64_t mn = m * n;
     if (mn % 4 == 0)
       hipLaunchKernelGGL((gemm_split_reduce_kernel<true>), dim3((unsigned)((mn / 4 + 255) / 256)),
