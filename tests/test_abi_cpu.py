@@ -97,6 +97,17 @@ def test_dequant_gemm_validation():
     assert L.slq_dequant_gemm(None, ctypes.byref(w), 0, None, None, None) == slq.SLQ_OK
 
 
+def test_decode_plan_beyond_grid_is_not_supported():
+    """A decode plan whose k splits exceed a launch grid's y limit (65535) is
+    reported as not supported before any HIP call: 4 activation rows over
+    600M-long weight rows need 73,243 splits of 64 groups."""
+    L = slq.lib()
+    G64 = 1 << 36            # fake addresses 64 GiB apart (the codes span 4.8 GB)
+    w = slq.SlqPacked(4, 128, 16, 600_000_000, G64, 2 * G64, 3 * G64)
+    assert L.slq_gemm_workspace_bytes(4, ctypes.byref(w)) == 0
+    assert L.slq_dequant_gemm(4 * G64, ctypes.byref(w), 4, 5 * G64, None, None) == slq.SLQ_ENOTSUP
+
+
 def test_fidelity_and_error_validation():
     L = slq.lib()
     assert L.slq_ear_kl(A, B, 4, 0, C, C + 64, D, E, None) == slq.SLQ_EINVAL       # empty vocab

@@ -880,7 +880,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
     p.gw = (int)gw;
     p.ksplits = (int)((G + gw - 1) / gw);
     p.nblocks = (int)nb;
-    if (p.nblocks > kMaxTicketBlocks && p.ksplits > 1) p.ksplits = 0;
+    if ((p.nblocks > kMaxTicketBlocks && p.ksplits > 1) || p.ksplits > 65535) p.ksplits = 0;
     p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
     return p;
   }
@@ -977,7 +977,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   p.b = (p.xd && p.mt > 1) ? 1 : p.nt == 1 ? kBatchNt1 : p.nt == 2 ? kBatchNt2 : kBatchNt4;
   p.ksplits = (int)std::max<int64_t>(1, (G + p.gw - 1) / p.gw);
   p.nblocks = (int)nb;
-  if (p.nblocks > kMaxTicketBlocks && p.ksplits > 1) p.ksplits = 0;   // not supported
+  if ((p.nblocks > kMaxTicketBlocks && p.ksplits > 1) || p.ksplits > 65535) p.ksplits = 0;   // not supported
   p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
   return p;
 }
