@@ -493,6 +493,14 @@ __global__ __launch_bounds__(kThreads) void topk_stats_kernel(
           online4<false>(vb[u], vb[u], mb, zb, unused, escale);
           mx = fmaxf(mx, fmaxf(fmaxf(va[u].x, va[u].y), fmaxf(va[u].z, va[u].w)));
         }
+      if (theta == -INFINITY) {
+        // First batch: the K-th largest of the lanes' maxima (K distinct
+        // elements) bounds the wave's K-th largest value from below, so it can
+        // serve as the threshold before any offer; lanes without elements
+        // take key 0, which ranks below every element.
+        uint64_t lk[1] = {mx > -INFINITY ? topk_key(mx, (uint32_t)lane) : 0ull};
+        if (__popcll(__ballot(lk[0] != 0ull)) >= k) theta = topk_value(kth_key<1>(lk, k));
+      }
       if (__ballot(mx >= theta)) {   // rare once the threshold has risen
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
