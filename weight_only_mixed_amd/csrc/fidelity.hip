@@ -673,24 +673,28 @@ __global__ __launch_bounds__(kThreads) void topk_rows_kernel(
       d += __shfl_xor(d, o, kWave);
     }
     if (lane == 0) {
-      rowres[row * 4 + 2] = d;
-      rowres[row * 4 + 3] = e;
+      // device-scope stores: coherent across XCDs without an L2 writeback
+      // (a device-scope fence here wrote back the L2 once per wave)
+      __hip_atomic_store(&rowres[row * 4 + 2], d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&rowres[row * 4 + 3], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ear_rows[row] = (float)e;
       kl_rows[row] = (float)d;
-      __threadfence();   // the row's results before this workgroup's ticket
     }
   }
   __shared__ bool last;
   __shared__ double lds[kThreads / kWave];
+  // every row result of this workgroup has completed before its ticket
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           gridDim.x - 1;
   __syncthreads();
   if (!last) return;
-  __threadfence();   // every other workgroup's rows are visible from here
   double se = 0.0, sk = 0.0;
   for (int64_t r = threadIdx.x; r < rows; r += kThreads) {
-    se += rowres[r * 4 + 3];
-    sk += rowres[r * 4 + 2];
+    se += __hip_atomic_load(&rowres[r * 4 + 3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sk += __hip_atomic_load(&rowres[r * 4 + 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const double te = block_sum_f64(se, lds);
   const double tk = block_sum_f64(sk, lds);
