@@ -87,9 +87,9 @@ def test_dequant_gemm_validation():
     assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, A, None, None) == slq.SLQ_EINVAL  # y aliases x
     assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, B, None, None) == slq.SLQ_EINVAL  # y aliases codes
     assert L.slq_dequant_gemm(A, None, 1, y, None, None) == slq.SLQ_EINVAL
-    # split-K workspace required when the plan uses one (16 activation rows of
-    # K=4096 exceed one workgroup's activation tile, so the plan splits k)
-    big = packed(n=1024, k=4096)
+    # split-K workspace required when the plan uses one (16 activation rows on
+    # a 14336 x 4096 layer: the plan splits k for parallelism)
+    big = packed(n=14336, k=4096)
     assert L.slq_gemm_workspace_bytes(16, ctypes.byref(big)) > 0
     assert L.slq_dequant_gemm(A, ctypes.byref(big), 16, y, None, None) == slq.SLQ_EINVAL
     assert L.slq_dequant_gemm(A, ctypes.byref(big), 16, y, E + 0x100000 + 8, None) == slq.SLQ_EINVAL

@@ -155,7 +155,7 @@ def test_exact_pins(bits):
 
 
 def test_decode_deterministic_and_workspace_reset():
-    n, k = 4096, 4096
+    n, k = 4096, 14336   # 16 rows on this layer split k four ways
     W = S.skewed_weights(n, k, 1)
     pw = slq.slq_quantize_pack(gpu(W), 4)
     x = x_gpu(S.activations_bf16(16, k, 2))

@@ -690,6 +690,10 @@ size_t gemv_lds_bytes(int64_t m, int mt, int nt, int gw, bool xd, int wv) {
 #define SLQ_GEMV_LDS_BUDGET 65536
 #endif
 constexpr size_t kLdsBudget = SLQ_GEMV_LDS_BUDGET;   // activation bytes per workgroup
+#ifndef SLQ_GEMV_LDS_BUDGET_WIDE
+#define SLQ_GEMV_LDS_BUDGET_WIDE 131072
+#endif
+constexpr size_t kLdsBudgetWide = SLQ_GEMV_LDS_BUDGET_WIDE;   // the same for a workgroup alone on its CU
 #ifndef SLQ_GEMV_TARGET_BLOCKS
 #define SLQ_GEMV_TARGET_BLOCKS 256
 #endif
@@ -733,7 +737,7 @@ constexpr int kBatchNt1 = SLQ_GEMV_B_NT1, kBatchNt2 = SLQ_GEMV_B_NT2, kBatchNt4 
 constexpr int64_t kWvBlocks = SLQ_GEMV_WV_BLOCKS;
 // Dynamic LDS ceiling per workgroup: activations (<= 64 KiB + pitch padding)
 // plus scales/zero points (<= 32 KiB), or the reduction area (<= 64 KiB).
-constexpr size_t kMaxDynLds = 128 * 1024;
+constexpr size_t kMaxDynLds = 152 * 1024;   // activation tile, metadata and the kernel's own LDS stay within 160 KiB
 
 template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV, bool CM>
 hipError_t gemv_launch(const uint16_t *x, const uint32_t *codes, const void *scales,
@@ -971,12 +975,27 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
       }
     }
   }
+  if (p.mt == 1 && !p.xd && m > 4) {
+    // A split k on a layer narrow enough for 16-row tiles of 16 waves in at
+    // most kWvBlocks workgroups: one such workgroup, alone on its CU, holds
+    // the whole k range's activations in the larger LDS budget, so the split
+    // (partial sums and their reduction) goes away.
+    const int64_t g_now = gw_wide ? gw_wide : k_block(wv);
+    const int64_t nb1 = (n + 15) / 16;
+    const int64_t gw_max_wide = (int64_t)kLdsBudgetWide / (m * 256);
+    if (g_now < G && G <= gw_max_wide && G >= 16 && nb1 <= kWvBlocks) {
+      p.nt = 1;
+      p.mv = false;
+      wv = 16;
+      gw_wide = G;
+    }
+  }
   p.wv = wv;
   const int64_t gw = gw_wide ? gw_wide : k_block(wv);
   p.gw = (int)gw;
   p.b = (p.xd && p.mt > 1) ? 1 : p.nt == 1 ? kBatchNt1 : p.nt == 2 ? kBatchNt2 : kBatchNt4;
   p.ksplits = (int)std::max<int64_t>(1, (G + p.gw - 1) / p.gw);
-  p.nblocks = (int)nb;
+  p.nblocks = (int)((n + 16 * p.nt - 1) / (16 * p.nt));
   if ((p.nblocks > kMaxTicketBlocks && p.ksplits > 1) || p.ksplits > 65535) p.ksplits = 0;   // not supported
   p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
   return p;
