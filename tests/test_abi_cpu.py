@@ -88,8 +88,8 @@ def test_dequant_gemm_validation():
     assert L.slq_dequant_gemm(A, ctypes.byref(w), 1, B, None, None) == slq.SLQ_EINVAL  # y aliases codes
     assert L.slq_dequant_gemm(A, None, 1, y, None, None) == slq.SLQ_EINVAL
     # split-K workspace required when the plan uses one (16 activation rows on
-    # a 14336 x 4096 layer: the plan splits k for parallelism)
-    big = packed(n=14336, k=4096)
+    # a 4096 x 14336 layer: the plan splits k four ways for parallelism)
+    big = packed(n=4096, k=14336)
     assert L.slq_gemm_workspace_bytes(16, ctypes.byref(big)) > 0
     assert L.slq_dequant_gemm(A, ctypes.byref(big), 16, y, None, None) == slq.SLQ_EINVAL
     assert L.slq_dequant_gemm(A, ctypes.byref(big), 16, y, E + 0x100000 + 8, None) == slq.SLQ_EINVAL

@@ -976,18 +976,24 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
     }
   }
   if (p.mt == 1 && !p.xd && m > 4) {
-    // A split k on a layer narrow enough for 16-row tiles of 16 waves in at
-    // most kWvBlocks workgroups: one such workgroup, alone on its CU, holds
-    // the whole k range's activations in the larger LDS budget, so the split
-    // (partial sums and their reduction) goes away.
+    // A split k on a layer narrow enough for at most kWvBlocks wide
+    // workgroups: one workgroup per row tile, alone on its CU, holds the whole
+    // k range's activations in the larger LDS budget, so the split (partial
+    // sums and their reduction) goes away.  16-row tiles take 16 waves; wider
+    // layers take 64-row tiles of 8 waves.
     const int64_t g_now = gw_wide ? gw_wide : k_block(wv);
-    const int64_t nb1 = (n + 15) / 16;
     const int64_t gw_max_wide = (int64_t)kLdsBudgetWide / (m * 256);
-    if (g_now < G && G <= gw_max_wide && G >= 16 && nb1 <= kWvBlocks) {
-      p.nt = 1;
-      p.mv = false;
-      wv = 16;
-      gw_wide = G;
+    if (g_now < G && G <= gw_max_wide) {
+      if (G >= 16 && (n + 15) / 16 <= kWvBlocks) {
+        p.nt = 1;
+        p.mv = false;
+        wv = 16;
+        gw_wide = G;
+      } else if (G >= 8 && p.nt == 4 && (n + 63) / 64 <= kWvBlocks) {
+        p.mv = false;
+        wv = 8;
+        gw_wide = G;
+      }
     }
   }
   p.wv = wv;
