@@ -154,6 +154,29 @@ def test_exact_pins(bits):
     assert np.all(np.abs(y - wh[:, 300]) <= np.abs(wh[:, 300]) * 2 ** -8)
 
 
+@pytest.mark.parametrize("bits", [3, 8])
+def test_decode_plans_whole_k_and_odd_k(bits):
+    """Decode plans that hold a layer's whole k range in one workgroup (16-row
+    tiles of 16 waves, 64-row tiles of 8 waves, the latter up to the LDS
+    ceiling with 63 groups), and layers whose group count is not a multiple of
+    4 (metadata staged per group), against the oracle on sampled outputs."""
+    cases = [(8192, 8064, (1, 5, 8, 12, 16)), (5000, 7936, (4, 5, 16)), (2000, 4096, (5, 16)),
+             (14336, 4096, (12, 16)), (4096, 4096, (12, 16))]
+    for (n, k, ms) in cases:
+        W = S.skewed_weights(n, k, 41 * bits + n, row_offset_std=0.005)
+        pw = slq.slq_quantize_pack(gpu(W), bits)
+        for m in ms:
+            say(f"decode plan bits={bits} m={m} {n}x{k}: {slq.kernel_name(m, pw)}")
+            x = S.activations_bf16(m, k, 3 * m + n)
+            y = slq.slq_dequant_gemm(x_gpu(x), pw)
+            mi, ni = sample_pairs(m, n, 1500, seed=m + n)
+            ys = y[torch.from_numpy(mi).to(DEV), torch.from_numpy(ni).to(DEV)].cpu().numpy()
+            yr, br = oracle_sampled(W, bits, x, mi, ni)
+            assert_gemm_close(ys, yr, br, what=f"plan b{bits} m{m} {n}x{k}")
+        del pw
+        torch.cuda.empty_cache()
+
+
 def test_decode_deterministic_and_workspace_reset():
     n, k = 4096, 14336   # 16 rows on this layer split k four ways
     W = S.skewed_weights(n, k, 1)

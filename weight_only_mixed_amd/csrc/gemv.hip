@@ -921,7 +921,7 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // A wave's share of a k-block is bounded by the metadata it stages through
   // its registers: kMetaRounds float4 units per lane (MV).
   auto per_limit = [&](bool mv) {
-    int64_t lim = std::numeric_limits<int64_t>::max();
+    int64_t lim = G;   // a wave's share never exceeds the k range (and lim * waves cannot overflow)
     if (mv) lim = std::min<int64_t>(lim, (int64_t)kWave * kMetaRounds * 4 / (16 * p.nt));
     return lim;
   };
@@ -983,13 +983,15 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
     // layers take 64-row tiles of 8 waves.
     const int64_t g_now = gw_wide ? gw_wide : k_block(wv);
     const int64_t gw_max_wide = (int64_t)kLdsBudgetWide / (m * 256);
+    // (the activations, metadata and reduction area must fit the LDS ceiling)
+    auto fits = [&](int nt, int w) { return gemv_lds_bytes(m, 1, nt, (int)G, false, w) <= kMaxDynLds; };
     if (g_now < G && G <= gw_max_wide) {
-      if (G >= 16 && (n + 15) / 16 <= kWvBlocks) {
+      if (G >= 16 && (n + 15) / 16 <= kWvBlocks && fits(1, 16)) {
         p.nt = 1;
         p.mv = false;
         wv = 16;
         gw_wide = G;
-      } else if (G >= 8 && p.nt == 4 && (n + 63) / 64 <= kWvBlocks) {
+      } else if (G >= 8 && p.nt == 4 && (n + 63) / 64 <= kWvBlocks && fits(4, 8)) {
         p.mv = false;
         wv = 8;
         gw_wide = G;
