@@ -147,6 +147,27 @@ def test_exact_pins(bits):
         y = slq.slq_dequant_gemm(x_gpu(xb), pw).cpu().numpy()
         assert (y[:, 7] == 0).all()
         assert np.array_equal(y[0], y[m // 2])
+    # the same decode pins on the mid-width 49..64-row kernel (ragged last
+    # row tile, an all-zero first and last row)
+    n2 = 2050
+    W2 = S.skewed_weights(n2, k, 6 + bits)
+    W2[0] = 0.0
+    W2[n2 - 1] = 0.0
+    q2, s2, z2 = oracle.quantize(W2, bits)
+    wh2 = oracle.dequantize(q2, s2, z2)
+    pw2 = slq.slq_quantize_pack(gpu(W2), bits)
+    for m in (50, 64):
+        assert slq.kernel_name(m, pw2).startswith("slq::gemv_mk_kernel")
+        for k0 in (0, 129, 511):
+            xb = np.zeros((m, k), np.uint16)
+            xb[:, k0] = 0x3F80
+            y = slq.slq_dequant_gemm(x_gpu(xb), pw2).cpu().numpy()
+            assert np.array_equal(y, np.broadcast_to(wh2[:, k0], (m, n2))), (bits, k0, m)
+        xb = S.activations_bf16(m, k, 11)
+        xb[m // 2] = xb[0]
+        y = slq.slq_dequant_gemm(x_gpu(xb), pw2).cpu().numpy()
+        assert (y[:, 0] == 0).all() and (y[:, n2 - 1] == 0).all()
+        assert np.array_equal(y[0], y[m // 2])
     # prefill one-hot: within bf16 rounding of w_hat
     xb = np.zeros((96, k), np.uint16)
     xb[:, 300] = 0x3F80
@@ -282,4 +303,44 @@ def test_prefill_workload_sampled(bits):
         yr, br = oracle_sampled(W, bits, xb, mi, ni)
         assert_gemm_close(ys, yr, br, what=f"prefill {name} b{bits}")
         del y, pw, W
+        torch.cuda.empty_cache()
+
+
+def _splits(m, pw):
+    """k-blocks of the decode plan, from the workspace it asks for (tickets,
+    then one fp32 partial per k-block and output)."""
+    ws = slq.gemm_workspace_bytes(m, pw)
+    return (ws - 65536) // (4 * m * pw.n) if ws else 1
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_decode_split_tails_and_mid_width_kernel(bits):
+    """The split-k tail (the last workgroup of a row block adds the k-blocks'
+    partials, several outputs and up to eight partial loads in flight per
+    thread) with more than eight and a non-multiple of eight k-blocks, in all
+    three decode kernels; and the mid-width 49..64-row kernel with whole and
+    uneven k-blocks, a ragged row edge and a trailing group outside its
+    two-group ring blocks.  Every output against the oracle, and bit-identical
+    results across calls."""
+    cases = [((16, 200, 20480), "slq::gemv_kernel", 20),
+             ((8, 300, 16384), "slq::gemv_kernel", 13),
+             ((40, 256, 32768), "slq::gemv_rows_kernel", 32),
+             ((64, 2048, 4096), "slq::gemv_mk_kernel", 8),
+             ((60, 3000, 8320), "slq::gemv_mk_kernel", 6),
+             ((64, 8191, 1152), "slq::gemv_mk_kernel", 2),
+             ((49, 2100, 640), "slq::gemv_mk_kernel", 1)]
+    for (m, n, k), kname, ks in cases:
+        say(f"split tails bits={bits} m={m} n={n} k={k}")
+        W = S.skewed_weights(n, k, 17 * bits + n + m, row_offset_std=0.005)
+        x = S.activations_bf16(m, k, 5 * m + bits + k)
+        pw = slq.slq_quantize_pack(gpu(W), bits)
+        assert slq.kernel_name(m, pw).startswith(kname)
+        assert _splits(m, pw) == ks
+        y = slq.slq_dequant_gemm(x_gpu(x), pw)
+        y2 = slq.slq_dequant_gemm(x_gpu(x), pw)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        yr, br, _ = full_ref(W, bits, x)
+        assert_gemm_close(y.cpu().numpy(), yr, br, what=f"tails b{bits} m{m} {n}x{k}")
+        del y, y2, pw
         torch.cuda.empty_cache()

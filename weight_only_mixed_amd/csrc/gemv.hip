@@ -168,6 +168,51 @@ __device__ __forceinline__ void x_fragments(const uint32_t (&X)[16], uint32_t (&
   for (int j = 0; j < 16; ++j) F[j] = x_pair<BITS>(X, j);
 }
 
+// Split-k tail, run by the last workgroup of a row block: y[m][n0 + r] for
+// r < rows is the sum of the k-blocks' partials, added in k-block order.  Each
+// thread keeps kRedOut outputs x kRedBatch partial loads in flight (relaxed
+// device-scope loads, coherent across XCDs); a chain of dependent loads per
+// output had made this tail the longest part of a decode call with many rows.
+constexpr int kRedOut = 4;
+constexpr int kRedBatch = 8;
+__device__ __forceinline__ void reduce_partials(const float *__restrict__ partial,
+                                                float *__restrict__ y, int M, int N, int n0,
+                                                int rows, int ksplits, int nthreads) {
+  const int total = M * rows;
+  const int64_t st = (int64_t)M * N;   // floats per k-block
+  for (int i0 = threadIdx.x; i0 < total; i0 += kRedOut * nthreads) {
+    int64_t off[kRedOut];
+    bool ok[kRedOut];
+#pragma unroll
+    for (int e = 0; e < kRedOut; ++e) {
+      const int i = i0 + e * nthreads;
+      const int m = i / rows, n = n0 + i % rows;
+      ok[e] = i < total && n < N;
+      off[e] = ok[e] ? (int64_t)m * N + n : 0;
+    }
+    float sum[kRedOut];
+#pragma unroll
+    for (int e = 0; e < kRedOut; ++e) sum[e] = 0.f;
+    for (int sp0 = 0; sp0 < ksplits; sp0 += kRedBatch) {
+      float v[kRedOut][kRedBatch];
+#pragma unroll
+      for (int e = 0; e < kRedOut; ++e)
+#pragma unroll
+        for (int j = 0; j < kRedBatch; ++j)
+          v[e][j] = __hip_atomic_load(partial + off[e] + (int64_t)min(sp0 + j, ksplits - 1) * st,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int e = 0; e < kRedOut; ++e)
+#pragma unroll
+        for (int j = 0; j < kRedBatch; ++j)
+          if (sp0 + j < ksplits) sum[e] += v[e][j];
+    }
+#pragma unroll
+    for (int e = 0; e < kRedOut; ++e)
+      if (ok[e]) y[off[e]] = sum[e];
+  }
+}
+
 // Workgroup: 4 wavefronts on the same 16*NT rows, each taking a contiguous
 // quarter of the workgroup's k-block.  The activations of the k-block are
 // staged once in LDS, already permuted into MFMA fragment order, and so are
@@ -483,16 +528,7 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
   }
   __syncthreads();
   if (!last) return;
-  const int rows = 16 * NT;
-  for (int i = threadIdx.x; i < M * rows; i += WV * kWave) {
-    const int m = i / rows, n = n0 + i % rows;
-    if (n >= N) continue;
-    float sum = 0.f;
-    for (int sp = 0; sp < ksplits; ++sp)
-      sum += __hip_atomic_load(&partial[((int64_t)sp * M + m) * N + n], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    y[(int64_t)m * N + n] = sum;
-  }
+  reduce_partials(partial, y, M, N, n0, 16 * NT, ksplits, WV * kWave);
   if (threadIdx.x == 0)
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -658,16 +694,227 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
   }
   __syncthreads();
   if (!last) return;
-  const int n0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < M * 64; i += kThreads) {
-    const int m = i / 64, nn = n0 + i % 64;
-    if (nn >= N) continue;
-    float sum = 0.f;
-    for (int sp = 0; sp < ksplits; ++sp)
-      sum += __hip_atomic_load(&partial[((int64_t)sp * M + m) * N + nn], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    y[(int64_t)m * N + nn] = sum;
+  reduce_partials(partial, y, M, N, blockIdx.x * 64, 64, ksplits, kThreads);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Several m-tiles on mid-width layers: `gemv_mk_kernel`.
+// The four wavefronts of a workgroup work on the same group at a time, each on
+// its own NT tiles of 16 weight rows (64*NT rows per workgroup), so one LDS copy
+// of a group's activations serves all of them and every A operand read from
+// LDS feeds NT MFMA chains.  The offset chain S = x . 128 (x . 1 for 8 bits)
+// does not depend on the weight row: it is formed once per workgroup and group,
+// by wavefront mt for m-tile mt, one group ahead, and shared through LDS.  It is
+// the same MFMA instruction sequence as a code chain on all-zero codes, so
+// C - S is exactly 0 for an all-zero group.  Activations pass through three LDS
+// buffers (the current group's, the next group's, from which S is formed, and
+// the one being written), with one barrier per group.  Each lane keeps
+// kMkDepth groups of its codes, scales and zero points in flight in registers.
+#ifndef SLQ_GEMV_MK_DEPTH
+#define SLQ_GEMV_MK_DEPTH 2
+#endif
+constexpr int kMkDepth = SLQ_GEMV_MK_DEPTH;
+static_assert(kMkDepth % 2 == 0, "activation register sets alternate per group");
+
+template <int BITS, int NT>
+struct MkSlot {
+  Chunk<BITS> c[NT];
+  float s[NT];
+  uint32_t z[NT];
+};
+
+template <int BITS, int MT, int NT, bool CM>
+__global__ __launch_bounds__(kThreads) void gemv_mk_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
+    unsigned *__restrict__ tickets) {
+  static_assert(kThreads == 256 && MT <= kWaves, "four wavefronts, one per S m-tile");
+  constexpr int RW = 16 * NT;           // weight rows per wavefront
+  constexpr int RB = kWaves * RW;       // weight rows per workgroup
+  const MetaRd<BITS, CM> md{scales, zeros};
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = K / kGroup;
+  const int kb = blockIdx.y;
+  const int gbase = kb * GW;
+  const int gcount = min(GW, G - gbase);
+  const int nw = blockIdx.x * RB + RW * wave;   // this wave's first row
+  const int64_t wpr = (int64_t)K * BITS / 32;
+  const int xw = M * kRowsXPitch;               // words per activation buffer
+  float *sbuf = reinterpret_cast<float *>(lds + 3 * xw);   // [2][16 * MT]
+  auto xbuf = [&](int g) { return lds + (g % 3) * xw; };
+
+  // activation staging: thread t owns chunk t % 4 of row t / 4 (clamped past M)
+  const int xm = min((int)threadIdx.x / 4, M - 1), xc = threadIdx.x % 4;
+  const bool xowner = (int)threadIdx.x < 4 * M;
+  const u32x4_t *xsrc =
+      reinterpret_cast<const u32x4_t *>(x + (int64_t)xm * K + (int64_t)gbase * kGroup + 32 * xc);
+  auto xload = [&](int g, u32x4_t (&v)[4]) {
+    const int gg = min(g, gcount - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = xsrc[gg * (kGroup / 8) + q];
+  };
+  auto xstore = [&](uint32_t *buf, const u32x4_t (&v)[4]) {
+    if (!xowner) return;
+    uint32_t X[16], F[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      X[4 * q + 0] = v[q][0];
+      X[4 * q + 1] = v[q][1];
+      X[4 * q + 2] = v[q][2];
+      X[4 * q + 3] = v[q][3];
+    }
+    x_fragments<BITS>(X, F);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(buf + xm * kRowsXPitch + xc * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = u32x4_t{F[4 * q], F[4 * q + 1], F[4 * q + 2], F[4 * q + 3]};
+  };
+
+  // codes, scale and zero point of this lane's rows for group g
+  const uint32_t *crow[NT];
+  int64_t mrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t r = min(nw + 16 * t + col, N - 1);
+    crow[t] = codes + r * wpr + (int64_t)gbase * 4 * BITS + kq * BITS;
+    mrow[t] = r * G + gbase;
   }
+  auto sload = [&](int g, MkSlot<BITS, NT> &o) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      o.c[t] = load_chunk<BITS>(crow[t] + (int64_t)g * 4 * BITS);
+      o.s[t] = md.scale(mrow[t] + g);
+      o.z[t] = md.zero(mrow[t] + g);
+    }
+  };
+
+  const uint32_t unit1 = (BITS == 8) ? kOne2 : kMagic2;
+  const u32x4_t unit = u32x4_t{unit1, unit1, unit1, unit1};
+  // S of group g for m-tile `wave`, from its activation buffer
+  auto s_chain = [&](int g) {
+    if (wave >= MT) return;
+    const int m = min(16 * wave + col, M - 1);
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(xbuf(g) + m * kRowsXPitch + kq * 16);
+    f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S = mfma16(src[r], unit, S);
+    if (col == 0) *reinterpret_cast<f32x4_t *>(sbuf + (g & 1) * 16 * MT + 16 * wave + 4 * kq) = S;
+  };
+
+  // prologue: x(0), x(1) staged; x(2), x(3) in registers; the code ring; S(0)
+  u32x4_t xr[2][4];
+  xload(0, xr[0]);
+  xload(1, xr[1]);
+  MkSlot<BITS, NT> ring[kMkDepth];
+  // (loads are unconditional, clamped to the last group, so the number of
+  // loads in flight is the same on every path and the waits stay partial)
+#pragma unroll
+  for (int d = 0; d < kMkDepth; ++d) sload(min(d, gcount - 1), ring[d]);
+  xstore(xbuf(0), xr[0]);
+  xstore(xbuf(1), xr[1]);
+  xload(2, xr[0]);
+  xload(3, xr[1]);
+  __syncthreads();
+  s_chain(0);
+  __syncthreads();
+
+  const uint32_t magic = in_vgpr(kMagic2);
+  f32x4_t acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // group g: x(g) in buffer g % 3, x(g + 1) in buffer (g + 1) % 3 (both
+  // published), S(g) in sbuf[g & 1]; x(g + 2) waits in xs and goes to buffer
+  // (g + 2) % 3, which was last read before the previous barrier.
+  auto body = [&](int g, const MkSlot<BITS, NT> &c, u32x4_t (&xs)[4]) {
+    if (g + 1 < gcount) s_chain(g + 1);
+    const uint32_t *buf = xbuf(g);
+    uint32_t p[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) unpack_pairs<BITS>(c.c[t], p[t], magic);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = min(16 * mt + col, M - 1);
+      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(buf + m * kRowsXPitch + kq * 16);
+      u32x4_t A[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) A[r] = src[r];
+      const f32x4_t S = *reinterpret_cast<const f32x4_t *>(sbuf + (g & 1) * 16 * MT + 16 * mt + 4 * kq);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4_t C = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          C = mfma16(A[r], u32x4_t{p[t][4 * r], p[t][4 * r + 1], p[t][4 * r + 2], p[t][4 * r + 3]}, C);
+        const float zf = (float)c.z[t];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float tv;
+          if constexpr (BITS == 8) tv = fmaf(-zf, S[v], C[v]);
+          else tv = fmaf(-zf * 0.0078125f, S[v], C[v] - S[v]);
+          acc[t][mt][v] = fmaf(c.s[t], tv, acc[t][mt][v]);
+        }
+      }
+    }
+    // buffer (g + 2) % 3 is read by no one in this step; past the end it
+    // receives a copy of the last group that is never used
+    xstore(xbuf(g + 2), xs);
+    xload(g + 4, xs);
+    __syncthreads();
+  };
+
+  // whole blocks of kMkDepth groups (no exit inside, so every trip leaves the
+  // same loads in flight), then the remaining groups, already in the ring
+  const int nfull = gcount / kMkDepth;
+  for (int it = 0; it < nfull; ++it) {
+#pragma unroll
+    for (int j = 0; j < kMkDepth; ++j) {
+      const int g = it * kMkDepth + j;
+      body(g, ring[j], xr[j % 2]);
+      sload(min(g + kMkDepth, gcount - 1), ring[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMkDepth - 1; ++j) {
+    const int g = nfull * kMkDepth + j;
+    if (g >= gcount) break;
+    body(g, ring[j], xr[j % 2]);
+  }
+
+  // ---- outputs: rows nw + 16 t + col, m = 16 mt + 4 kq + v ----
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = nw + 16 * t + col;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 16 * mt + 4 * kq + v;
+        if (m >= M || n >= N) continue;
+        if (ksplits == 1) y[(int64_t)m * N + n] = acc[t][mt][v];
+        else
+          __hip_atomic_store(&partial[((int64_t)kb * M + m) * N + n], acc[t][mt][v],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  }
+  if (ksplits == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ unsigned last;
+  if (threadIdx.x == 0) {
+    const unsigned ticket = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    last = (ticket == (unsigned)ksplits - 1u);
+  }
+  __syncthreads();
+  if (!last) return;
+  reduce_partials(partial, y, M, N, blockIdx.x * RB, RB, ksplits, kThreads);
   if (threadIdx.x == 0)
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -714,6 +961,35 @@ constexpr int64_t kXdMinGroups = SLQ_GEMV_XD_MIN_GROUPS;
 #define SLQ_GEMV_ROWS_MIN_MT 3
 #endif
 constexpr int kRowsMinMt = SLQ_GEMV_ROWS_MIN_MT;   // fewest m-tiles for the row-split kernel
+// gemv_mk_kernel: workgroups aimed for, fewest groups per k-block, and the
+// narrowest layer given 128-row workgroups (by default none: 128-row
+// workgroups measured slower than 64-row ones on every layer tried).
+// It serves 49..64 rows (4 m-tiles) on layers 2048..8191 wide, where it measured
+// 8-11% faster than the per-lane-activation and row-split kernels; on wider and
+// narrower layers and with fewer rows those measured faster.
+#ifndef SLQ_GEMV_MK_MIN_MT
+#define SLQ_GEMV_MK_MIN_MT 4
+#endif
+constexpr int kMkMinMt = SLQ_GEMV_MK_MIN_MT;
+#ifndef SLQ_GEMV_MK_MIN_N
+#define SLQ_GEMV_MK_MIN_N 2048
+#endif
+#ifndef SLQ_GEMV_MK_MAX_N
+#define SLQ_GEMV_MK_MAX_N 8191
+#endif
+constexpr int64_t kMkMinN = SLQ_GEMV_MK_MIN_N, kMkMaxN = SLQ_GEMV_MK_MAX_N;
+#ifndef SLQ_GEMV_MK_TARGET
+#define SLQ_GEMV_MK_TARGET 256
+#endif
+constexpr int64_t kMkTarget = SLQ_GEMV_MK_TARGET;
+#ifndef SLQ_GEMV_MK_MIN_GROUPS
+#define SLQ_GEMV_MK_MIN_GROUPS 4
+#endif
+constexpr int64_t kMkMinGroups = SLQ_GEMV_MK_MIN_GROUPS;
+#ifndef SLQ_GEMV_MK_NT2_MIN_N
+#define SLQ_GEMV_MK_NT2_MIN_N (1LL << 40)
+#endif
+constexpr int64_t kMkNt2MinN = SLQ_GEMV_MK_NT2_MIN_N;
 // Groups per load batch for 1, 2 and 4 row tiles (two batches in flight).
 #ifndef SLQ_GEMV_B_NT1
 #define SLQ_GEMV_B_NT1 4
@@ -834,10 +1110,63 @@ hipError_t gemv_rows_launch(const uint16_t *x, const uint32_t *codes, const void
   return hipGetLastError();
 }
 
+size_t gemv_mk_lds_bytes(int64_t m, int mt) {
+  return (size_t)3 * m * kRowsXPitch * 4 + (size_t)2 * 16 * mt * 4 + 16;
+}
+
+template <int BITS, int MT, int NT, bool CM>
+hipError_t gemv_mk_launch(const uint16_t *x, const uint32_t *codes, const void *scales,
+                          const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
+                          void *ws, const GemvPlan &plan, hipStream_t st) {
+  float *partial = nullptr;
+  unsigned *tickets = nullptr;
+  if (plan.ksplits > 1) {
+    tickets = static_cast<unsigned *>(ws);
+    partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
+  }
+  const size_t lds = gemv_mk_lds_bytes(m, MT);
+  if (lds > kMaxDynLds) return hipErrorInvalidValue;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&gemv_mk_kernel<BITS, MT, NT, CM>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
+  if (attr != hipSuccess) {
+    (void)hipGetLastError();
+    return attr;
+  }
+  hipLaunchKernelGGL((gemv_mk_kernel<BITS, MT, NT, CM>), dim3(plan.nblocks, plan.ksplits),
+                     dim3(kThreads), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
+                     plan.gw, plan.ksplits, y, partial, tickets);
+  return hipGetLastError();
+}
+
+template <int BITS, int MT, bool CM>
+hipError_t gemv_mk_nt(const uint16_t *x, const uint32_t *codes, const void *scales,
+                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
+                      const GemvPlan &plan, hipStream_t st) {
+  if constexpr (kMkNt2MinN < ((int64_t)1 << 40))
+    if (plan.nt == 2) return gemv_mk_launch<BITS, MT, 2, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+  return gemv_mk_launch<BITS, MT, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+}
+
 template <int BITS, bool CM>
 hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      const GemvPlan &plan, hipStream_t st) {
+  if (plan.mk) {
+    // only the m-tile counts and row tiles the planner can choose are built
+    switch (plan.mt) {
+      case 2:
+        if constexpr (kMkMinMt <= 2)
+          return gemv_mk_nt<BITS, 2, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+        return hipErrorInvalidValue;
+      case 3:
+        if constexpr (kMkMinMt <= 3)
+          return gemv_mk_nt<BITS, 3, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+        return hipErrorInvalidValue;
+      case 4: return gemv_mk_nt<BITS, 4, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (plan.rows) {
     switch (plan.mt) {
       case 1: return gemv_rows_launch<BITS, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
@@ -860,15 +1189,39 @@ hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const void *scale
 
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   (void)bits;
-  GemvPlan p;
+  GemvPlan p{};
   p.mt = (int)((m + 15) / 16);
   const int64_t G = k / kGroup;
   // 33..64 activation rows on a wide or deep layer: the row-split kernel (one
   // LDS copy of each group's activations for 64 weight rows) beats per-lane
   // activation loads, whose L2 traffic grows with n * k * m / 16; narrower
   // layers and 17..32 rows measured faster with per-lane loads.
-  p.rows = p.mt >= kRowsMinMt && (n >= 8192 || k >= 8192);
   p.wv = kWaves;
+  if (p.mt >= kMkMinMt && n >= kMkMinN && n <= kMkMaxN) {
+    // 49..64 rows on a mid-width layer: gemv_mk_kernel, one LDS copy of each
+    // group's activations for 64*nt rows; k is split only for lack of
+    // workgroups, keeping at least kMkMinGroups groups per k-block.
+    p.mk = true;
+    p.rows = false;
+    p.mv = false;
+    p.xd = false;
+    p.b = kMkDepth;
+    p.nt = n >= kMkNt2MinN ? 2 : 1;
+    const int64_t rb = 64 * p.nt;
+    const int64_t nb = (n + rb - 1) / rb;
+    int64_t ks = std::max<int64_t>(1, (kMkTarget + nb - 1) / nb);
+    ks = std::min<int64_t>(ks, std::max<int64_t>(1, G / kMkMinGroups));
+    const int64_t gw = std::max<int64_t>(1, (G + ks - 1) / ks);
+    p.gw = (int)std::min<int64_t>(gw, std::numeric_limits<int>::max());
+    p.ksplits = (int)((G + gw - 1) / gw);
+    p.nblocks = (int)nb;
+    if ((p.nblocks > kMaxTicketBlocks && p.ksplits > 1) || (G + gw - 1) / gw > 65535 ||
+        gemv_mk_lds_bytes(m, p.mt) > kMaxDynLds)
+      p.ksplits = 0;   // not supported
+    p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
+    return p;
+  }
+  p.rows = p.mt >= kRowsMinMt && (n >= 8192 || k >= 8192);
   if (p.rows) {
     // row-split kernel: 64 rows per workgroup; split k only for lack of
     // workgroups, keeping at least 8 groups per k-block

@@ -182,7 +182,9 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
   if (m <= kDecodeMaxM) {
     const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
     const char *cm = w->meta == SLQ_META_COMPACT ? "true" : "false";
-    if (p.rows)
+    if (p.mk)
+      snprintf(buf, sizeof buf, "slq::gemv_mk_kernel<%d, %d, %d, %s>", w->bits, p.mt, p.nt, cm);
+    else if (p.rows)
       snprintf(buf, sizeof buf, "slq::gemv_rows_kernel<%d, %d, %s>", w->bits, p.mt, cm);
     else
       snprintf(buf, sizeof buf, "slq::gemv_kernel<%d, %d, %d, %d, %s, %s, %d, %s>", w->bits, p.mt,
