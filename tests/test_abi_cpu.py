@@ -182,6 +182,14 @@ def test_sizes_and_strings():
     assert L.slq_quant_error_workspace_bytes(ctypes.byref(packed())) > 0
     name = L.slq_dequant_gemm_kernel_name(1, ctypes.byref(packed(n=4096, k=4096)))
     assert name.startswith(b"slq::gemv_kernel<4, 1,")
+    # decode routing by activation rows and layer width (planning only)
+    mid, wide = packed(n=4096, k=4096), packed(n=14336, k=4096)
+    assert L.slq_dequant_gemm_kernel_name(64, ctypes.byref(mid)) == b"slq::gemv_mk_kernel<4, 4, 1, false>"
+    assert L.slq_dequant_gemm_kernel_name(49, ctypes.byref(mid)) == b"slq::gemv_mk_kernel<4, 4, 1, false>"
+    assert L.slq_dequant_gemm_kernel_name(48, ctypes.byref(mid)).startswith(b"slq::gemv_kernel<4, 3,")
+    assert L.slq_dequant_gemm_kernel_name(64, ctypes.byref(wide)) == b"slq::gemv_rows_kernel<4, 4, false>"
+    assert L.slq_dequant_gemm_kernel_name(64, ctypes.byref(packed(n=1024, k=4096))).startswith(
+        b"slq::gemv_kernel<4, 4,")
     assert L.slq_dequant_gemm_kernel_name(100, ctypes.byref(packed())) == b"slq::gemm_kernel<4, false>"
     assert L.slq_dequant_gemm_kernel_name(1, ctypes.byref(packed(bits=9))) == b""
     for s in range(4):

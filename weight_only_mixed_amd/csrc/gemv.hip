@@ -36,6 +36,11 @@
 //    stores; the last workgroup of each row block (relaxed atomic ticket after
 //    the stores have completed) sums them in split order, so results are
 //    deterministic, and resets its ticket.
+//  * Three kernels: `gemv_kernel` (any m, the general form above),
+//    `gemv_rows_kernel` (33..64 rows on wide or deep layers: the waves split
+//    rows and share each group's activations) and `gemv_mk_kernel` (49..64
+//    rows on mid-width layers: the same sharing with the offset chain formed
+//    once per workgroup); the planner at the end of this file picks one.
 
 #include <algorithm>
 #include <limits>
@@ -533,7 +538,7 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Decode with 17..64 activation rows.  The activations of a group (up to
+// Decode with 33..64 activation rows on wide or deep layers.  The activations of a group (up to
 // 64 x 128 bf16) are the large operand next to a 16-row weight tile, so the
 // four wavefronts of a workgroup split rows instead of k: wavefront w owns
 // rows [16w, 16w + 16) of the workgroup's 64, and all four read one copy of
