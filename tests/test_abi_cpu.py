@@ -186,7 +186,11 @@ def test_sizes_and_strings():
     mid, wide = packed(n=4096, k=4096), packed(n=14336, k=4096)
     assert L.slq_dequant_gemm_kernel_name(64, ctypes.byref(mid)) == b"slq::gemv_mk_kernel<4, 4, 1, false>"
     assert L.slq_dequant_gemm_kernel_name(49, ctypes.byref(mid)) == b"slq::gemv_mk_kernel<4, 4, 1, false>"
-    assert L.slq_dequant_gemm_kernel_name(48, ctypes.byref(mid)).startswith(b"slq::gemv_kernel<4, 3,")
+    assert L.slq_dequant_gemm_kernel_name(48, ctypes.byref(mid)) == b"slq::gemv_mk_kernel<4, 3, 1, false>"
+    assert L.slq_dequant_gemm_kernel_name(40, ctypes.byref(mid)).startswith(b"slq::gemv_kernel<4, 3,")
+    deep = packed(n=4096, k=14336)
+    assert L.slq_dequant_gemm_kernel_name(40, ctypes.byref(deep)) == b"slq::gemv_mk_kernel<4, 3, 1, false>"
+    assert L.slq_dequant_gemm_kernel_name(32, ctypes.byref(deep)).startswith(b"slq::gemv_kernel<4, 2,")
     assert L.slq_dequant_gemm_kernel_name(64, ctypes.byref(wide)) == b"slq::gemv_rows_kernel<4, 4, false>"
     assert L.slq_dequant_gemm_kernel_name(64, ctypes.byref(packed(n=1024, k=4096))).startswith(
         b"slq::gemv_kernel<4, 4,")

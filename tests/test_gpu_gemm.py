@@ -147,7 +147,7 @@ def test_exact_pins(bits):
         y = slq.slq_dequant_gemm(x_gpu(xb), pw).cpu().numpy()
         assert (y[:, 7] == 0).all()
         assert np.array_equal(y[0], y[m // 2])
-    # the same decode pins on the mid-width 49..64-row kernel (ragged last
+    # the same decode pins on the mid-width 33..64-row kernel (ragged last
     # row tile, an all-zero first and last row)
     n2 = 2050
     W2 = S.skewed_weights(n2, k, 6 + bits)
@@ -156,7 +156,7 @@ def test_exact_pins(bits):
     q2, s2, z2 = oracle.quantize(W2, bits)
     wh2 = oracle.dequantize(q2, s2, z2)
     pw2 = slq.slq_quantize_pack(gpu(W2), bits)
-    for m in (50, 64):
+    for m in (48, 50, 64):
         assert slq.kernel_name(m, pw2).startswith("slq::gemv_mk_kernel")
         for k0 in (0, 129, 511):
             xb = np.zeros((m, k), np.uint16)
@@ -318,7 +318,7 @@ def test_decode_split_tails_and_mid_width_kernel(bits):
     """The split-k tail (the last workgroup of a row block adds the k-blocks'
     partials, several outputs and up to eight partial loads in flight per
     thread) with more than eight and a non-multiple of eight k-blocks, in all
-    three decode kernels; and the mid-width 49..64-row kernel with whole and
+    three decode kernels; and the mid-width 33..64-row kernel with whole and
     uneven k-blocks, a ragged row edge and a trailing group outside its
     two-group ring blocks.  Every output against the oracle, and bit-identical
     results across calls."""
@@ -328,14 +328,16 @@ def test_decode_split_tails_and_mid_width_kernel(bits):
              ((64, 2048, 4096), "slq::gemv_mk_kernel", 8),
              ((60, 3000, 8320), "slq::gemv_mk_kernel", 6),
              ((64, 8191, 1152), "slq::gemv_mk_kernel", 2),
-             ((49, 2100, 640), "slq::gemv_mk_kernel", 1)]
+             ((49, 2100, 640), "slq::gemv_mk_kernel", 1),
+             ((40, 2500, 8320), "slq::gemv_mk_kernel", None),
+             ((48, 2048, 1152), "slq::gemv_mk_kernel", None)]
     for (m, n, k), kname, ks in cases:
         say(f"split tails bits={bits} m={m} n={n} k={k}")
         W = S.skewed_weights(n, k, 17 * bits + n + m, row_offset_std=0.005)
         x = S.activations_bf16(m, k, 5 * m + bits + k)
         pw = slq.slq_quantize_pack(gpu(W), bits)
         assert slq.kernel_name(m, pw).startswith(kname)
-        assert _splits(m, pw) == ks
+        assert ks is None or _splits(m, pw) == ks
         y = slq.slq_dequant_gemm(x_gpu(x), pw)
         y2 = slq.slq_dequant_gemm(x_gpu(x), pw)
         torch.cuda.synchronize()

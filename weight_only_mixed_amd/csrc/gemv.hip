@@ -38,7 +38,7 @@
 //    deterministic, and resets its ticket.
 //  * Three kernels: `gemv_kernel` (any m, the general form above),
 //    `gemv_rows_kernel` (33..64 rows on wide or deep layers: the waves split
-//    rows and share each group's activations) and `gemv_mk_kernel` (49..64
+//    rows and share each group's activations) and `gemv_mk_kernel` (33..64
 //    rows on mid-width layers: the same sharing with the offset chain formed
 //    once per workgroup); the planner at the end of this file picks one.
 
@@ -538,7 +538,8 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Decode with 33..64 activation rows on wide or deep layers.  The activations of a group (up to
+// Decode with 33..64 activation rows on wide or deep layers (mid-width layers
+// take gemv_mk_kernel instead).  The activations of a group (up to
 // 64 x 128 bf16) are the large operand next to a 16-row weight tile, so the
 // four wavefronts of a workgroup split rows instead of k: wavefront w owns
 // rows [16w, 16w + 16) of the workgroup's 64, and all four read one copy of
@@ -969,13 +970,23 @@ constexpr int kRowsMinMt = SLQ_GEMV_ROWS_MIN_MT;   // fewest m-tiles for the row
 // gemv_mk_kernel: workgroups aimed for, fewest groups per k-block, and the
 // narrowest layer given 128-row workgroups (by default none: 128-row
 // workgroups measured slower than 64-row ones on every layer tried).
-// It serves 49..64 rows (4 m-tiles) on layers 2048..8191 wide, where it measured
-// 8-11% faster than the per-lane-activation and row-split kernels; on wider and
-// narrower layers and with fewer rows those measured faster.
+// It serves layers 2048..8191 wide with 49..64 rows (4 m-tiles), or with
+// 33..48 rows (3 m-tiles) when there are at least kMkMinM rows or the layer is
+// at least kMkDeepK deep: there it measured 3-11% faster than the
+// per-lane-activation and row-split kernels (q/o at 48 and 64 rows, the down
+// projection at 40, 48 and 64); on wider and narrower layers, with fewer rows,
+// and on q/o at 40 rows those measured faster.
 #ifndef SLQ_GEMV_MK_MIN_MT
-#define SLQ_GEMV_MK_MIN_MT 4
+#define SLQ_GEMV_MK_MIN_MT 3
 #endif
 constexpr int kMkMinMt = SLQ_GEMV_MK_MIN_MT;
+#ifndef SLQ_GEMV_MK_MIN_M
+#define SLQ_GEMV_MK_MIN_M 48
+#endif
+#ifndef SLQ_GEMV_MK_DEEP_K
+#define SLQ_GEMV_MK_DEEP_K 8192
+#endif
+constexpr int64_t kMkMinM = SLQ_GEMV_MK_MIN_M, kMkDeepK = SLQ_GEMV_MK_DEEP_K;
 #ifndef SLQ_GEMV_MK_MIN_N
 #define SLQ_GEMV_MK_MIN_N 2048
 #endif
@@ -1202,8 +1213,9 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // activation loads, whose L2 traffic grows with n * k * m / 16; narrower
   // layers and 17..32 rows measured faster with per-lane loads.
   p.wv = kWaves;
-  if (p.mt >= kMkMinMt && n >= kMkMinN && n <= kMkMaxN) {
-    // 49..64 rows on a mid-width layer: gemv_mk_kernel, one LDS copy of each
+  const bool mk_rows = p.mt >= 4 || (p.mt == 3 && (m >= kMkMinM || k >= kMkDeepK));
+  if (p.mt >= kMkMinMt && mk_rows && n >= kMkMinN && n <= kMkMaxN) {
+    // 33..64 rows on a mid-width layer: gemv_mk_kernel, one LDS copy of each
     // group's activations for 64*nt rows; k is split only for lack of
     // workgroups, keeping at least kMkMinGroups groups per k-block.
     p.mk = true;

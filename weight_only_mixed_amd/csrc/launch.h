@@ -32,7 +32,7 @@ struct GemvPlan {
   bool mv;         // scales/zero points staged as vectors of 4 groups per row
   bool xd;         // activations loaded by each lane with the weight batches (mt == 1)
   bool rows;       // 17..64 activation rows: row-split kernel, 64 rows per workgroup
-  bool mk;         // 49..64 activation rows, mid-width layer: gemv_mk_kernel, 64 * nt rows per workgroup
+  bool mk;         // 33..64 activation rows, mid-width layer: gemv_mk_kernel, 64 * nt rows per workgroup
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);
