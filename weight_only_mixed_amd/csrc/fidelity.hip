@@ -336,15 +336,6 @@ __device__ __forceinline__ float topk_value(uint64_t key) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t w = __shfl_xor(v, o, kWave);
-    v = v > w ? v : w;
-  }
-  return v;
-}
-
 constexpr int kCandCap = 512;   // per-wave candidate buffer (entries)
 
 // The K-th largest of the keys the wave holds (PER per lane, 0 = no entry),
