@@ -349,9 +349,18 @@ constexpr int64_t kMaxGridY = 65535;   // workgroups along a grid's y dimension
 
 // VALU instructions to place after each MFMA (the dequantization of one
 // 8-code B slice per 32-column tile, spread over the 16 MFMAs of a slice).
+// Measured on the 70B q/o and gate shapes at M = 4096: 3 and 5 run 3-6%
+// faster than 4 and 6, and than 2/4, 3/4, 3/6, 4/5 or 5/7 (the rest of a
+// slice's dequantization trails its MFMAs).
+#ifndef SLQ_GEMM_WIDE_VPM_POW2
+#define SLQ_GEMM_WIDE_VPM_POW2 3   // widths 2, 4 and 8
+#endif
+#ifndef SLQ_GEMM_WIDE_VPM_ODD
+#define SLQ_GEMM_WIDE_VPM_ODD 5    // widths 3, 5, 6 and 7
+#endif
 template <int BITS>
 constexpr int wide_valu_per_mfma() {
-  return BITS == 4 ? 4 : BITS == 8 ? 4 : BITS == 2 ? 4 : 6;
+  return (BITS == 2 || BITS == 4 || BITS == 8) ? SLQ_GEMM_WIDE_VPM_POW2 : SLQ_GEMM_WIDE_VPM_ODD;
 }
 
 template <int BITS, bool CM>
