@@ -40,9 +40,15 @@ struct Fid {
   int64_t chunk;  // elements per chunk (multiple of 4)
 };
 
+// Chunks per row: about kFidTargetWgs workgroups per launch, chunks of at
+// least 4096 elements.
+#ifndef SLQ_FID_TARGET_WGS
+#define SLQ_FID_TARGET_WGS 1024
+#endif
+constexpr int64_t kFidTargetWgs = SLQ_FID_TARGET_WGS;
 Fid fid_plan(int64_t rows, int64_t vocab) {
   Fid f;
-  int64_t c = (1024 + rows - 1) / rows;
+  int64_t c = (kFidTargetWgs + rows - 1) / rows;
   const int64_t maxc = std::max<int64_t>(1, (vocab + 4095) / 4096);
   c = std::min(std::max<int64_t>(c, 1), maxc);
   int64_t chunk = (vocab + c - 1) / c;
