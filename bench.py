@@ -508,14 +508,9 @@ def main():
     if "gptq" in rows_sel:
         log("bench: GPTQ, Llama-3-8B q (4096x4096) and gate (14336x4096) at 4 bits")
         kq = 4096
-        g = np.random.Generator(np.random.PCG64(S.seed_for(6)))
-        # synthetic Hessian 2 X X^T / T from correlated seeded activations (T = 2k);
-        # the product is input synthesis on the device
-        Xa = torch.from_numpy((g.standard_normal((kq, 8)) @ g.standard_normal((8, 2 * kq))
-                               + 0.5 * g.standard_normal((kq, 2 * kq))).astype(np.float32)).to(dev)
-        Hd = (2.0 / (2 * kq)) * (Xa @ Xa.T)
-        Hd = 0.5 * (Hd + Hd.T).contiguous()
-        del Xa
+        # the tests' synthetic layer Hessian 2 X X^T / T (correlated channels,
+        # lognormal channel scales), built on the host
+        Hd = to_dev(S.gptq_hessian(kq, S.seed_for(6), tokens=2 * kq))
         res = {}
         for (shape, n_) in (("q", 4096), ("gate", 14336)):
             Wg = to_dev(S.skewed_weights(n_, kq, S.seed_for(6, 1)))
@@ -525,6 +520,16 @@ def main():
                 slq.slq_gptq_quantize(Wg, Hd, 4)
             res[shape] = {"n": n_, "k": kq, "ms": round(T.ms, 2)}
             log(f"bench: GPTQ {shape} {n_}x{kq}: {T.ms:.1f} ms")
+            if shape == "q":
+                # one factor for the layer, then the column pass at every
+                # bit-width 2..8 (the pipeline quantizes each layer at all of them)
+                with Timer(torch) as T:
+                    Uf, dead, _ = slq.slq_gptq_factor(Hd)
+                    for b in range(2, 9):
+                        slq.slq_gptq_columns(Wg, Uf, b, dead=dead)
+                res["q_all_bitwidths"] = {"n": n_, "k": kq, "bits": "2..8", "ms": round(T.ms, 2)}
+                log(f"bench: GPTQ q, factor once + column pass at 7 bit-widths: {T.ms:.1f} ms")
+                del Uf, dead
             del Wg
         rows["gptq"] = res
         del Hd

@@ -236,6 +236,8 @@ size_t slq_gptq_workspace_bytes(int64_t n, int64_t k);
  *   from the group's current weights (the slq_quantize_pack steps), the column
  *   is quantized, and the later columns move by -err_i * U[i][j] with
  *   err_i = (w_i - w_hat_i) / U[i][i]  (weights updated in fp32).
+ * It is slq_gptq_factor followed by slq_gptq_columns on the fp32 U (their
+ * comments give the exact operation order).
  * In : W fp32 [n][k], H fp32 [k][k] symmetric positive semi-definite (the
  *      layer Hessian 2 X X^T; device, 16-byte aligned), 1 <= n, 128 <= k <=
  *      32768, k % 128 == 0, bits 2..8, group 128, damp > 0 and finite.
@@ -249,13 +251,62 @@ slq_status slq_gptq_quantize(const float *W, const float *H, int64_t n, int64_t 
                              int group, double damp, slq_packed *out, double *u_out,
                              void *workspace, slq_stream stream);
 
+/* Workspace bytes slq_gptq_factor needs for a k x k Hessian (0 if k is invalid). */
+size_t slq_gptq_factor_workspace_bytes(int64_t k);
+
+/*
+ * The inverse-Hessian factor of GPTQ alone (steps 1-2 of slq_gptq_quantize),
+ * so that one factor serves a layer at every bit-width (README, Pipeline:
+ * layer-wise GPTQ at each bit-width 2..8 against the same calibration data):
+ *   dead[i] = (H_ii == 0); dead inputs get H_ii = 1;
+ *   H += damp * mean(diag H) * I;  U upper triangular with U^T U = H^-1,
+ *   computed in fp64 and written rounded to fp32 (zeros below the diagonal).
+ * In : H fp32 [k][k] symmetric positive semi-definite (device, 16-byte
+ *      aligned), 128 <= k <= 32768, k % 128 == 0, damp > 0 and finite.
+ * Out: U fp32 [k][k] (16-byte aligned), dead uint8 [k], u_out fp64 [k][k]
+ *      (8-byte aligned) or NULL: U before rounding.  No output may overlap H
+ *      or another output.
+ * workspace: slq_gptq_factor_workspace_bytes(k) bytes, 256-byte aligned.
+ * If H + damping is not positive definite U holds NaN.
+ */
+slq_status slq_gptq_factor(const float *H, int64_t k, double damp, float *U, uint8_t *dead,
+                           double *u_out, void *workspace, slq_stream stream);
+
+/* Workspace bytes slq_gptq_columns needs for W[n][k] (0 if invalid). */
+size_t slq_gptq_columns_workspace_bytes(int64_t n, int64_t k);
+
+/*
+ * The GPTQ column pass alone (step 3 of slq_gptq_quantize), given the fp32
+ * factor U of slq_gptq_factor (or any upper-triangular U with a nonzero
+ * diagonal; entries below the diagonal are never read).  Lazy blocks of the
+ * 128-group, fp32 with one rounding per operation, in this order: the
+ * working weights are W with the columns of dead inputs set to 0; per group
+ * (first column i1) the scale and zero point come from the group's current
+ * weights by the slq_quantize_pack steps; for each column i of the group,
+ * ascending: q_i = clamp(rint(w_i / s) + z), e_i = fl32(fl32(w_i - w_hat_i) /
+ * U_ii), and every later column j of the group takes w_j = fma(-e_i, U_ij,
+ * w_j); then every column c after the group takes w_c = fl32(w_c - a_c),
+ * a_c = fma(e_p, U[i1 + p][c], a) chained over p = 0..127 from a = 0.
+ * Results are bit-identical across calls.
+ * In : W fp32 [n][k], U fp32 [k][k] (device, 16-byte aligned), dead uint8
+ *      [k] or NULL (nonzero = dead input), n >= 1, k as for slq_gptq_factor,
+ *      bits 2..8, group 128 (else SLQ_ENOTSUP).
+ * Out: out as for slq_gptq_quantize (out->meta must be SLQ_META_F32), not
+ *      overlapping the inputs.
+ * workspace: slq_gptq_columns_workspace_bytes(n, k) bytes, 256-byte aligned.
+ */
+slq_status slq_gptq_columns(const float *W, const float *U, const uint8_t *dead, int64_t n,
+                            int64_t k, int bits, int group, slq_packed *out, void *workspace,
+                            slq_stream stream);
+
 /* Workspace bytes slq_mckp_search needs for L items and budgets 0..W. */
 size_t slq_mckp_workspace_bytes(int64_t L, int64_t W);
 
 /*
  * Bit-width allocation (gist.science summary, 3. The SLQ Pipeline: a
  * multiple-choice knapsack over the cost table solved exactly under a bit
- * budget; README, Pipeline: binary-searched down to the target).
+ * budget; README, Pipeline: the budget is searched by bisection until the
+ * target is met).
  * Item l (a layer or projection) takes exactly one of nb options (bit-widths);
  * option j occupies sizes[l*nb+j] budget units and costs costs[l*nb+j]
  * (predicted degradation).  best(w) = least total cost with total size <= w

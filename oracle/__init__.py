@@ -56,6 +56,8 @@ def load(path: str):
     L.oracle_pack_zeros.argtypes = [_u8p, _i64, _int, _u8p]
     L.oracle_pack_zeros.restype = _i64
     L.oracle_dequantize_compact.argtypes = [_u8p, _u16p, _u8p, _i64, _i64, _int, _int, _f32p]
+    L.oracle_gptq_columns.argtypes = [_f32p, _f32p, ctypes.c_void_p, _i64, _i64, _int, _int, _u8p,
+                                      _f32p, _u8p]
     return L
 
 
@@ -252,3 +254,21 @@ def dequantize_compact(q, scales16, zpacked, bits: int, group: int = 128):
     lib().oracle_dequantize_compact(q, _c(scales16, np.uint16).ravel(), _c(zpacked, np.uint8),
                                     n, k, group, bits, out)
     return out
+
+
+def gptq_columns(W, U, bits: int, dead=None, group: int = 128):
+    """fp32 GPTQ column pass with lazy 128-column blocks (oracle.c,
+    oracle_gptq_columns): W fp32 [n][k], U fp32 [k][k] upper factor of the
+    inverse Hessian, dead bool [k] or None.  Returns codes uint8 [n][k],
+    scales fp32 [n][G], zeros uint8 [n][G]."""
+    W = _c(W, np.float32)
+    U = _c(U, np.float32)
+    n, k = W.shape
+    q = np.zeros((n, k), np.uint8)
+    s = np.zeros((n, k // group), np.float32)
+    z = np.zeros((n, k // group), np.uint8)
+    d = None
+    if dead is not None:
+        d = _c(np.asarray(dead).astype(np.uint8), np.uint8)
+    lib().oracle_gptq_columns(W, U, None if d is None else d.ctypes.data, n, k, bits, group, q, s, z)
+    return q, s, z

@@ -8,10 +8,17 @@ group size 128) without defining it; this follows the published algorithm
 Quantization for Generative Pre-trained Transformers", ICLR 2023: Algorithm 1
 with the Cholesky form of the inverse Hessian), column by column.
 
+Two column passes follow the same steps: `gptq_columns64` (fp64 weights,
+every column's update applied to all later columns at once) and the C
+oracle's fp32 pass with the algorithm's lazy 128-column blocks
+(`oracle.gptq_columns`, the form the GPU runs, operation for operation);
+`gptq` and `gptq32` run them from a Hessian.
+
 Parity is pinned by properties, not by the pages: an identity Hessian gives
 round-to-nearest exactly; the first column's update equals the closed-form
 optimal-brain-surgeon step from an explicitly inverted Hessian; on correlated
-Hessians the proxy loss is below round-to-nearest's.
+Hessians the proxy loss is below round-to-nearest's; on inputs where every
+fp32 operation is exact the two column passes agree code for code.
 """
 from __future__ import annotations
 
@@ -58,6 +65,32 @@ def gptq(W, H, bits: int, group: int = 128, damp: float = 0.01):
     fp32-rounded current weights with the plain quantizer's fp32 steps."""
     H, Wk = prepare_hessian(H, W, damp)
     U = upper_inverse_factor(H)
+    q, scales, zeros = gptq_columns64(Wk, U, bits, group)
+    return q, scales, zeros, U
+
+
+def dead_inputs(H):
+    """Inputs whose Hessian diagonal is zero (they never fire)."""
+    return np.diag(np.asarray(H)) == 0
+
+
+def gptq32(W, H, bits: int, group: int = 128, damp: float = 0.01):
+    """The fp32 lazy-block form from a Hessian: U in fp64 as in `gptq`,
+    rounded to fp32, then the C oracle's column pass.  Returns codes, scales,
+    zeros and the fp64 U."""
+    Hp, _ = prepare_hessian(H, W, damp)
+    U = upper_inverse_factor(Hp)
+    q, s, z = oracle.gptq_columns(np.asarray(W, np.float32), U.astype(np.float32), bits,
+                                  dead=dead_inputs(H), group=group)
+    return q, s, z, U
+
+
+def gptq_columns64(W, U, bits: int, group: int = 128):
+    """Column pass with fp64 weights, given the upper factor U of the inverse
+    Hessian: column i is quantized from its fp32-rounded current weight, its
+    error is divided by U_ii and every later column moves at once."""
+    Wk = np.array(W, np.float64, copy=True)
+    U = np.asarray(U, np.float64)
     n, k = Wk.shape
     G = k // group
     maxq = 2 ** bits - 1
@@ -79,7 +112,7 @@ def gptq(W, H, bits: int, group: int = 128, damp: float = 0.01):
         w_hat = ((qi.astype(np.int32) - zeros[:, g]).astype(np.float32) * s).astype(np.float64)
         err = (Wk[:, i] - w_hat) / U[i, i]
         Wk[:, i + 1:] -= np.outer(err, U[i, i + 1:])
-    return q, scales, zeros, U
+    return q, scales, zeros
 
 
 def proxy_loss(W, w_hat, H):

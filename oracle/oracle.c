@@ -28,7 +28,7 @@
  *  [SLQ-summary] gist.science summary, "3. The SLQ Pipeline": bit-width
  *               allocation as a multiple-choice knapsack problem solved exactly
  *               (ILP) under a bit budget; [SLQ-readme] Pipeline paragraph: the
- *               solve is binary-searched down to the target.
+ *               budget is found by bisection until the target is met.
  * Where the pages leave a step open, the reading taken is stated at the
  * function (readings R1..R12 in the design notes).
  *
@@ -384,7 +384,7 @@ double oracle_bits_per_param(int bits, int meta_bits, int group) {
 /*
  * Bit-width allocation ([SLQ-summary] "3. The SLQ Pipeline": a multiple-choice
  * knapsack over the cost table, solved exactly under a budget; [SLQ-readme]
- * Pipeline: binary-searched down to the target).
+ * Pipeline: the budget is found by bisection until the target is met).
  *
  * Items l = 0..L-1 (layers or projection groups) each take exactly one of nb
  * options (bit-widths); option j of item l occupies sizes[l*nb+j] budget units
@@ -591,5 +591,84 @@ void oracle_dequantize_compact(const uint8_t *q, const uint16_t *scales16, const
       float d = (float)((int)q[r * k + j] - z);
       w_hat[r * k + j] = d * s;
     }
+  }
+}
+
+/*
+ * GPTQ column pass in fp32 with lazy block updates.  The pages name GPTQ as
+ * the code-choice step ([SLQ-readme] Pipeline paragraph: layer-wise GPTQ at
+ * every bit-width, asymmetric INT, group 128) without defining it; the steps
+ * are those of the published algorithm (Frantar, Ashkboos, Hoefler, Alistarh,
+ * "GPTQ", ICLR 2023, Algorithm 1: quantize the columns in order, divide each
+ * column's error by the diagonal of the inverse-Hessian factor, move the
+ * block's later columns at once and every later column once per block).
+ *
+ * In : W fp32 [n][k]; U fp32 [k][k] upper triangular with U^T U = H^-1
+ *      (entries below the diagonal are never read); dead [k] or NULL
+ *      (nonzero: an input that never fires, whose weight column is zero).
+ * Out: q [n][k] codes, scales fp32 [n][G], zeros [n][G].
+ * Readings (R28-R32 in the design notes):
+ *   - the lazy block is the 128-group, so each group's scale and zero point
+ *     come from its current (already moved) weights at its first column, by
+ *     the plain quantizer's fp32 steps (R1-R4 above);
+ *   - every operation is one fp32 rounding, in this order: for column i of
+ *     the block, e_i = fl32(fl32(w_i - w_hat_i) / U_ii), then each later
+ *     column j of the block takes w_j = fma(-e_i, U_ij, w_j); after the block
+ *     every later column c takes w_c = fl32(w_c - a_c) with a_c the fma chain
+ *     a = fma(e_p, U[i1 + p][c], a) over p = 0, 1, ..., 127 from a = 0.
+ * Rows are independent given U.
+ */
+void oracle_gptq_columns(const float *W, const float *U, const uint8_t *dead, int64_t n,
+                         int64_t k, int bits, int group, uint8_t *q, float *scales,
+                         uint8_t *zeros) {
+  const int maxq = (1 << bits) - 1;
+  const int64_t G = k / group;
+#pragma omp parallel
+  {
+    float *w = (float *)malloc((size_t)k * sizeof(float));
+    float *e = (float *)malloc((size_t)group * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+      for (int64_t c = 0; c < k; ++c) w[c] = (dead && dead[c]) ? 0.0f : W[r * k + c];
+      for (int64_t g = 0; g < G; ++g) {
+        const int64_t i1 = g * group;
+        /* group parameters from the current weights (R1-R4) */
+        float lo = 0.0f, hi = 0.0f;
+        for (int p = 0; p < group; ++p) {
+          if (w[i1 + p] < lo) lo = w[i1 + p];
+          if (w[i1 + p] > hi) hi = w[i1 + p];
+        }
+        float range = hi - lo;
+        float s = range / (float)maxq;
+        int z;
+        if (s == 0.0f) {
+          s = 1.0f;
+          z = 0;
+        } else {
+          z = (int)clamp_code(rintf((-lo) / s), maxq);
+        }
+        scales[r * G + g] = s;
+        zeros[r * G + g] = (uint8_t)z;
+        /* the block's columns in order, moving the block's later columns */
+        for (int p = 0; p < group; ++p) {
+          const int64_t i = i1 + p;
+          float t = rintf(w[i] / s);
+          int qi = (int)clamp_code(t + (float)z, maxq);
+          q[r * k + i] = (uint8_t)qi;
+          float w_hat = (float)(qi - z) * s;
+          float d = w[i] - w_hat;
+          e[p] = d / U[i * k + i];
+          for (int64_t j = i + 1; j < i1 + group; ++j) w[j] = fmaf(-e[p], U[i * k + j], w[j]);
+        }
+        /* every later column once, by the block's errors */
+        for (int64_t c = i1 + group; c < k; ++c) {
+          float a = 0.0f;
+          for (int p = 0; p < group; ++p) a = fmaf(e[p], U[(i1 + p) * k + c], a);
+          w[c] = w[c] - a;
+        }
+      }
+    }
+    free(w);
+    free(e);
   }
 }

@@ -35,6 +35,9 @@ void oracle_quantize_compact(const float *W, int64_t n, int64_t k, int bits, int
 int64_t oracle_pack_zeros(const uint8_t *zeros, int64_t count, int bits, uint8_t *out);
 void oracle_dequantize_compact(const uint8_t *q, const uint16_t *scales16, const uint8_t *zpacked,
                                int64_t n, int64_t k, int group, int bits, float *w_hat);
+void oracle_gptq_columns(const float *W, const float *U, const uint8_t *dead, int64_t n,
+                         int64_t k, int bits, int group, uint8_t *q, float *scales,
+                         uint8_t *zeros);
 int oracle_mckp_search(int64_t L, int nb, const int64_t *sizes, const double *costs, int64_t W,
                        double tau, int32_t *choice, int64_t *budget_out, int64_t *size_out,
                        double *cost_out, double *best_out);

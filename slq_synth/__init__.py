@@ -175,6 +175,16 @@ def gptq_hessian(k: int, seed: int, tokens: int | None = None, rank: int = 8) ->
     return (2.0 * (X @ X.T) / T).astype(np.float32)
 
 
+def gptq_factor(k: int, seed: int, coupling: float = 0.5) -> np.ndarray:
+    """A synthetic inverse-Hessian factor for the GPTQ column pass: float32
+    [k][k] upper triangular, diagonal lognormal around 1 (a few strong inputs),
+    entries above it N(0, (coupling / sqrt(k))^2), zeros below."""
+    g = rng(seed)
+    U = np.triu(g.standard_normal((k, k)) * (coupling / np.sqrt(k)), 1)
+    U[np.arange(k), np.arange(k)] = np.exp(0.3 * g.standard_normal(k))
+    return U.astype(np.float32)
+
+
 def uniform_group_weights(n_groups: int, lo: float, hi: float, seed: int,
                           group: int = 128) -> np.ndarray:
     """Rows of uniform[lo, hi] samples with both endpoints pinned in every group.

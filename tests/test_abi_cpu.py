@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 23
     for name in names:
         assert hasattr(L, name), name
 
@@ -143,6 +143,28 @@ def test_fidelity_and_error_validation():
     assert Q(A, A, 64, 256, 4, 128, 0.01, ctypes.byref(packed(codes=A)), None, E, None) == slq.SLQ_EINVAL
     assert L.slq_gptq_workspace_bytes(64, 256) > 2 * 256 * 256 * 8
     assert L.slq_gptq_workspace_bytes(64, 200) == 0
+    # factor and column pass alone
+    Fc = L.slq_gptq_factor
+    assert Fc(A, 200, 0.01, B, C, None, E, None) == slq.SLQ_EINVAL               # k % 128
+    assert Fc(A, 256, -1.0, B, C, None, E, None) == slq.SLQ_EINVAL               # damp <= 0
+    assert Fc(A, 256, 0.01, None, C, None, E, None) == slq.SLQ_EINVAL            # no U
+    assert Fc(A, 256, 0.01, B, None, None, E, None) == slq.SLQ_EINVAL            # no mask
+    assert Fc(A, 256, 0.01, A + 4096, C, None, E, None) == slq.SLQ_EINVAL        # U overlaps H
+    assert Fc(A, 256, 0.01, B, B + 16, None, E, None) == slq.SLQ_EINVAL          # mask overlaps U
+    assert Fc(A, 256, 0.01, B, C, D + 4, E, None) == slq.SLQ_EINVAL              # misaligned fp64 U
+    assert L.slq_gptq_factor_workspace_bytes(256) >= 2 * 256 * 256 * 8
+    assert L.slq_gptq_factor_workspace_bytes(100) == 0
+    Cp = L.slq_gptq_columns
+    assert Cp(A, B, None, 64, 256, 9, 128, ctypes.byref(packed()), E, None) == slq.SLQ_EINVAL
+    assert Cp(A, B, None, 64, 256, 4, 64, ctypes.byref(packed()), E, None) == slq.SLQ_ENOTSUP
+    assert Cp(A, B, None, 0, 256, 4, 128, ctypes.byref(packed()), E, None) == slq.SLQ_EINVAL
+    assert Cp(A, None, None, 64, 256, 4, 128, ctypes.byref(packed()), E, None) == slq.SLQ_EINVAL
+    assert Cp(A, B, None, 64, 256, 4, 128, ctypes.byref(packed()), None, None) == slq.SLQ_EINVAL
+    assert Cp(A, B, None, 64, 256, 4, 128, ctypes.byref(cp), E, None) == slq.SLQ_ENOTSUP
+    assert Cp(A, B, None, 64, 256, 4, 128, ctypes.byref(packed(codes=B + 64)), E, None) == slq.SLQ_EINVAL
+    assert Cp(A, B, C + 8, 64, 256, 4, 128, ctypes.byref(packed(scales=C)), E, None) == slq.SLQ_EINVAL
+    assert L.slq_gptq_columns_workspace_bytes(64, 256) == 64 * 256 * 4 + 64 * 128 * 4
+    assert L.slq_gptq_columns_workspace_bytes(64, 200) == 0
     M = L.slq_mckp_search
     assert M(A, B, 0, 7, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL   # L = 0
     assert M(A, B, 4, 0, 100, 1.0, C, C + 256, C + 512, None, E, None) == slq.SLQ_EINVAL   # nb = 0

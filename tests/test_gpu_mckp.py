@@ -1,6 +1,6 @@
 """GPU parity of the bit-width allocation (gist.science summary, 3. The SLQ
 Pipeline: a multiple-choice knapsack over the cost table, solved exactly under
-a budget; SLQ README, Pipeline: binary-searched down to the target).
+a budget; SLQ README, Pipeline: the budget is found by bisection until the target is met).
 
 Both sides run the same exact recurrence in fp64 with the same order of
 additions and the same tie rule, so every output must be identical: the best

@@ -1,6 +1,6 @@
 """Pins of the oracle's bit-width allocation (gist.science summary, "3. The SLQ
 Pipeline": a multiple-choice knapsack solved exactly under a budget; SLQ
-README, Pipeline: binary-searched down to the target).
+README, Pipeline: the budget is found by bisection until the target is met).
 
 Readings: one option (bit-width) per item; sizes are integers in budget units;
 best(w) is the least total cost with total size <= w; the search returns the

@@ -15,7 +15,8 @@ import pytest
 
 import oracle
 from tests import (test_oracle_compact, test_oracle_fidelity, test_oracle_gamma, test_oracle_gemm,
-                   test_oracle_mckp, test_oracle_pack, test_oracle_quant, test_oracle_topk)
+                   test_oracle_gptq32, test_oracle_mckp, test_oracle_pack, test_oracle_quant,
+                   test_oracle_topk)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 HDR_DIR = os.path.dirname(SRC)
@@ -69,6 +70,16 @@ MUTANTS = {
                                      "        z ="),
     "compact_nibble_high_first": ("out[i / 2] |= (uint8_t)((zeros[i] & 15) << (4 * (i % 2)));",
                                   "out[i / 2] |= (uint8_t)((zeros[i] & 15) << (4 * (1 - i % 2)));"),
+    "gptq_trailing_sign": ("          w[c] = w[c] - a;", "          w[c] = w[c] + a;"),
+    "gptq_no_block_update": ("for (int64_t j = i + 1; j < i1 + group; ++j) w[j] = fmaf(-e[p], U[i * k + j], w[j]);",
+                             "/* block update dropped */"),
+    "gptq_error_not_scaled": ("e[p] = d / U[i * k + i];", "e[p] = d;"),
+    "gptq_trailing_transposed": ("a = fmaf(e[p], U[(i1 + p) * k + c], a);", "a = fmaf(e[p], U[c * k + (i1 + p)], a);"),
+    "gptq_trailing_drops_last_term": ("for (int p = 0; p < group; ++p) a = fmaf(",
+                                      "for (int p = 0; p < group - 1; ++p) a = fmaf("),
+    "gptq_params_from_original": ("          if (w[i1 + p] < lo) lo = w[i1 + p];\n          if (w[i1 + p] > hi) hi = w[i1 + p];",
+                                  "          if (W[r * k + i1 + p] < lo) lo = W[r * k + i1 + p];\n          if (W[r * k + i1 + p] > hi) hi = W[r * k + i1 + p];"),
+    "gptq_dead_kept": ("w[c] = (dead && dead[c]) ? 0.0f : W[r * k + c];", "w[c] = W[r * k + c];"),
     "compact_zero_bits_always_4": ("int oracle_compact_zero_bits(int bits) { return bits <= 4 ? 4 : 8; }",
                                    "int oracle_compact_zero_bits(int bits) { return 4; }"),
 }
@@ -79,7 +90,7 @@ def _pin_calls():
     calls = []
     for mod in (test_oracle_quant, test_oracle_pack, test_oracle_gemm,
                 test_oracle_fidelity, test_oracle_gamma, test_oracle_topk, test_oracle_mckp,
-                test_oracle_compact):
+                test_oracle_compact, test_oracle_gptq32):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue

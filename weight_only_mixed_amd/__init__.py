@@ -68,6 +68,12 @@ def lib():
         L.slq_gptq_workspace_bytes.restype = _sz
         L.slq_gptq_quantize.argtypes = [_vp, _vp, _i64, _i64, _int, _int, ctypes.c_double, _pp, _vp,
                                         _vp, _vp]
+        L.slq_gptq_factor_workspace_bytes.argtypes = [_i64]
+        L.slq_gptq_factor_workspace_bytes.restype = _sz
+        L.slq_gptq_factor.argtypes = [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp]
+        L.slq_gptq_columns_workspace_bytes.argtypes = [_i64, _i64]
+        L.slq_gptq_columns_workspace_bytes.restype = _sz
+        L.slq_gptq_columns.argtypes = [_vp, _vp, _vp, _i64, _i64, _int, _int, _pp, _vp, _vp]
         L.slq_mckp_workspace_bytes.argtypes = [_i64, _i64]
         L.slq_mckp_workspace_bytes.restype = _sz
         L.slq_mckp_search.argtypes = [_vp, _vp, _i64, ctypes.c_int32, _i64, ctypes.c_double, _vp,
@@ -263,6 +269,35 @@ def slq_gptq_quantize(W: torch.Tensor, H: torch.Tensor, bits: int, damp: float =
                                    ctypes.byref(desc), _ptr(U), _ptr(ws), _stream(W)),
            "slq_gptq_quantize")
     return pw, U
+
+
+def slq_gptq_factor(H: torch.Tensor, damp: float = 0.01, with_u64: bool = False):
+    """The GPTQ inverse-Hessian factor of H[k][k] (fp32, device): U fp32
+    [k][k], the dead-input mask uint8 [k], and U in fp64 on request."""
+    assert H.dtype == torch.float32 and H.is_contiguous()
+    k = H.shape[0]
+    U = torch.empty((k, k), dtype=torch.float32, device=H.device)
+    dead = torch.empty(k, dtype=torch.uint8, device=H.device)
+    U64 = torch.empty((k, k), dtype=torch.float64, device=H.device) if with_u64 else None
+    ws = workspace(lib().slq_gptq_factor_workspace_bytes(k), H.device, "gptq_factor")
+    _check(lib().slq_gptq_factor(_ptr(H), k, float(damp), _ptr(U), _ptr(dead), _ptr(U64), _ptr(ws),
+                                 _stream(H)), "slq_gptq_factor")
+    return U, dead, U64
+
+
+def slq_gptq_columns(W: torch.Tensor, U: torch.Tensor, bits: int, dead: torch.Tensor | None = None):
+    """The GPTQ column pass of fp32 W[n][k] given the fp32 factor U[k][k] and
+    an optional dead-input mask (uint8 [k]): a PackedWeight (fp32 metadata)."""
+    assert W.dtype == torch.float32 and U.dtype == torch.float32
+    assert W.is_contiguous() and U.is_contiguous()
+    assert dead is None or (dead.dtype == torch.uint8 and dead.is_contiguous())
+    n, k = W.shape
+    pw = alloc_packed(n, k, bits, W.device)
+    desc = pw.c()
+    ws = workspace(lib().slq_gptq_columns_workspace_bytes(n, k), W.device, "gptq_columns")
+    _check(lib().slq_gptq_columns(_ptr(W), _ptr(U), _ptr(dead), n, k, bits, GROUP,
+                                  ctypes.byref(desc), _ptr(ws), _stream(W)), "slq_gptq_columns")
+    return pw
 
 
 def slq_mckp_search(sizes: torch.Tensor, costs: torch.Tensor, W: int, tau: float,

@@ -17,6 +17,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # per-source extra flags: quantization must be bit-exact IEEE (no contraction)
 EXTRA = {"quantize.hip": ["-ffp-contract=off"],
+         # GPTQ's column pass matches the oracle operation for operation: every
+         # fused multiply-add is written out, nothing else may be contracted
+         "gptq.hip": ["-ffp-contract=off"],
          # MFMA results in VGPRs: the decode epilogue reads them with plain VALU ops
          "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 SOURCES = ["quantize.hip", "gemv.hip", "gemm.hip", "fidelity.hip", "mckp.hip", "gptq.hip", "slq_abi.cpp"]

@@ -13,13 +13,16 @@
 //     right-looking Cholesky (64 x 64 diagonal blocks in LDS, a panel solve and
 //     a tiled trailing update), and L is inverted by right-looking block
 //     substitution (every step a grid of tile updates).
-//  3. Columns in groups of 128 (the lazy batch is the group): per weight row,
-//     one lane takes the group's 128 current weights into registers, computes
-//     the group's scale and zero point from them (the plain quantizer's fp32
-//     steps), and for each column quantizes it, divides the error by U_ii and
-//     moves the group's later columns by err * U_ij (U read as wave-uniform
-//     scalars).  A tiled GEMM then moves every later column of the layer by
-//     the group's errors times the matching block of U.
+//  3. Columns in groups of 128 (the lazy batch is the group), in fp32 with
+//     one rounding per operation (built without contraction): per weight row,
+//     a team of lanes holds the group's 128 current weights, computes the
+//     group's scale and zero point from them (the plain quantizer's steps),
+//     and for each column i quantizes it, takes e_i = (w_i - w_hat_i) / U_ii
+//     and moves the group's later columns by w_j = fma(-e_i, U_ij, w_j).  A
+//     tiled update then moves every later column c of the layer once:
+//     w_c -= a_c, a_c the fma chain of e_p * U[i1 + p][c] over p = 0..127.
+//  Steps 1-2 (the factor) and 3 (the column pass) are separate entry points
+//  as well, so one factor serves the layer at every bit-width.
 #include <cmath>
 
 #include "launch.h"
@@ -44,14 +47,17 @@ __device__ __forceinline__ double block_sum(double v, double *lds) {
   return t;
 }
 
-// mean of the diagonal after dead inputs get 1 (one workgroup, fixed order)
+// mean of the diagonal after dead inputs get 1 (one workgroup, fixed order),
+// and the dead-input mask (H_ii == 0: the input never fires)
 __global__ __launch_bounds__(kThr) void diag_mean_kernel(const float *__restrict__ H, int64_t k,
-                                                         double *__restrict__ stat) {
+                                                         double *__restrict__ stat,
+                                                         uint8_t *__restrict__ dead) {
   __shared__ double lds[kThr / kWave];
   double s = 0.0;
   for (int64_t i = threadIdx.x; i < k; i += kThr) {
     const float h = H[i * k + i];
     s += h == 0.0f ? 1.0 : (double)h;
+    dead[i] = h == 0.0f ? 1 : 0;
   }
   const double t = block_sum(s, lds);
   if (threadIdx.x == 0) stat[0] = t / (double)k;
@@ -73,14 +79,14 @@ __global__ __launch_bounds__(kThr) void prep_kernel(const float *__restrict__ H,
   A[e] = h;
 }
 
-// working weights: dead input columns zeroed
+// working weights: dead input columns zeroed (no mask: none is dead)
 __global__ __launch_bounds__(kThr) void wcopy_kernel(const float *__restrict__ W,
-                                                     const float *__restrict__ H, int64_t n,
+                                                     const uint8_t *__restrict__ dead, int64_t n,
                                                      int64_t k, float *__restrict__ Wk) {
   const int64_t e = (int64_t)blockIdx.x * kThr + threadIdx.x;
   if (e >= n * k) return;
   const int64_t c = e % k;
-  Wk[e] = H[c * k + c] == 0.0f ? 0.0f : W[e];
+  Wk[e] = dead && dead[c] ? 0.0f : W[e];
 }
 
 // Cholesky of the diagonal block at j0: one wavefront, lane i holds row i of
@@ -501,30 +507,34 @@ hipError_t group_launch(float *Wk, const float *Uf, int64_t n, int64_t k, int64_
 
 }  // namespace
 
-// Workspace: A, X fp64 [k][k] | Uf fp32 [k][k] | Wk fp32 [n][k] | err fp32 [n][128] |
-// gap | stat | Dinv fp64 [k/64][64][64]
-size_t gptq_workspace(int64_t n, int64_t k) {
-  const size_t b = (size_t)k * k * 8 * 2 + (size_t)k * k * 4 + (size_t)n * k * 4 +
-                   (size_t)n * kGroup * 4 + 256 + 256 + (size_t)k * kNb * 8;
+// Factor workspace: A, X fp64 [k][k] | stat (256 B) | Dinv fp64 [k/64][64][64].
+size_t gptq_factor_workspace(int64_t k) {
+  const size_t b = (size_t)k * k * 8 * 2 + 256 + (size_t)k * kNb * 8;
   return (b + 255) / 256 * 256;
 }
 
-hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int bits, double damp,
-                       uint32_t *codes, float *scales, uint8_t *zeros, double *u_out, void *ws,
-                       hipStream_t s) {
+// Column-pass workspace: Wk fp32 [n][k] | err fp32 [n][128].
+size_t gptq_columns_workspace(int64_t n, int64_t k) {
+  const size_t b = (size_t)n * k * 4 + (size_t)n * kGroup * 4;
+  return (b + 255) / 256 * 256;
+}
+
+// Whole pipeline: Uf fp32 [k][k] | dead [k] (256-byte padded) | factor | column pass.
+size_t gptq_workspace(int64_t n, int64_t k) {
+  const size_t uf = (size_t)k * k * 4, dead = ((size_t)k + 255) / 256 * 256;
+  return uf + dead + gptq_factor_workspace(k) + gptq_columns_workspace(n, k);
+}
+
+hipError_t launch_gptq_factor(const float *H, int64_t k, double damp, float *Uf, uint8_t *dead,
+                              double *u_out, void *ws, hipStream_t s) {
   double *A = static_cast<double *>(ws);
   double *X = A + k * k;
-  float *Uf = reinterpret_cast<float *>(X + k * k);
-  float *Wk = Uf + k * k;
-  float *err = Wk + n * k;
-  double *stat = reinterpret_cast<double *>(err + n * kGroup + 64);   // 256-byte gap
-  double *Dinv = stat + 32;                                            // [k / 64][64][64]
+  double *stat = X + k * k;                // 256 bytes
+  double *Dinv = stat + 32;                // [k / 64][64][64]
   hipError_t e;
   const unsigned kk = (unsigned)((k * k + kThr - 1) / kThr);
-  hipLaunchKernelGGL(diag_mean_kernel, dim3(1), dim3(kThr), 0, s, H, k, stat);
+  hipLaunchKernelGGL(diag_mean_kernel, dim3(1), dim3(kThr), 0, s, H, k, stat, dead);
   hipLaunchKernelGGL(prep_kernel, dim3(kk), dim3(kThr), 0, s, H, k, damp, stat, A);
-  hipLaunchKernelGGL(wcopy_kernel, dim3((unsigned)((n * k + kThr - 1) / kThr)), dim3(kThr), 0, s,
-                     W, H, n, k, Wk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nbk = k / kNb;
   for (int64_t b = 0; b < nbk; ++b) {
@@ -549,6 +559,17 @@ hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(u_kernel, dim3(kk), dim3(kThr), 0, s, X, k, Uf, u_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gptq_columns(const float *W, const float *Uf, const uint8_t *dead, int64_t n,
+                               int64_t k, int bits, uint32_t *codes, float *scales,
+                               uint8_t *zeros, void *ws, hipStream_t s) {
+  float *Wk = static_cast<float *>(ws);
+  float *err = Wk + n * k;
+  hipError_t e;
+  hipLaunchKernelGGL(wcopy_kernel, dim3((unsigned)((n * k + kThr - 1) / kThr)), dim3(kThr), 0, s,
+                     W, dead, n, k, Wk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t G = k / kGroup;
   for (int64_t g = 0; g < G; ++g) {
@@ -572,6 +593,19 @@ hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int
     }
   }
   return hipSuccess;
+}
+
+hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int bits, double damp,
+                       uint32_t *codes, float *scales, uint8_t *zeros, double *u_out, void *ws,
+                       hipStream_t s) {
+  char *p = static_cast<char *>(ws);
+  float *Uf = reinterpret_cast<float *>(p);
+  uint8_t *dead = reinterpret_cast<uint8_t *>(p + (size_t)k * k * 4);
+  char *fws = reinterpret_cast<char *>(dead) + ((size_t)k + 255) / 256 * 256;
+  char *cws = fws + gptq_factor_workspace(k);
+  hipError_t e = launch_gptq_factor(H, k, damp, Uf, dead, u_out, fws, s);
+  if (e != hipSuccess) return e;
+  return launch_gptq_columns(W, Uf, dead, n, k, bits, codes, scales, zeros, cws, s);
 }
 
 }  // namespace slq

@@ -33,6 +33,9 @@ struct GemvPlan {
   bool xd;         // activations loaded by each lane with the weight batches (mt == 1)
   bool rows;       // 17..64 activation rows: row-split kernel, 64 rows per workgroup
   bool mk;         // 33..64 activation rows, mid-width layer: gemv_mk_kernel, 64 * nt rows per workgroup
+  bool s1;         // one m-tile, streaming kernel gemv_s1_kernel (b = ring depth, xd = activations per lane)
+  int xr;          // gemv_s1_kernel: activation chunks per thread staged into LDS
+  int ng;          // gemv_s1_kernel: most groups one wavefront streams
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);
@@ -59,6 +62,14 @@ hipError_t launch_row_lse(const float *a, int64_t rows, int64_t vocab, double *l
 hipError_t launch_ear_kl(const float *a, const float *b, int64_t rows, int64_t vocab, float *ear,
                          float *kl, double *means, void *ws, hipStream_t s);
 size_t gptq_workspace(int64_t n, int64_t k);
+size_t gptq_factor_workspace(int64_t k);
+size_t gptq_columns_workspace(int64_t n, int64_t k);
+// U fp32 [k][k] upper with U^T U = (H + damping)^-1, dead [k] = (H_ii == 0)
+hipError_t launch_gptq_factor(const float *H, int64_t k, double damp, float *Uf, uint8_t *dead,
+                              double *u_out, void *ws, hipStream_t s);
+hipError_t launch_gptq_columns(const float *W, const float *Uf, const uint8_t *dead, int64_t n,
+                               int64_t k, int bits, uint32_t *codes, float *scales,
+                               uint8_t *zeros, void *ws, hipStream_t s);
 hipError_t launch_gptq(const float *W, const float *H, int64_t n, int64_t k, int bits, double damp,
                        uint32_t *codes, float *scales, uint8_t *zeros, double *u_out, void *ws,
                        hipStream_t s);

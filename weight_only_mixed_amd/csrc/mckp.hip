@@ -2,8 +2,8 @@
 // table for every budget, then the smallest budget that meets a target
 // (gist.science summary "Statistically-Lossless Quantization of Large
 // Language Models", 3. The SLQ Pipeline: allocation as a multiple-choice
-// knapsack solved exactly under a bit budget; SLQ README, Pipeline: the solve
-// is binary-searched down to the target).
+// knapsack solved exactly under a bit budget; SLQ README, Pipeline: the budget
+// is found by bisection until the target is met).
 //
 // Item l takes one of nb options; option j occupies s_lj budget units and
 // costs c_lj.  best_l(w) = least cost of items 0..l within budget w:

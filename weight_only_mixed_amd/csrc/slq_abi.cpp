@@ -182,7 +182,10 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
   if (m <= kDecodeMaxM) {
     const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
     const char *cm = w->meta == SLQ_META_COMPACT ? "true" : "false";
-    if (p.mk)
+    if (p.s1)
+      snprintf(buf, sizeof buf, "slq::gemv_s1_kernel<%d, %d, %d, %d, %d, %d, %s, %s>", w->bits, p.nt,
+               p.wv, p.b, p.ng, p.xr, p.xd ? "false" : "true", cm);
+    else if (p.mk)
       snprintf(buf, sizeof buf, "slq::gemv_mk_kernel<%d, %d, %d, %s>", w->bits, p.mt, p.nt, cm);
     else if (p.rows)
       snprintf(buf, sizeof buf, "slq::gemv_rows_kernel<%d, %d, %s>", w->bits, p.mt, cm);
@@ -318,6 +321,70 @@ slq_status slq_gptq_quantize(const float *W, const float *H, int64_t n, int64_t 
   return from_hip(slq::launch_gptq(W, H, n, k, bits, damp, out->codes,
                                    static_cast<float *>(out->scales), out->zeros, u_out, workspace,
                                    static_cast<hipStream_t>(stream)));
+}
+
+static bool gptq_k_ok(int64_t k) { return k >= kGroupSize && k <= 32768 && k % kGroupSize == 0; }
+
+size_t slq_gptq_factor_workspace_bytes(int64_t k) {
+  if (!gptq_k_ok(k)) return 0;
+  return slq::gptq_factor_workspace(k);
+}
+
+slq_status slq_gptq_factor(const float *H, int64_t k, double damp, float *U, uint8_t *dead,
+                           double *u_out, void *workspace, slq_stream stream) {
+  if (!gptq_k_ok(k) || !(damp > 0.0) || !std::isfinite(damp)) return SLQ_EINVAL;
+  if (!H || !U || !dead || !workspace) return SLQ_EINVAL;
+  if (!aligned(H, 16) || !aligned(U, 16) || !aligned(workspace, 256) || (u_out && !aligned(u_out, 8)))
+    return SLQ_EINVAL;
+  const size_t hb = (size_t)(k * k) * 4;
+  const void *outs[4] = {U, dead, u_out, workspace};
+  const size_t outb[4] = {(size_t)(k * k) * 4, (size_t)k, u_out ? (size_t)(k * k) * 8 : 0,
+                          slq_gptq_factor_workspace_bytes(k)};
+  for (int i = 0; i < 4; ++i) {
+    if (!outs[i]) continue;
+    if (overlap(outs[i], outb[i], H, hb)) return SLQ_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j] && overlap(outs[i], outb[i], outs[j], outb[j])) return SLQ_EINVAL;
+  }
+  return from_hip(slq::launch_gptq_factor(H, k, damp, U, dead, u_out, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t slq_gptq_columns_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 1 || n >= kMaxDim || !gptq_k_ok(k) || n * k >= kMaxDim * 64) return 0;
+  return slq::gptq_columns_workspace(n, k);
+}
+
+slq_status slq_gptq_columns(const float *W, const float *U, const uint8_t *dead, int64_t n,
+                            int64_t k, int bits, int group, slq_packed *out, void *workspace,
+                            slq_stream stream) {
+  if (!out || bits < 2 || bits > 8 || group <= 0) return SLQ_EINVAL;
+  if (group != kGroupSize) return SLQ_ENOTSUP;
+  if (n < 1 || n >= kMaxDim || !gptq_k_ok(k) || n * k >= kMaxDim * 64) return SLQ_EINVAL;
+  if (!meta_ok(out->meta)) return SLQ_EINVAL;
+  if (out->meta != SLQ_META_F32) return SLQ_ENOTSUP;
+  if (!W || !U || !workspace || !out->codes || !out->scales || !out->zeros) return SLQ_EINVAL;
+  if (!aligned(W, 16) || !aligned(U, 16) || !aligned(workspace, 256) || !aligned(out->codes, 16) ||
+      !aligned(out->scales, 16) || !aligned(out->zeros, 4))
+    return SLQ_EINVAL;
+  const PackedSizes sz = sizes_of(n, k, bits, group, out->meta);
+  const void *in[3] = {W, U, dead};
+  const size_t inb[3] = {(size_t)(n * k) * 4, (size_t)(k * k) * 4, dead ? (size_t)k : 0};
+  const void *outs[4] = {out->codes, out->scales, out->zeros, workspace};
+  const size_t outb[4] = {sz.codes, sz.scales, sz.zeros, slq_gptq_columns_workspace_bytes(n, k)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (in[j] && overlap(outs[i], outb[i], in[j], inb[j])) return SLQ_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return SLQ_EINVAL;
+  }
+  out->bits = bits;
+  out->group = group;
+  out->n = n;
+  out->k = k;
+  return from_hip(slq::launch_gptq_columns(W, U, dead, n, k, bits, out->codes,
+                                           static_cast<float *>(out->scales), out->zeros,
+                                           workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t slq_mckp_workspace_bytes(int64_t L, int64_t W) {
