@@ -8,7 +8,7 @@ order on both sides (oracle.c, oracle_gptq_columns; include/slq.h,
 slq_gptq_columns), so its integer outputs are compared exactly: codes, scale
 bit patterns and zero points.  Given the same fp32 factor the two column
 passes must agree bit for bit.  From a Hessian the two sides' factors (fp64,
-different routes) may round to fp32 one unit apart in a few entries; the
+different routes) may round to fp32 differently in a few entries; the
 composed result is then checked by code agreement and layer loss, and
 exactly wherever the rounded factors are equal."""
 import numpy as np
@@ -87,21 +87,21 @@ def test_identity_hessian_is_round_to_nearest(bits):
     assert_same_codes((q, s, z), oracle.quantize(W, bits), f"identity bits={bits}")
 
 
-def ulp_diff(a, b):
-    """Elementwise distance in units in the last place of two fp32 arrays."""
-    ia = a.view(np.int32).astype(np.int64)
-    ib = b.view(np.int32).astype(np.int64)
-    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
-    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
-    return np.abs(ia - ib)
+def factor_gap(a, b):
+    """Entries where two fp32 factors differ, and the largest difference in
+    units of 2^-24 of the factor's largest magnitude (one rounding step of the
+    largest entries; small entries that differ by a few of their own ulps count
+    well below one)."""
+    d = np.abs(a.astype(np.float64) - b.astype(np.float64))
+    return int((d > 0).sum()), float(d.max() / (np.abs(b).max() * 2.0 ** -24))
 
 
 @pytest.mark.parametrize("bits", [3, 4, 8])
 def test_against_oracle(bits):
     """From a correlated Hessian.  The factor is floating point: the two sides
     compute it by different fp64 routes (within 1e-9), so its fp32 rounding
-    may differ by one unit in the last place in a few entries; every other
-    entry is equal.  The column pass is exact given its factor (the test
+    may differ in a few entries by at most one rounding step of the largest
+    entries; every other entry is equal.  The column pass is exact given its factor (the test
     above), so codes can differ only through those entries: almost all codes
     are equal, and the layer loss matches to 1e-4."""
     n, k = 96, 1024
@@ -110,16 +110,16 @@ def test_against_oracle(bits):
     Uf, _, _ = slq.slq_gptq_factor(gpu(H))
     q, s, z, _ = gpu_gptq(W, H, bits)
     qr, sr, zr, Ur = G.gptq32(W, H, bits)
-    d = ulp_diff(Uf.cpu().numpy(), Ur.astype(np.float32))
+    ndiff, gap = factor_gap(Uf.cpu().numpy(), Ur.astype(np.float32))
     agree = (q == qr).mean()
     l_gpu = G.proxy_loss(W, oracle.dequantize(q, s, z), H)
     l_ref = G.proxy_loss(W, oracle.dequantize(qr, sr, zr), H)
     q0, s0, z0 = oracle.quantize(W, bits)
     l_rtn = G.proxy_loss(W, oracle.dequantize(q0, s0, z0), H)
-    say(f"gptq bits={bits}: factor entries off by one ulp {int((d == 1).sum())} (max {int(d.max())}); "
+    say(f"gptq bits={bits}: {ndiff} factor entries differ (largest gap {gap:.3f} of 2^-24 max|U|); "
         f"codes agree {agree:.6f}; loss {l_gpu:.6g} vs {l_ref:.6g}, rtn {l_rtn:.4g}")
-    assert d.max() <= 1 and (d > 0).mean() <= 1e-4
-    if d.max() == 0:
+    assert gap <= 1.0 and ndiff <= 1e-4 * k * k
+    if ndiff == 0:
         assert_same_codes((q, s, z), (qr, sr, zr), f"gptq bits={bits}")
     assert agree >= 0.9999
     assert abs(l_gpu - l_ref) <= 1e-4 * l_ref
@@ -158,8 +158,8 @@ def test_full_layer_column_pass_sampled_rows():
 
 def test_full_q_layer_from_hessian_sampled_rows():
     """The whole pipeline on the 4096 x 4096 layer with a 4096^2 Hessian: the
-    fp32 factors differ by at most one unit in the last place in a few
-    entries, and the codes of 24 sampled rows agree with the oracle's."""
+    fp32 factors differ in a few entries by at most one rounding step of the
+    largest entries, and the codes of 24 sampled rows agree with the oracle's."""
     k = 4096
     H = S.gptq_hessian(k, 91, tokens=2 * k)
     W = S.skewed_weights(4096, k, 92, row_offset_std=0.005)
@@ -167,11 +167,11 @@ def test_full_q_layer_from_hessian_sampled_rows():
     q, s, z, _ = gpu_gptq(W, H, 4)
     rows = np.random.default_rng(93).choice(4096, 24, replace=False)
     qr, sr, zr, Ur = G.gptq32(W[rows], H, 4)
-    d = ulp_diff(Uf.cpu().numpy(), Ur.astype(np.float32))
+    ndiff, gap = factor_gap(Uf.cpu().numpy(), Ur.astype(np.float32))
     agree = (q[rows] == qr).mean()
-    say(f"gptq 4096x4096 sampled: {int((d > 0).sum())} factor entries off by one ulp "
-        f"(max {int(d.max())}); codes agree {agree:.6f}")
-    assert d.max() <= 1 and (d > 0).mean() <= 1e-4
-    if d.max() == 0:
+    say(f"gptq 4096x4096 sampled: {ndiff} factor entries differ (largest gap {gap:.3f} of 2^-24 "
+        f"max|U|); codes agree {agree:.6f}")
+    assert gap <= 1.0 and ndiff <= 1e-4 * k * k
+    if ndiff == 0:
         assert_same_codes((q[rows], s[rows], z[rows]), (qr, sr, zr), "4096x4096 from H")
     assert agree >= 0.9999

@@ -35,7 +35,13 @@
 //  * Split-K across workgroups writes fp32 partials with device-coherent
 //    stores; the last workgroup of each row block (relaxed atomic ticket after
 //    the stores have completed) sums them in split order, so results are
-//    deterministic, and resets its ticket.
+//    deterministic, and resets its ticket.  Every access to the partials is an
+//    agent-scope atomic: the stores are written through to the device's
+//    coherence point and the kernel waits for their completion before taking
+//    the ticket, and the last workgroup's loads read from that point, so no
+//    cache of another chiplet can hold a stale copy.  The formal form, an
+//    acquire-release ticket, adds an L2 writeback and invalidate per workgroup
+//    and measured 0.3-7 us slower per launch.
 //  * Three kernels: `gemv_kernel` (any m, the general form above),
 //    `gemv_rows_kernel` (33..64 rows on wide or deep layers: the waves split
 //    rows and share each group's activations) and `gemv_mk_kernel` (33..64
@@ -925,284 +931,6 @@ __global__ __launch_bounds__(kThreads) void gemv_mk_kernel(
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One m-tile (m <= 16), streaming form: `gemv_s1_kernel`.
-// A workgroup of WV wavefronts owns 16*NT weight rows over one k-block and
-// the waves split the k-block into contiguous group ranges.  The vector-memory
-// counter retires loads in issue order, so the prologue issues, in order: the
-// k-block's activation chunks (XL: into registers, XR chunks of 32 values per
-// thread), then each wave's first D groups of codes with their scales and zero
-// points, and only then writes the activations to LDS in fragment order: that
-// write waits for the activation loads alone while the code ring is in
-// flight.  The main loop consumes one group per step from a ring of D
-// register slots and refills the slot D groups ahead.  All loads are buffer
-// loads, and a slot past the wave's last group (or a row past n) gets an
-// offset past the resource: the load returns zeros without touching memory,
-// so every path issues the same loads and the waits stay partial.  Without XL
-// each slot also carries the lane's 32 activations of its group.  Zero points
-// fold into a second MFMA chain against the pair the codes would unpack to if
-// they all equalled z (zero_pair), so t = C - S' is exact for all-zero groups
-// and one-hot x.
-template <int BITS, int NT, bool XL>
-struct S1Slot {
-  Chunk<BITS> c[NT];
-  uint32_t s[NT];   // scale bits (fp32, or binary16 in the low half)
-  uint32_t z[NT];   // the aligned word holding the zero point (byte or nibble)
-  u32x4_t xa[XL ? 1 : 4];
-};
-
-template <int BITS>
-__device__ __forceinline__ Chunk<BITS> buf_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  Chunk<BITS> c;
-  if constexpr (BITS == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    c.w[0] = v[0];
-    c.w[1] = v[1];
-  } else if constexpr (BITS == 3) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
-    c.w[0] = v[0];
-    c.w[1] = v[1];
-    c.w[2] = v[2];
-  } else {
-    const u32x4_t v = buf_b128(r, off);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c.w[i] = v[i];
-    if constexpr (BITS == 5) {
-      c.w[4] = buf_b32(r, off + 16);
-    } else if constexpr (BITS == 6) {
-      const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off + 16, 0, 0);
-      c.w[4] = u[0];
-      c.w[5] = u[1];
-    } else if constexpr (BITS == 7) {
-      const auto u = __builtin_amdgcn_raw_buffer_load_b96(r, off + 16, 0, 0);
-      c.w[4] = u[0];
-      c.w[5] = u[1];
-      c.w[6] = u[2];
-    } else if constexpr (BITS == 8) {
-      const u32x4_t u = buf_b128(r, off + 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c.w[4 + i] = u[i];
-    }
-  }
-  return c;
-}
-
-template <int BITS, int NT, int WV, int D, int NG, int XR, bool XL, bool CM>
-__global__ __launch_bounds__(WV * kWave) void gemv_s1_kernel(
-    const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
-    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
-    int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
-    unsigned *__restrict__ tickets) {
-  constexpr int TH = WV * kWave;
-  constexpr bool NIB = CM && BITS <= 4;          // zero points as nibbles
-  constexpr uint32_t ES = CM ? 2u : 4u;          // scale bytes
-  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int col = lane & 15, kq = lane >> 4;
-  const int G = K / kGroup;
-  const int kb = blockIdx.y;
-  const int gbase = kb * GW;
-  const int gcount = min(GW, G - gbase);
-  const int xpitch = gcount * 64 + 4;           // words per activation row (+16 B vs bank conflicts)
-  const int n0 = blockIdx.x * 16 * NT;
-  const int rows = min(16 * NT, N - n0);
-  const uint32_t rowb = (uint32_t)K * BITS / 8;  // code bytes per weight row
-  const int ga = wave * gcount / WV, gz = (wave + 1) * gcount / WV;
-
-  const auto rx = buf_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-  const auto rc = buf_rsrc(codes + (int64_t)n0 * (rowb / 4), (uint32_t)rows * rowb);
-  const int64_t mi0 = (int64_t)n0 * G;           // first group index of the workgroup's rows
-  const auto rs = buf_rsrc(static_cast<const char *>(scales) + mi0 * ES, (uint32_t)(rows * G) * ES);
-  // zero points are read as the aligned word holding them: the range is
-  // rounded up to whole words (the word of a valid byte lies in the array's
-  // page; a word reaching past the range would read as zero)
-  const uint32_t zbytes = NIB ? (uint32_t)(rows * G + 1) / 2 : (uint32_t)(rows * G);
-  const auto rz = buf_rsrc(zeros + (NIB ? mi0 / 2 : mi0), (zbytes + 3u) & ~3u);
-
-  // 1. activation chunks (m, group, quarter) of the k-block
-  const int xchunks = M * gcount * 4;
-  u32x4_t xv[XL ? XR : 1][4];
-  if constexpr (XL) {
-#pragma unroll
-    for (int r = 0; r < XR; ++r) {
-      const int c = (int)threadIdx.x + r * TH;
-      const int m = c / (gcount * 4), cc = c % (gcount * 4);
-      const uint32_t off = c < xchunks ? ((uint32_t)m * K + gbase * kGroup + 32 * cc) * 2u : kNoLoad;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xv[r][q] = buf_b128(rx, off + 16 * q);
-    }
-  }
-
-  // 2. the code ring: lane (col, kq) reads row 16 t + col, quarter kq of each group
-  uint32_t cofs[NT], mofs[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    cofs[t] = (uint32_t)(16 * t + col) * rowb + (uint32_t)gbase * 16 * BITS + kq * 4 * BITS;
-    mofs[t] = (uint32_t)((16 * t + col) * G + gbase);
-  }
-  const uint32_t xofs = ((uint32_t)min(col, M - 1) * K + gbase * kGroup + 32 * kq) * 2u;
-#ifndef SLQ_S1_GLOBAL
-#define SLQ_S1_GLOBAL 0
-#endif
-  const MetaRd<BITS, CM> md{scales, zeros};
-  const uint32_t *crow[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-    crow[t] = codes + (int64_t)min(n0 + 16 * t + col, N - 1) * (rowb / 4) + (int64_t)gbase * 4 * BITS + kq * BITS;
-  auto load = [&](S1Slot<BITS, NT, XL> &o, int g) {
-    const bool live = g < gz;
-    if constexpr (SLQ_S1_GLOBAL) {
-      const int gg = min(g, gz - 1);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        o.c[t] = load_chunk<BITS>(crow[t] + (int64_t)gg * 4 * BITS);
-        const int64_t i = (int64_t)min(n0 + 16 * t + col, N - 1) * G + gbase + gg;
-        o.s[t] = CM ? (uint32_t)static_cast<const uint16_t *>(scales)[i] : __float_as_uint(static_cast<const float *>(scales)[i]);
-        o.z[t] = zeros[NIB ? i >> 1 : i];
-      }
-      return;
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      o.c[t] = buf_chunk<BITS>(rc, live ? cofs[t] + (uint32_t)g * 16 * BITS : kNoLoad);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint32_t i = mofs[t] + g;
-      if constexpr (CM)
-        o.s[t] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? i * 2u : kNoLoad, 0, 0);
-      else
-        o.s[t] = buf_b32(rs, live ? i * 4u : kNoLoad);
-      const uint32_t zb = NIB ? i >> 1 : i;   // byte holding the zero point
-      o.z[t] = buf_b32(rz, live ? zb & ~3u : kNoLoad);   // the word; the byte is taken at use
-    }
-    if constexpr (!XL) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o.xa[q] = buf_b128(rx, live ? xofs + g * 256u + 16 * q : kNoLoad);
-    }
-  };
-  S1Slot<BITS, NT, XL> ring[D];
-#pragma unroll
-  for (int j = 0; j < D; ++j) load(ring[j], ga + j);
-
-  // 3. activations to LDS in fragment order
-  if constexpr (XL) {
-#pragma unroll
-    for (int r = 0; r < XR; ++r) {
-      const int c = (int)threadIdx.x + r * TH;
-      if (c < xchunks) {
-        const int m = c / (gcount * 4), cc = c % (gcount * 4);
-        uint32_t X[16], F[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          X[4 * q + 0] = xv[r][q][0];
-          X[4 * q + 1] = xv[r][q][1];
-          X[4 * q + 2] = xv[r][q][2];
-          X[4 * q + 3] = xv[r][q][3];
-        }
-        x_fragments<BITS>(X, F);
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(lds + m * xpitch + cc * 16);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = u32x4_t{F[4 * q], F[4 * q + 1], F[4 * q + 2], F[4 * q + 3]};
-      }
-    }
-    __syncthreads();
-  }
-
-  const uint32_t magic = in_vgpr(kMagic2);
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const S1Slot<BITS, NT, XL> &o, int g) {
-    u32x4_t A[4];
-    if constexpr (XL) {
-      const u32x4_t *src =
-          reinterpret_cast<const u32x4_t *>(lds + min(col, M - 1) * xpitch + (g * 4 + kq) * 16);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) A[r] = src[r];
-    } else {
-      uint32_t X[16], F[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        X[4 * q + 0] = o.xa[q][0];
-        X[4 * q + 1] = o.xa[q][1];
-        X[4 * q + 2] = o.xa[q][2];
-        X[4 * q + 3] = o.xa[q][3];
-      }
-      x_fragments<BITS>(X, F);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) A[r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      uint32_t p[16];
-      unpack_pairs<BITS>(o.c[t], p, magic);
-      f32x4_t C = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        C = mfma16(A[r], u32x4_t{p[4 * r], p[4 * r + 1], p[4 * r + 2], p[4 * r + 3]}, C);
-      const uint32_t zi = mofs[t] + g;       // this lane's group index
-      uint32_t z = SLQ_S1_GLOBAL ? o.z[t] : (o.z[t] >> (8 * ((NIB ? zi >> 1 : zi) & 3u))) & 0xFFu;
-      if constexpr (NIB) z = (z >> ((zi & 1u) * 4)) & 15u;
-      const uint32_t zp = zero_pair<BITS>(z);
-      const u32x4_t zb = u32x4_t{zp, zp, zp, zp};
-      f32x4_t Z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Z = mfma16(A[r], zb, Z);
-      const float sc = CM ? f16_bits_to_f32(o.s[t] & 0xFFFFu) : __uint_as_float(o.s[t]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(sc, C[v] - Z[v], acc[t][v]);
-    }
-  };
-
-  // 4. stream: one group per step, the slot refilled D groups ahead.  Fully
-  // unrolled over the NG steps a wave can have (no loop, so the slots keep
-  // their registers and no copy waits for a load in flight); every step issues
-  // its refill, past the last group with the no-load offset.
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    if (ga + j < gz) compute(ring[j % D], ga + j);
-    if (j + D < NG) load(ring[j % D], ga + j + D);
-  }
-
-  // 5. the WV waves' partials meet in LDS (reusing the activation area)
-  if constexpr (XL) __syncthreads();
-  f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) red[(wave * NT + t) * kWave + lane] = acc[t];
-  __syncthreads();
-  for (int t = wave; t < NT; t += WV) {
-    f32x4_t sum = red[t * kWave + lane];
-#pragma unroll
-    for (int w = 1; w < WV; ++w) sum += red[(w * NT + t) * kWave + lane];
-    const int n = n0 + 16 * t + col;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * kq + v;
-      if (m >= M || n >= N) continue;
-      if (ksplits == 1) {
-        y[(int64_t)m * N + n] = sum[v];
-      } else {
-        __hip_atomic_store(&partial[((int64_t)kb * M + m) * N + n], sum[v], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  if (ksplits == 1) return;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  __shared__ unsigned last;
-  if (threadIdx.x == 0) {
-    const unsigned ticket = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-    last = (ticket == (unsigned)ksplits - 1u);
-  }
-  __syncthreads();
-  if (!last) return;
-  reduce_partials(partial, y, M, N, n0, 16 * NT, ksplits, TH);
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Split-K tickets live in a fixed area at the start of the workspace, so no
 // call's partial sums ever overlap another call's tickets; every completed
 // call leaves all tickets at zero.
@@ -1442,68 +1170,10 @@ hipError_t gemv_mk_nt(const uint16_t *x, const uint32_t *codes, const void *scal
   return gemv_mk_launch<BITS, MT, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
 }
 
-#ifndef SLQ_S1_NT
-#define SLQ_S1_NT 1
-#endif
-#ifndef SLQ_S1_WV
-#define SLQ_S1_WV 8
-#endif
-#ifndef SLQ_S1_D
-#define SLQ_S1_D 4
-#endif
-#ifndef SLQ_S1_XR
-#define SLQ_S1_XR 4
-#endif
-#ifndef SLQ_S1_XL
-#define SLQ_S1_XL 1
-#endif
-#ifndef SLQ_S1_TARGET
-#define SLQ_S1_TARGET 256
-#endif
-#ifndef SLQ_S1_NG
-#define SLQ_S1_NG 16
-#endif
-constexpr int kS1Nt = SLQ_S1_NT, kS1Wv = SLQ_S1_WV, kS1D = SLQ_S1_D, kS1Xr = SLQ_S1_XR, kS1Ng = SLQ_S1_NG;
-constexpr bool kS1Xl = SLQ_S1_XL != 0;
-constexpr int64_t kS1Target = SLQ_S1_TARGET;
-
-size_t gemv_s1_lds_bytes(int64_t m, int gw, bool xl, int wv, int nt) {
-  const size_t xs = xl ? (size_t)m * (gw * 64 + 4) * 4 : 0;
-  const size_t red = (size_t)wv * nt * kWave * 16;
-  return std::max(xs, red) + 16;
-}
-
-template <int BITS, bool CM>
-hipError_t gemv_s1_launch(const uint16_t *x, const uint32_t *codes, const void *scales,
-                          const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
-                          const GemvPlan &plan, hipStream_t st) {
-  float *partial = nullptr;
-  unsigned *tickets = nullptr;
-  if (plan.ksplits > 1) {
-    tickets = static_cast<unsigned *>(ws);
-    partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
-  }
-  const size_t lds = gemv_s1_lds_bytes(m, plan.gw, kS1Xl, kS1Wv, kS1Nt);
-  if (lds > kMaxDynLds) return hipErrorInvalidValue;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&gemv_s1_kernel<BITS, kS1Nt, kS1Wv, kS1D, kS1Ng, kS1Xr, kS1Xl, CM>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDynLds);
-  if (attr != hipSuccess) {
-    (void)hipGetLastError();
-    return attr;
-  }
-  hipLaunchKernelGGL((gemv_s1_kernel<BITS, kS1Nt, kS1Wv, kS1D, kS1Ng, kS1Xr, kS1Xl, CM>),
-                     dim3(plan.nblocks, plan.ksplits), dim3(kS1Wv * kWave), lds, st, x, codes,
-                     scales, zeros, (int)m, (int)n, (int)k, plan.gw, plan.ksplits, y, partial,
-                     tickets);
-  return hipGetLastError();
-}
-
 template <int BITS, bool CM>
 hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      const GemvPlan &plan, hipStream_t st) {
-  if (plan.s1) return gemv_s1_launch<BITS, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
   if (plan.mk) {
     // only the m-tile counts and row tiles the planner can choose are built
     switch (plan.mt) {
@@ -1540,6 +1210,7 @@ hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const void *scale
 }  // namespace
 
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
+  (void)bits;
   GemvPlan p{};
   p.mt = (int)((m + 15) / 16);
   const int64_t G = k / kGroup;
@@ -1548,32 +1219,6 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // activation loads, whose L2 traffic grows with n * k * m / 16; narrower
   // layers and 17..32 rows measured faster with per-lane loads.
   p.wv = kWaves;
-#if defined(SLQ_GEMV_S1) && SLQ_GEMV_S1
-  if (p.mt == 1 && 16 * kS1Nt * k * bits / 8 < ((int64_t)1 << 31) && m * k * 2 < ((int64_t)1 << 31)) {
-    p.s1 = true;
-    p.nt = kS1Nt;
-    p.wv = kS1Wv;
-    p.b = kS1D;
-    p.xd = !kS1Xl;
-    p.xr = kS1Xr;
-    p.ng = kS1Ng;
-    const int64_t nb = (n + 16 * p.nt - 1) / (16 * p.nt);
-    int64_t ks = std::min<int64_t>(std::max<int64_t>(1, (kS1Target + nb - 1) / nb), G);
-    int64_t gw = (G + ks - 1) / ks;
-    while (gw > 1 && ((gw + kS1Wv - 1) / kS1Wv > kS1Ng ||
-                      (kS1Xl && m * gw * 4 > (int64_t)kS1Xr * kS1Wv * kWave) ||
-            (kS1Xl && gemv_s1_lds_bytes(m, (int)gw, true, kS1Wv, kS1Nt) > kMaxDynLds))) {
-      ++ks;
-      gw = (G + ks - 1) / ks;
-    }
-    p.gw = (int)gw;
-    p.ksplits = (int)((G + gw - 1) / gw);
-    p.nblocks = (int)nb;
-    if ((p.nblocks > kMaxTicketBlocks && p.ksplits > 1) || p.ksplits > 65535) p.ksplits = 0;
-    p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
-    return p;
-  }
-#endif
   const bool mk_rows = p.mt >= 4 || (p.mt == 3 && (m >= kMkMinM || k >= kMkDeepK));
   if (p.mt >= kMkMinMt && mk_rows && n >= kMkMinN && n <= kMkMaxN) {
     // 33..64 rows on a mid-width layer: gemv_mk_kernel, one LDS copy of each

@@ -33,9 +33,6 @@ struct GemvPlan {
   bool xd;         // activations loaded by each lane with the weight batches (mt == 1)
   bool rows;       // 17..64 activation rows: row-split kernel, 64 rows per workgroup
   bool mk;         // 33..64 activation rows, mid-width layer: gemv_mk_kernel, 64 * nt rows per workgroup
-  bool s1;         // one m-tile, streaming kernel gemv_s1_kernel (b = ring depth, xd = activations per lane)
-  int xr;          // gemv_s1_kernel: activation chunks per thread staged into LDS
-  int ng;          // gemv_s1_kernel: most groups one wavefront streams
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);

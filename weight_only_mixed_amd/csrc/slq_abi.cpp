@@ -182,10 +182,7 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
   if (m <= kDecodeMaxM) {
     const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
     const char *cm = w->meta == SLQ_META_COMPACT ? "true" : "false";
-    if (p.s1)
-      snprintf(buf, sizeof buf, "slq::gemv_s1_kernel<%d, %d, %d, %d, %d, %d, %s, %s>", w->bits, p.nt,
-               p.wv, p.b, p.ng, p.xr, p.xd ? "false" : "true", cm);
-    else if (p.mk)
+    if (p.mk)
       snprintf(buf, sizeof buf, "slq::gemv_mk_kernel<%d, %d, %d, %s>", w->bits, p.mt, p.nt, cm);
     else if (p.rows)
       snprintf(buf, sizeof buf, "slq::gemv_rows_kernel<%d, %d, %s>", w->bits, p.mt, cm);

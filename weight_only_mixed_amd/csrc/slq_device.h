@@ -98,21 +98,6 @@ struct MetaRd {
   }
 };
 
-// Buffer resources (raw, unstrided): a load whose byte offset is at or past
-// `bytes` returns zeros and makes no memory access, so a loop can issue the
-// same number of loads on every path (the vector-memory counter then allows
-// partial waits) and skip the memory traffic of the loads it does not need.
-constexpr uint32_t kNoLoad = 0x80000000u;   // an offset past every resource here
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t buf_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t buf_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
