@@ -109,7 +109,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default="all", help="extra rows: all, none, or a comma list of "
-                    "quantize,gemm,stack,fidelity,allocation,gptq,gamma,compact")
+                    "config1,ceiling,quantize,gemm,stack,fidelity,allocation,gptq,gamma,compact")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--pmc", default=None, metavar="KERNEL",
@@ -118,6 +118,16 @@ def main():
     ap.add_argument("--pmc-prefill", action="store_true",
                     help="counter mode: 3 launches of each prefill GEMM point (M=4096, "
                          "Llama-3.3-70B shapes, bits 4 and 6); prints what ran and exits")
+    ap.add_argument("--pmc-shapes", default=None, metavar="M:N:K:BITS[,...]",
+                    help="counter mode: 5 copies of 256 MiB (known bytes), then 10 launches of "
+                         "each listed dequant-matmul shape (decode-sweep weight generator); "
+                         "prints what ran and exits")
+    ap.add_argument("--pmc-fidelity", action="store_true",
+                    help="counter mode: 3 calls of EAR/KL and of top-10 EAR/KL on 512 x 151936 "
+                         "logits (sigma 0.05); prints what ran and exits")
+    ap.add_argument("--pmc-quantize", action="store_true",
+                    help="counter mode: 3 quantize+pack calls per decode-sweep shape and width; "
+                         "prints what ran and exits")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -135,7 +145,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     torch.manual_seed(0)
-    rows_sel = {"quantize", "gemm", "stack", "fidelity", "allocation", "gptq", "gamma", "compact"} if args.rows == "all" else (
+    rows_sel = {"quantize", "gemm", "stack", "fidelity", "allocation", "gptq", "gamma", "compact",
+                "config1", "ceiling"} if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
 
     def to_dev(a):
@@ -163,6 +174,68 @@ def main():
             del Wd, y
         torch.cuda.synchronize()
         print(json.dumps({"pmc_prefill": ran, "launches_each": 3}))
+        return
+
+    def copy_calibration():
+        src = torch.empty(256 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if args.pmc_shapes:
+        copy_calibration()
+        ran = []
+        for spec in args.pmc_shapes.split(","):
+            m, n, k, bits = (int(v) for v in spec.split(":"))
+            Wd = to_dev(S.skewed_weights(n, k, S.seed_for(2, 0, n % 97 + k % 89), row_offset_std=0.005))
+            pw = slq.slq_quantize_pack(Wd, bits)
+            del Wd
+            xx = x_dev(S.activations_bf16(m, k, S.seed_for(2, m, k % 97)))
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            ws_ = torch.zeros(max(slq.gemm_workspace_bytes(m, pw), 256), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            for _ in range(10):
+                slq.slq_dequant_gemm(xx, pw, y=y, ws=ws_)
+            torch.cuda.synchronize()
+            ran.append({"m": m, "n": n, "k": k, "bits": bits, "kernel": slq.kernel_name(m, pw),
+                        "alg_bytes_per_launch": alg_bytes(m, n, k, bits), "launches": 10})
+            del pw, y, ws_
+        print(json.dumps({"pmc_shapes": ran, "copy_bytes_each": 2 * 256 * 2**20, "copies": 5}))
+        return
+
+    if args.pmc_fidelity:
+        copy_calibration()
+        a, b = S.fidelity_logits(S.FIDELITY_ROWS, S.VOCAB, 0.05, S.seed_for(5) + 50)
+        ad, bd = to_dev(a), to_dev(b)
+        del a, b
+        for _ in range(3):
+            slq.slq_ear_kl(ad, bd)
+        for _ in range(3):
+            slq.slq_ear_kl_topk(ad, bd, 10, 1.0)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_fidelity": {"rows": S.FIDELITY_ROWS, "vocab": S.VOCAB, "calls_each": 3,
+                                           "alg_bytes_per_call": 2 * S.FIDELITY_ROWS * S.VOCAB * 4},
+                          "copy_bytes_each": 2 * 256 * 2**20, "copies": 5}))
+        return
+
+    if args.pmc_quantize:
+        copy_calibration()
+        ran = []
+        for i, (name, n, k) in enumerate(SWEEP_SHAPES):
+            Wd = to_dev(S.skewed_weights(n, k, S.seed_for(2, 0, i), row_offset_std=0.005))
+            for bits in SWEEP_BITS:
+                out = slq.alloc_packed(n, k, bits, dev)
+                for _ in range(3):
+                    slq.slq_quantize_pack(Wd, bits, out=out)
+                ran.append({"shape": name, "n": n, "k": k, "bits": bits,
+                            "alg_bytes_per_call": n * k * 4 + packed_bytes(n, k, bits)})
+                del out
+            del Wd
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_quantize": ran, "calls_each": 3, "copy_bytes_each": 2 * 256 * 2**20,
+                          "copies": 5}))
         return
 
     # ---------------- headline: decode sweep ----------------
@@ -333,6 +406,90 @@ def main():
         "GBps_packed_step": round(value, 1),
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "points": point_rows}}
+
+    def clone_packed(pw):
+        c = slq.alloc_packed(pw.n, pw.k, pw.bits, dev, meta=pw.meta)
+        c.codes.copy_(pw.codes)
+        c.scales.copy_(pw.scales)
+        c.zeros.copy_(pw.zeros)
+        return c
+
+    def graph_time(launch, copies, reps=5):
+        """Average duration of one launch: a HIP graph of `copies` launches,
+        events around `reps` replays (kernels back to back: kernel time)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for c in range(copies):
+                launch(c)
+        g.replay()
+        torch.cuda.synchronize()
+        with Timer(torch) as T:
+            for _ in range(reps):
+                g.replay()
+        del g
+        return T.ms / (reps * copies)
+
+    # ---------------- config 1: one decode token on one 4096 x 4096 INT4 layer ----------------
+    if "config1" in rows_sel:
+        pi1 = points.index(("q", 4096, 4096, 4, 1))
+        base = packs[0][pi1]
+        copies = max(2, int(1.1e9 // base.nbytes) + 1)   # >= 1.1 GB of distinct copies
+        cps = [clone_packed(base) for _ in range(copies)]
+        x1 = xs[(1, 4096)]
+        y1 = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+        ms1 = graph_time(lambda c: slq.slq_dequant_gemm(x1, cps[c], y=y1, ws=ws), copies)
+        bw = packed_bytes(4096, 4096, 4)
+        rows["config1_single_layer"] = {
+            "workload": "M=1, K=N=4096, asymmetric INT4 g128, bf16 x, fp32 y",
+            "kernel": slq.kernel_name(1, base), "us_per_launch": round(ms1 * 1e3, 3),
+            "packed_bytes": bw, "GBps_packed": round(bw / (ms1 * 1e-3) / 1e9, 1),
+            "frac_hbm_packed": round(bw / (ms1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "alg_bytes": alg_bytes(1, 4096, 4096, 4),
+            "timing": f"HIP graph of {copies} launches over distinct copies ({copies * bw / 1e9:.2f} GB), "
+                      "events around 5 replays"}
+        log(f"bench: config 1 (M=1 4096x4096 INT4): {ms1 * 1e3:.2f} us per launch")
+        del cps
+
+    # ---------------- read ceiling and per-size launch floor ----------------
+    if "ceiling" in rows_sel:
+        sink = torch.zeros(slq.stream_read_words(512 * 2**20), dtype=torch.int32, device=dev)
+        sizes = sorted({packed_bytes(n, k, b) for (_, n, k, b, m) in points})
+        floor_us = {}
+        per_size = []
+        for nb in sizes:
+            nb16 = (nb + 15) // 16 * 16
+            copies = max(2, int(1.1e9 // nb16) + 1)
+            bufs = torch.empty((copies, nb16), dtype=torch.uint8, device=dev)
+            bufs.fill_(1)
+            msr = graph_time(lambda c: slq.slq_stream_read(bufs[c], sink, nb16), copies)
+            floor_us[nb] = msr * 1e3
+            per_size.append({"bytes": nb, "us": round(msr * 1e3, 3),
+                             "GBps": round(nb / (msr * 1e-3) / 1e9, 1)})
+            del bufs
+        tiny = torch.zeros(16, dtype=torch.uint8, device=dev)
+        empty_us = graph_time(lambda c: slq.slq_stream_read(tiny, sink, 16), 200) * 1e3
+        big = 512 * 2**20
+        bufb = torch.empty((3, big), dtype=torch.uint8, device=dev)
+        bufb.fill_(1)
+        ms_big = graph_time(lambda c: slq.slq_stream_read(bufb[c], sink), 3)
+        del bufb
+        floor_step_us = sum(floor_us[packed_bytes(n, k, b)] for (_, n, k, b, m) in points)
+        dom_pts = by_kernel[dom_name]["pts"]
+        dom_floor = float(np.mean([floor_us[packed_bytes(points[pi][1], points[pi][2], points[pi][3])]
+                                   for pi in dom_pts]))
+        rows["read_ceiling"] = {
+            "probe": "slq_stream_read: one coalesced 16-byte-load read of a device buffer, "
+                     "graph-timed over >= 1.1 GB of distinct copies per size",
+            "read_GBps_512MiB": round(big / (ms_big * 1e-3) / 1e9, 1),
+            "launch_floor_us": round(empty_us, 3),
+            "per_size": per_size,
+            "sweep_floor_us_per_step": round(floor_step_us, 2),
+            "sweep_frac_of_floor": round(floor_step_us / (step_ms * 1e3), 4),
+            "sweep_GBps_at_floor": round(sweep_bytes / (floor_step_us * 1e-6) / 1e9, 1),
+            "dominant_kernel_frac_of_read_at_same_bytes": round(dom_floor / (dom_ms * 1e3), 4)}
+        roofline["frac_of_read_ceiling"] = rows["read_ceiling"]["dominant_kernel_frac_of_read_at_same_bytes"]
+        log(f"bench: read ceiling {rows['read_ceiling']['read_GBps_512MiB']} GB/s (512 MiB); sweep floor "
+            f"{floor_step_us:.1f} us per step ({floor_step_us / (step_ms * 1e3):.2f} of the step)")
     if compact_row is not None:
         rows["decode_sweep_compact_metadata"] = compact_row
 
@@ -359,6 +516,13 @@ def main():
                                  "shapes": "sweep shapes x bits {3,4,8}", "ms": round(tot_ms, 3)}
         log(f"bench: quantize+pack {gbs:.1f} GB/s")
 
+    # GPU outputs kept for the oracle checks of the CPU leg (never timed)
+    keep = {}
+
+    def sample_pairs(m, n, count, seed):
+        g = np.random.Generator(np.random.PCG64(seed))
+        return g.integers(0, m, count).astype(np.int64), g.integers(0, n, count).astype(np.int64)
+
     # ---------------- prefill GEMM ----------------
     if "gemm" in rows_sel:
         log("bench: prefill GEMM (Llama-3.3-70B shapes, M=4096)")
@@ -383,6 +547,10 @@ def main():
                 tot_ms += ms
                 per.append({"shape": label, "n": n, "k": k, "bits": bits, "ms": round(ms, 3),
                             "TFLOPs": round(f / (ms * 1e-3) / 1e12, 1)})
+                if label == "q/o" and bits == 4:
+                    mi, ni = sample_pairs(4096, n, 512, 11)
+                    keep["prefill"] = (n, k, bits, S.seed_for(4, 0, i), S.seed_for(4) + 1, mi, ni,
+                                       y.cpu().numpy()[mi, ni])
                 del pw
             del Wd, y
             torch.cuda.empty_cache()
@@ -433,6 +601,12 @@ def main():
             ms = T.ms / 3
             res[f"M{m}"] = {"ms": round(ms, 4), "GBps_packed": round(sbytes / (ms * 1e-3) / 1e9, 1),
                             "frac_hbm": round(sbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            # the last layer's projections wrote ysk: sampled outputs of each, for the oracle check
+            for j, p in enumerate(S.PROJ_ORDER):
+                n_, k_ = S.LLAMA3_8B_PROJ[p]
+                mi, ni = sample_pairs(m, n_, 64, 100 + 7 * m + j)
+                keep[f"stack_M{m}_{p}"] = (n_, k_, bmap[31][p], S.seed_for(3, 0, j), S.seed_for(3, m, k_ % 97),
+                                          mi, ni, ysk[p].cpu().numpy()[mi, ni], m)
             log(f"bench: stack M={m}: {ms:.3f} ms, {sbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
             del g
         rows["mixed_stack"] = res
@@ -447,6 +621,8 @@ def main():
         for sigma in S.FIDELITY_SIGMAS:
             a, b = S.fidelity_logits(S.FIDELITY_ROWS, S.VOCAB, sigma, S.seed_for(5) + int(sigma * 1000))
             ad, bd = to_dev(a), to_dev(b)
+            if sigma == 0.05:
+                keep["fid_in"] = (a[:8].copy(), b[:8].copy())
             del a, b
             ear, kl, means = slq.slq_ear_kl(ad, bd)
             torch.cuda.synchronize()
@@ -459,8 +635,11 @@ def main():
             tot_ms += ms
             mh = means.cpu().numpy()
             # top-10 EAR / KL at temperature 1 (the form the sensitivity search uses)
-            _, _, tmeans = slq.slq_ear_kl_topk(ad, bd, 10, 1.0)
+            tear, tkl, tmeans = slq.slq_ear_kl_topk(ad, bd, 10, 1.0)
             torch.cuda.synchronize()
+            if sigma == 0.05:
+                keep["fid_out"] = (ear.cpu().numpy()[:8], kl.cpu().numpy()[:8],
+                                   tear.cpu().numpy()[:8], tkl.cpu().numpy()[:8])
             with Timer(torch) as T:
                 for _ in range(3):
                     slq.slq_ear_kl_topk(ad, bd, 10, 1.0)
@@ -560,38 +739,129 @@ def main():
         del Wd
         torch.cuda.empty_cache()
 
-    # ---------------- CPU baseline (oracle) ----------------
+    # ---------------- CPU baseline (oracle), and the oracle checks of every row ----------------
+    # The CPU leg runs the oracle on the same inputs: timed on all host threads
+    # and on one, and its results decide a parity verdict for each row
+    # (outside every timed GPU region).
     cpu = None
+    parity = {}
     if not args.no_cpu_baseline:
         import oracle
-        log("bench: timing the CPU oracle on a sample of the sweep")
+        cpu_model = "unknown"
+        try:
+            for line_ in open("/proc/cpuinfo"):
+                if line_.startswith("model name"):
+                    cpu_model = line_.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+        threads_all = oracle.num_threads()
+        log("bench: CPU oracle on the sweep, and the oracle checks")
         sample = list(points)          # the whole 36-point sweep, in bench order
         qcache = {}
-        for (name, n, k, bits, m) in sample:
+        q_bad, q_checked = 0, 0
+        for pi, (name, n, k, bits, m) in enumerate(sample):
             if (name, bits) not in qcache:
-                q, s, z = oracle.quantize(W_host[name], bits)
-                qcache[(name, bits)] = (oracle.pack(q, bits), s, z)
-        tb, tt, npts = 0, 0.0, 0
+                q, s_, z = oracle.quantize(W_host[name], bits)
+                words = oracle.pack(q, bits)
+                qcache[(name, bits)] = (words, s_, z)
+                pw = packs[0][pi]
+                q_checked += 1
+                same = (np.array_equal(pw.codes.cpu().numpy().view(np.uint32), words) and
+                        np.array_equal(pw.scales.cpu().numpy().view(np.uint32), s_.view(np.uint32)) and
+                        np.array_equal(pw.zeros.cpu().numpy(), z))
+                q_bad += 0 if same else 1
+        parity["quantize_pack"] = {"verdict": "pass" if q_bad == 0 else "fail",
+                                   "checked": f"{q_checked} (shape, width) layers, every code word, "
+                                              "scale bit pattern and zero point", "mismatching": q_bad}
         xcache = {}
+
+        def oracle_point(name, n, k, bits, m):
+            words, s_, z = qcache[(name, bits)]
+            if (m, k) not in xcache:
+                xcache[(m, k)] = S.activations_bf16(m, k, S.seed_for(2, m, k % 97))
+            q = oracle.unpack(words, k, bits)
+            wh = oracle.dequantize(q, s_, z)
+            return oracle.gemm(xcache[(m, k)], wh)
+
+        tb, tt, npts, worst, bad = 0, 0.0, 0, 0.0, 0
         while tt < 10.0 and npts < 12 * len(sample):   # whole passes until >= 10 s of CPU work
-            for (name, n, k, bits, m) in sample:
-                words, s, z = qcache[(name, bits)]
-                if (m, k) not in xcache:
-                    xcache[(m, k)] = S.activations_bf16(m, k, S.seed_for(2, m, k % 97))
-                x = xcache[(m, k)]
+            for pi, (name, n, k, bits, m) in enumerate(sample):
                 t1 = time.perf_counter()
-                q = oracle.unpack(words, k, bits)
-                wh = oracle.dequantize(q, s, z)
-                oracle.gemm(x, wh)
+                yr, br = oracle_point(name, n, k, bits, m)
                 tt += time.perf_counter() - t1
                 tb += packed_bytes(n, k, bits)
+                if npts < len(sample):     # first pass: every output of every point
+                    err = np.abs(y_eager[pi].cpu().numpy().astype(np.float64) - yr)
+                    r = err / np.maximum(1e-2 * br, 1e-300)
+                    worst = max(worst, float(r.max()))
+                    bad += int((r > 1.0).sum())
                 npts += 1
-        cpu = {"value": round(tb / tt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-               "kind": "oracle", "seconds": round(tt, 2),
+        parity["decode_sweep"] = {"verdict": "pass" if bad == 0 else "fail",
+                                  "max_err_over_tol": round(worst, 6),
+                                  "checked": "every output of all 36 points; tol = 1e-2 * sum|x||w_hat|"}
+        # one thread, on the first points of the sweep for >= 5 s
+        oracle.set_threads(1)
+        tb1, tt1, n1 = 0, 0.0, 0
+        while tt1 < 5.0 and n1 < len(sample):
+            name, n, k, bits, m = sample[n1]
+            t1 = time.perf_counter()
+            oracle_point(name, n, k, bits, m)
+            tt1 += time.perf_counter() - t1
+            tb1 += packed_bytes(n, k, bits)
+            n1 += 1
+        oracle.set_threads(threads_all)
+        cpu = {"value": round(tb / tt / 1e9, 4), "unit": "GB/s", "cores": threads_all,
+               "kind": "oracle", "seconds": round(tt, 2), "cpu_model": cpu_model,
+               "value_1thread": round(tb1 / tt1 / 1e9, 4), "seconds_1thread": round(tt1, 2),
                "sample": f"oracle unpack + dequantize + fp64 matmul over {npts // len(sample)} "
                          f"pass(es) of the full 36-point sweep (same shapes, bits and M as the "
-                         f"GPU step); packed-weight bytes / wall time"}
-        log(f"bench: cpu oracle {cpu['value']} GB/s in {tt:.1f}s on {cpu['cores']} threads")
+                         f"GPU step); packed-weight bytes / wall time; 1 thread: the first {n1} "
+                         f"points of the sweep"}
+        log(f"bench: cpu oracle {cpu['value']} GB/s on {threads_all} threads, "
+            f"{cpu['value_1thread']} GB/s on 1 ({cpu_model})")
+
+        def pairs_check(W, bits, x_bits, mi, ni, got):
+            rows_, inv = np.unique(ni, return_inverse=True)
+            q, s_, z = oracle.quantize(W[rows_], bits)
+            wh = oracle.dequantize(q, s_, z)
+            yr, br = oracle.gemm_pairs(x_bits, wh, mi, inv.astype(np.int64))
+            r = np.abs(got.astype(np.float64) - yr) / np.maximum(1e-2 * br, 1e-300)
+            return float(r.max()), int((r > 1.0).sum())
+
+        if "prefill" in keep:
+            n, k, bits, wseed, xseed, mi, ni, got = keep.pop("prefill")
+            W = S.skewed_weights(n, k, wseed, row_offset_std=0.005)
+            xb = S.activations_bf16(4096, k, xseed)
+            w_, b_ = pairs_check(W, bits, xb, mi, ni, got)
+            parity["prefill_gemm"] = {"verdict": "pass" if b_ == 0 else "fail", "max_err_over_tol": round(w_, 6),
+                                      "checked": f"{len(mi)} sampled outputs of the q/o 8192x8192 4-bit point"}
+            del W, xb
+        stack_keys = [key for key in keep if key.startswith("stack_")]
+        if stack_keys:
+            wcache, worst_s, bad_s, cnt = {}, 0.0, 0, 0
+            for key in stack_keys:
+                n, k, bits, wseed, xseed, mi, ni, got, m = keep.pop(key)
+                if wseed not in wcache:
+                    wcache[wseed] = S.skewed_weights(n, k, wseed, row_offset_std=0.005)
+                w_, b_ = pairs_check(wcache[wseed], bits, S.activations_bf16(m, k, xseed), mi, ni, got)
+                worst_s, bad_s, cnt = max(worst_s, w_), bad_s + b_, cnt + len(mi)
+            parity["mixed_stack"] = {"verdict": "pass" if bad_s == 0 else "fail",
+                                     "max_err_over_tol": round(worst_s, 6),
+                                     "checked": f"{cnt} sampled outputs: every projection of the last "
+                                                "layer at M = 1, 32, 64"}
+            del wcache
+        if "fid_in" in keep and "fid_out" in keep:
+            a8, b8 = keep.pop("fid_in")
+            ear_g, kl_g, tear_g, tkl_g = keep.pop("fid_out")
+            er, kr, _ = oracle.ear_kl(a8, b8)
+            ter, tkr, _ = oracle.ear_kl_topk(a8, b8, 10, 1.0)
+            d = max(float(np.abs(ear_g - er).max()), float(np.abs(kl_g - kr).max()),
+                    float(np.abs(tear_g - ter).max()), float(np.abs(tkl_g - tkr).max()))
+            parity["ear_kl"] = {"verdict": "pass" if d <= 1e-5 else "fail", "max_abs_err": d,
+                                "checked": "EAR, KL, top-10 EAR and top-10 KL of 8 rows at sigma 0.05 "
+                                           "(tolerance 1e-5 absolute)"}
+        log("bench: oracle checks " + ", ".join(f"{k_}: {v['verdict']}" for k_, v in parity.items()))
 
     line = {
         "metric": "dequant-GEMV packed-weight GB/s + GEMM TFLOP/s, W{2-8}A16 g128; % roofline",
@@ -614,6 +884,7 @@ def main():
                    "timing": "HIP graph of the 36 launches per rotation slot, events around K replays"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "rows": rows,
     }
     print(json.dumps(line), flush=True)

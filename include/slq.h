@@ -343,6 +343,21 @@ size_t slq_quant_error_workspace_bytes(const slq_packed *w);
 slq_status slq_quant_error(const float *W, const slq_packed *w, double *out, void *workspace,
                            slq_stream stream);
 
+/* Words of `folds` slq_stream_read writes for `bytes` bytes (one per 16 KiB). */
+size_t slq_stream_read_words(size_t bytes);
+
+/*
+ * Measurement aid (not part of the method): one plain read of `bytes` bytes
+ * of the device buffer `buf` with coalesced 16-byte loads, 1024 consecutive
+ * 16-byte words per workgroup; workgroup i writes the XOR of the 32-bit words
+ * it read to folds[i] (bytes past the end read as zero).  Timing it over
+ * buffers of the decode layers' sizes gives the read ceiling and per-launch
+ * floor that a dequant-GEMV of the same bytes could at best reach.
+ * bytes % 16 == 0; buf 16-byte aligned; folds: device uint32
+ * [slq_stream_read_words(bytes)], 4-byte aligned, outside buf.
+ */
+slq_status slq_stream_read(const void *buf, size_t bytes, uint32_t *folds, slq_stream stream);
+
 /* Static description of a status code. */
 const char *slq_strerror(slq_status s);
 

@@ -28,6 +28,7 @@ def load(path: str):
     """Load an oracle build from `path` and declare its C signatures."""
     L = ctypes.CDLL(path)
     L.oracle_num_threads.restype = _int
+    L.oracle_set_threads.argtypes = [_int]
     L.oracle_quantize.argtypes = [_f32p, _i64, _i64, _int, _int, _int, _u8p, _f32p, _u8p]
     L.oracle_pack.argtypes = [_u8p, _i64, _i64, _int, _u32p]
     L.oracle_unpack.argtypes = [_u32p, _i64, _i64, _int, _u8p]
@@ -81,6 +82,10 @@ def use(L):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
 
 
 def _c(a, dt):
@@ -197,13 +202,14 @@ def mckp_search(sizes, costs, W: int, tau: float, with_best: bool = False):
     """Bit-width allocation: exact multiple-choice knapsack over the cost table
     for every budget 0..W, then the smallest budget whose optimal cost is <= tau.
 
-    sizes int64 [L][nb] (budget units), costs float64 [L][nb].  Returns
+    sizes int64 [L][nb] (budget units; a negative size: an option never taken),
+    costs float64 [L][nb].  Returns
     (status, choice int32 [L], budget, size, cost[, best float64 [W+1]]);
     status 0: found, 1: W does not meet tau (choice at W), 2: nothing fits."""
     sizes = _c(sizes, np.int64)
     costs = _c(costs, np.float64)
     L, nb = sizes.shape
-    if costs.shape != sizes.shape or not (1 <= nb <= 127) or W < 0 or (sizes < 0).any():
+    if costs.shape != sizes.shape or not (1 <= nb <= 127) or W < 0:
         raise ValueError("bad knapsack instance")
     choice = np.empty(L, np.int32)
     budget, size, cost = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_double()

@@ -55,6 +55,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the parallel loops use from now on (the CPU baseline is timed on
+ * one thread and on all). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Round-to-nearest-even, then clamp to [0, maxq], all in fp32 (R4/R5). */
 static float clamp_code(float v, int maxq) {
   if (v < 0.0f) return 0.0f;
@@ -392,7 +402,8 @@ double oracle_bits_per_param(int bits, int meta_bits, int group) {
  *   best(w) = min over selections with sum of sizes <= w of the sum of costs
  * (+inf when nothing fits), computed by the textbook exact recurrence over the
  * items in order:  f_0(w) = 0,  f_{l+1}(w) = min_j f_l(w - s_lj) + c_lj  over
- * the options with s_lj <= w, ties to the lower j.  best is non-increasing in
+ * the options with 0 <= s_lj <= w (a negative size marks an option that is
+ * not available, R22), ties to the lower j.  best is non-increasing in
  * w, so the smallest budget in [0, W] at which something fits and best(w) <=
  * tau is found by binary search; the selection is then read back from the
  * recorded choices.
@@ -415,7 +426,7 @@ int oracle_mckp_search(int64_t L, int nb, const int64_t *sizes, const double *co
       int j_best = -1;
       for (int j = 0; j < nb; ++j) {
         const int64_t sz = sizes[l * nb + j];
-        if (sz > w) continue;
+        if (sz < 0 || sz > w) continue;   /* a negative size marks an option that is never taken */
         const double v = prev[w - sz] + costs[l * nb + j];
         if (v < b) {
           b = v;
@@ -633,27 +644,27 @@ void oracle_gptq_columns(const float *W, const float *U, const uint8_t *dead, in
       for (int64_t g = 0; g < G; ++g) {
         const int64_t i1 = g * group;
         /* group parameters from the current weights (R1-R4) */
-        float lo = 0.0f, hi = 0.0f;
+        float glo = 0.0f, ghi = 0.0f;
         for (int p = 0; p < group; ++p) {
-          if (w[i1 + p] < lo) lo = w[i1 + p];
-          if (w[i1 + p] > hi) hi = w[i1 + p];
+          if (w[i1 + p] < glo) glo = w[i1 + p];
+          if (w[i1 + p] > ghi) ghi = w[i1 + p];
         }
-        float range = hi - lo;
-        float s = range / (float)maxq;
+        const float grange = ghi - glo;
+        float s = grange / (float)maxq;
         int z;
         if (s == 0.0f) {
           s = 1.0f;
           z = 0;
         } else {
-          z = (int)clamp_code(rintf((-lo) / s), maxq);
+          z = (int)clamp_code(rintf((-glo) / s), maxq);
         }
         scales[r * G + g] = s;
         zeros[r * G + g] = (uint8_t)z;
         /* the block's columns in order, moving the block's later columns */
         for (int p = 0; p < group; ++p) {
           const int64_t i = i1 + p;
-          float t = rintf(w[i] / s);
-          int qi = (int)clamp_code(t + (float)z, maxq);
+          const float rq = rintf(w[i] / s);
+          int qi = (int)clamp_code(rq + (float)z, maxq);
           q[r * k + i] = (uint8_t)qi;
           float w_hat = (float)(qi - z) * s;
           float d = w[i] - w_hat;

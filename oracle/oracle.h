@@ -8,6 +8,7 @@ extern "C" {
 #endif
 
 int oracle_num_threads(void);
+void oracle_set_threads(int n);
 void oracle_quantize(const float *W, int64_t n, int64_t k, int bits, int group,
                      int symmetric, uint8_t *q, float *scales, uint8_t *zeros);
 void oracle_pack(const uint8_t *q, int64_t n, int64_t k, int bits, uint32_t *words);

@@ -31,9 +31,20 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     for name in names:
         assert hasattr(L, name), name
+
+
+def test_stream_read_validation():
+    L = slq.lib()
+    assert L.slq_stream_read(A, 0, B, None) == slq.SLQ_OK          # nothing to read
+    assert L.slq_stream_read(A, 100, B, None) == slq.SLQ_EINVAL    # not whole 16-byte words
+    assert L.slq_stream_read(A + 8, 4096, B, None) == slq.SLQ_EINVAL   # misaligned
+    assert L.slq_stream_read(None, 4096, B, None) == slq.SLQ_EINVAL
+    assert L.slq_stream_read(A, 4096, None, None) == slq.SLQ_EINVAL
+    assert L.slq_stream_read(A, 4096, A + 64, None) == slq.SLQ_EINVAL  # folds inside the buffer
+    assert L.slq_stream_read_words(16384) == 1 and L.slq_stream_read_words(16400) == 2
 
 
 def packed(bits=4, group=128, n=64, k=256, codes=B, scales=C, zeros=D):

@@ -88,3 +88,19 @@ def test_repeatable_and_empty():
     assert all(np.array_equal(u, v) for u, v in zip(a, b))
     empty = slq.slq_quantize_pack(torch.empty((0, 256), dtype=torch.float32, device=DEV), 4)
     assert empty.codes.numel() == 0
+
+
+def test_stream_read_covers_every_word():
+    """The read-ceiling probe reads every 16-byte word once: workgroup i's
+    fold is the XOR of the 32-bit words of bytes [16 KiB i, 16 KiB (i + 1))."""
+    rng = np.random.default_rng(5)
+    for nbytes in (16, 4096 * 16 + 48, 3 * 2 ** 20 + 4096):
+        words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+        nf = slq.stream_read_words(nbytes)
+        folds = torch.zeros(nf, dtype=torch.int32, device=DEV)
+        slq.slq_stream_read(gpu(words), folds)
+        got = folds.cpu().numpy().view(np.uint32)
+        per = 16384 // 4
+        expect = np.array([np.bitwise_xor.reduce(words[i * per:(i + 1) * per]) for i in range(nf)],
+                          np.uint32)
+        assert np.array_equal(got, expect), nbytes

@@ -101,3 +101,23 @@ def test_ties_go_to_the_lower_option():
     costs = np.array([[1.0, 1.0, 1.0], [2.0, 2.0, 2.0]])
     st, choice, budget, size, cost = oracle.mckp_search(sizes, costs, 5, 3.0)
     assert st == 0 and budget == 3 and list(choice) == [0, 0]
+
+
+def test_negative_sizes_are_never_selected():
+    """An option with a negative size is not available: the optimum equals the
+    brute force over the remaining options (a very negative size would
+    otherwise look like free storage), for every budget."""
+    rng = np.random.default_rng(77)
+    for t in range(6):
+        sizes, costs = random_instance(rng, 4, 3, 5)
+        sizes[rng.integers(0, 4), rng.integers(0, 3)] = -1000 if t % 2 else -1
+        costs[sizes < 0] = -1.0          # tempting: the cheapest option of its item
+        W = 12
+        allowed = np.where(sizes < 0, W + 1000, sizes)   # out of every budget
+        ref = brute(allowed, costs, W)
+        st, choice, budget, size, cost, best = oracle.mckp_search(sizes, costs, W, np.inf, True)
+        fin = np.isfinite(ref)
+        np.testing.assert_allclose(best[fin], ref[fin], rtol=0, atol=1e-12)
+        assert np.array_equal(np.isinf(best), np.isinf(ref))
+        if st != 2:
+            assert all(sizes[l, j] >= 0 for l, j in enumerate(choice))

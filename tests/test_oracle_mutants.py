@@ -57,7 +57,8 @@ MUTANTS = {
                                  "means[0] = rows > 1 ? se / (double)(rows - 1) : 0.0;"),
     "sse_not_squared": ("rs += e * e;", "rs += fabs(e);"),
     "bpp_meta_per_group": ("(double)meta_bits / (double)group", "(double)meta_bits / (double)(2 * group)"),
-    "mckp_size_strictly_below": ("if (sz > w) continue;", "if (sz >= w) continue;"),
+    "mckp_size_strictly_below": ("if (sz < 0 || sz > w) continue;", "if (sz < 0 || sz >= w) continue;"),
+    "mckp_negative_size_taken": ("if (sz < 0 || sz > w) continue;", "if (sz > w || w - sz >= NW) continue;"),
     "mckp_max_not_min": ("        if (v < b) {\n          b = v;", "        if (!(v < b) || isinf(b)) {\n          b = v;"),
     "mckp_ties_to_higher": ("        if (v < b) {\n          b = v;", "        if (v <= b) {\n          b = v;"),
     "mckp_search_off_by_one": ("      else lo = mid + 1;", "      else lo = mid + 2;"),
@@ -77,8 +78,8 @@ MUTANTS = {
     "gptq_trailing_transposed": ("a = fmaf(e[p], U[(i1 + p) * k + c], a);", "a = fmaf(e[p], U[c * k + (i1 + p)], a);"),
     "gptq_trailing_drops_last_term": ("for (int p = 0; p < group; ++p) a = fmaf(",
                                       "for (int p = 0; p < group - 1; ++p) a = fmaf("),
-    "gptq_params_from_original": ("          if (w[i1 + p] < lo) lo = w[i1 + p];\n          if (w[i1 + p] > hi) hi = w[i1 + p];",
-                                  "          if (W[r * k + i1 + p] < lo) lo = W[r * k + i1 + p];\n          if (W[r * k + i1 + p] > hi) hi = W[r * k + i1 + p];"),
+    "gptq_params_from_original": ("          if (w[i1 + p] < glo) glo = w[i1 + p];\n          if (w[i1 + p] > ghi) ghi = w[i1 + p];",
+                                  "          if (W[r * k + i1 + p] < glo) glo = W[r * k + i1 + p];\n          if (W[r * k + i1 + p] > ghi) ghi = W[r * k + i1 + p];"),
     "gptq_dead_kept": ("w[c] = (dead && dead[c]) ? 0.0f : W[r * k + c];", "w[c] = W[r * k + c];"),
     "compact_zero_bits_always_4": ("int oracle_compact_zero_bits(int bits) { return bits <= 4 ? 4 : 8; }",
                                    "int oracle_compact_zero_bits(int bits) { return 4; }"),

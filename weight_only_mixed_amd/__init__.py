@@ -83,6 +83,9 @@ def lib():
         L.slq_quant_error.argtypes = [_vp, _pp, _vp, _vp, _vp]
         L.slq_dequant_gemm_kernel_name.argtypes = [_i64, _pp]
         L.slq_dequant_gemm_kernel_name.restype = ctypes.c_char_p
+        L.slq_stream_read.argtypes = [_vp, _sz, _vp, _vp]
+        L.slq_stream_read_words.argtypes = [_sz]
+        L.slq_stream_read_words.restype = _sz
         L.slq_strerror.argtypes = [_int]
         L.slq_strerror.restype = ctypes.c_char_p
         for f in ("slq_quantize_pack", "slq_dequantize", "slq_dequant_gemm", "slq_row_lse",
@@ -269,6 +272,19 @@ def slq_gptq_quantize(W: torch.Tensor, H: torch.Tensor, bits: int, damp: float =
                                    ctypes.byref(desc), _ptr(U), _ptr(ws), _stream(W)),
            "slq_gptq_quantize")
     return pw, U
+
+
+def stream_read_words(nbytes: int) -> int:
+    return lib().slq_stream_read_words(nbytes)
+
+
+def slq_stream_read(buf: torch.Tensor, folds: torch.Tensor, nbytes: int | None = None):
+    """One plain read of the first nbytes (default: all) of a device buffer
+    (measurement aid: the read ceiling and per-launch floor); folds: int32
+    [stream_read_words(nbytes)] receives one XOR fold per 16 KiB."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    assert folds.numel() >= stream_read_words(n)
+    _check(lib().slq_stream_read(_ptr(buf), n, _ptr(folds), _stream(buf)), "slq_stream_read")
 
 
 def slq_gptq_factor(H: torch.Tensor, damp: float = 0.01, with_u64: bool = False):

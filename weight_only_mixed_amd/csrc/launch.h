@@ -80,4 +80,9 @@ hipError_t launch_ear_kl_topk(const float *a, const float *b, int64_t rows, int6
                               double invT, float *ear, float *kl, double *means, void *ws,
                               hipStream_t s);
 
+// probe.hip: one plain read of `bytes` (a multiple of 16) of `buf`; one XOR
+// fold per 16 KiB read into folds[stream_read_words(bytes)]
+size_t stream_read_words(size_t bytes);
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *folds, hipStream_t s);
+
 }  // namespace slq

@@ -70,6 +70,46 @@ slq_status check_packed(const slq_packed *w, PackedSizes *sz) {
 
 }  // namespace
 
+namespace {
+
+size_t gemm_ws_bytes(int64_t m, const slq_packed *w);
+
+// Validation and launch of slq_dequant_gemm.
+slq_status dequant_gemm_checked(const uint16_t *x_bf16, const slq_packed *w, int64_t m, float *y,
+                                void *workspace, slq_stream stream) {
+  PackedSizes sz;
+  slq_status st = check_packed(w, &sz);
+  if (st != SLQ_OK) return st;
+  if (m < 0 || m >= kMaxDim) return SLQ_EINVAL;
+  if (m == 0 || w->n == 0) return SLQ_OK;
+  const size_t xb = (size_t)(m * w->k) * 2, yb = (size_t)(m * w->n) * sizeof(float);
+  if (!y || !aligned(y, 16)) return SLQ_EINVAL;
+  if (xb > 0 && (!x_bf16 || !aligned(x_bf16, 16))) return SLQ_EINVAL;
+  const size_t wsb = gemm_ws_bytes(m, w);
+  if (wsb > 0 && (!workspace || !aligned(workspace, 256))) return SLQ_EINVAL;
+  if (overlap(y, yb, x_bf16, xb) || overlap(y, yb, w->codes, sz.codes) ||
+      overlap(y, yb, w->scales, sz.scales) || overlap(y, yb, w->zeros, sz.zeros) ||
+      overlap(y, yb, workspace, wsb) || overlap(workspace, wsb, x_bf16, xb) ||
+      overlap(workspace, wsb, w->codes, sz.codes) ||
+      overlap(workspace, wsb, w->scales, sz.scales) || overlap(workspace, wsb, w->zeros, sz.zeros))
+    return SLQ_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  slq::GemvPlan plan{};
+  if (m <= kDecodeMaxM) {
+    plan = slq::gemv_plan(m, w->n, w->k, w->bits);
+    if (plan.ksplits == 0) return SLQ_ENOTSUP;
+  }
+  if (m <= kDecodeMaxM)
+    return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros,
+                                     w->meta == SLQ_META_COMPACT, m, w->n, w->k, w->bits, y,
+                                     workspace, plan, s));
+  return from_hip(slq::launch_gemm(x_bf16, w->codes, w->scales, w->zeros,
+                                   w->meta == SLQ_META_COMPACT, m, w->n, w->k, w->bits, y,
+                                   workspace, s));
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t slq_codes_bytes(int64_t n, int64_t k, int bits) {
@@ -136,42 +176,26 @@ slq_status slq_dequantize(const slq_packed *w, float *W_deq, slq_stream stream) 
 }
 
 size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w) {
+  return gemm_ws_bytes(m, w);
+}
+
+}  // extern "C"
+
+namespace {
+size_t gemm_ws_bytes(int64_t m, const slq_packed *w) {
   PackedSizes sz;
   if (m < 0 || m >= kMaxDim || check_packed(w, &sz) != SLQ_OK) return 0;
   if (m == 0 || w->n == 0) return 0;
   if (m <= kDecodeMaxM) return slq::gemv_plan(m, w->n, w->k, w->bits).ws_bytes;
   return slq::gemm_workspace(m, w->n, w->k, w->bits);
 }
+}  // namespace
+
+extern "C" {
 
 slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t m, float *y,
                             void *workspace, slq_stream stream) {
-  PackedSizes sz;
-  slq_status st = check_packed(w, &sz);
-  if (st != SLQ_OK) return st;
-  if (m < 0 || m >= kMaxDim) return SLQ_EINVAL;
-  if (m == 0 || w->n == 0) return SLQ_OK;
-  const size_t xb = (size_t)(m * w->k) * 2, yb = (size_t)(m * w->n) * sizeof(float);
-  if (!y || !aligned(y, 16)) return SLQ_EINVAL;
-  if (xb > 0 && (!x_bf16 || !aligned(x_bf16, 16))) return SLQ_EINVAL;
-  const size_t wsb = slq_gemm_workspace_bytes(m, w);
-  if (wsb > 0 && (!workspace || !aligned(workspace, 256))) return SLQ_EINVAL;
-  if (overlap(y, yb, x_bf16, xb) || overlap(y, yb, w->codes, sz.codes) ||
-      overlap(y, yb, w->scales, sz.scales) || overlap(y, yb, w->zeros, sz.zeros) ||
-      overlap(y, yb, workspace, wsb) || overlap(workspace, wsb, x_bf16, xb) ||
-      overlap(workspace, wsb, w->codes, sz.codes) ||
-      overlap(workspace, wsb, w->scales, sz.scales) || overlap(workspace, wsb, w->zeros, sz.zeros))
-    return SLQ_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (m <= kDecodeMaxM) {
-    const slq::GemvPlan plan = slq::gemv_plan(m, w->n, w->k, w->bits);
-    if (plan.ksplits == 0) return SLQ_ENOTSUP;
-    return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros,
-                                     w->meta == SLQ_META_COMPACT, m, w->n, w->k, w->bits, y,
-                                     workspace, plan, s));
-  }
-  return from_hip(slq::launch_gemm(x_bf16, w->codes, w->scales, w->zeros,
-                                   w->meta == SLQ_META_COMPACT, m, w->n, w->k, w->bits, y,
-                                   workspace, s));
+  return dequant_gemm_checked(x_bf16, w, m, y, workspace, stream);
 }
 
 const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
@@ -439,6 +463,15 @@ slq_status slq_quant_error(const float *W, const slq_packed *w, double *out, voi
   return from_hip(slq::launch_quant_error(W, w->codes, w->scales, w->zeros,
                                           w->meta == SLQ_META_COMPACT, w->n, w->k, w->bits, out,
                                           workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t slq_stream_read_words(size_t bytes) { return slq::stream_read_words(bytes); }
+
+slq_status slq_stream_read(const void *buf, size_t bytes, uint32_t *folds, slq_stream stream) {
+  if (bytes == 0) return SLQ_OK;
+  if (!buf || !folds || bytes % 16 != 0 || !aligned(buf, 16) || !aligned(folds, 4)) return SLQ_EINVAL;
+  if (overlap(buf, bytes, folds, slq_stream_read_words(bytes) * 4)) return SLQ_EINVAL;
+  return from_hip(slq::launch_stream_read(buf, bytes, folds, static_cast<hipStream_t>(stream)));
 }
 
 const char *slq_strerror(slq_status s) {
