@@ -43,7 +43,9 @@ typedef enum {
   SLQ_OK = 0,
   SLQ_EINVAL = 1,   /* bad size, bit-width, pointer, alignment or aliasing   */
   SLQ_ENOTSUP = 2,  /* valid request the library does not implement (g!=128) */
-  SLQ_EHIP = 3      /* the HIP runtime reported an error at launch            */
+  SLQ_EHIP = 3,     /* the HIP runtime reported an error at launch            */
+  SLQ_ESCRATCH = 4  /* slq_dequant_gemm_noalloc: the request needs more split-k
+                       scratch than the static array holds                   */
 } slq_status;
 
 typedef enum {
@@ -160,6 +162,26 @@ size_t slq_gemm_workspace_bytes(int64_t m, const slq_packed *w);
  */
 slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t m,
                             float *y, void *workspace, slq_stream stream);
+
+/* Bytes of the static split-k scratch array slq_dequant_gemm_noalloc uses per GPU. */
+size_t slq_noalloc_scratch_bytes(void);
+
+/*
+ * slq_dequant_gemm for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and results, with the split-k scratch taken from a static device
+ * array of slq_noalloc_scratch_bytes() bytes (32 MiB) instead of a caller
+ * workspace.  The library holds one such array on every GPU it runs on until
+ * the process ends; the first call on a device looks up its address and
+ * clears its ticket area with a fill kernel on `stream`.  The call allocates
+ * nothing (no hipMalloc, no library allocation).  Calls on one GPU share its
+ * array: calls that overlap in time on the same GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ * Errors: as slq_dequant_gemm, and SLQ_ESCRATCH (nothing enqueued) when
+ * slq_gemm_workspace_bytes(m, w) exceeds the array.
+ */
+slq_status slq_dequant_gemm_noalloc(const uint16_t *x_bf16, const slq_packed *w, int64_t m,
+                                    float *y, slq_stream stream);
 
 /*
  * Name of the kernel instance slq_dequant_gemm launches for (m, w), as the

@@ -62,6 +62,10 @@ hipError_t launch_mckp(const int64_t *, const double *, int64_t, int, int64_t, d
 }
 hipError_t launch_ear_kl_topk(const float *, const float *, int64_t, int64_t, int, double, float *,
                               float *, double *, void *, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t noalloc_scratch(void **out, hipStream_t) {
+  *out = nullptr;
+  return hipErrorInvalidValue;
+}
 size_t stream_read_words(size_t bytes) { return (bytes + 16383) / 16384; }
 hipError_t launch_stream_read(const void *, size_t, uint32_t *, hipStream_t) {
   return hipErrorInvalidValue;

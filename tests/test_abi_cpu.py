@@ -31,9 +31,30 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = slq.lib()
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     for name in names:
         assert hasattr(L, name), name
+
+
+def test_noalloc_validation():
+    """Argument faults and an oversized split-k request are rejected before
+    any HIP call (the static scratch is not touched)."""
+    L = slq.lib()
+    assert L.slq_noalloc_scratch_bytes() == 32 * 2 ** 20
+    w = packed()
+    N = L.slq_dequant_gemm_noalloc
+    assert N(A, ctypes.byref(packed(bits=9)), 1, E, None) == slq.SLQ_EINVAL
+    assert N(A, ctypes.byref(packed(group=32)), 1, E, None) == slq.SLQ_ENOTSUP
+    assert N(A, ctypes.byref(w), -1, E, None) == slq.SLQ_EINVAL
+    assert N(A, ctypes.byref(w), 0, E, None) == slq.SLQ_OK
+    assert N(A, ctypes.byref(w), 1, A, None) == slq.SLQ_EINVAL          # y overlaps x
+    assert N(None, ctypes.byref(w), 1, E, None) == slq.SLQ_EINVAL
+    assert N(A, ctypes.byref(w), 1, E + 4, None) == slq.SLQ_EINVAL      # misaligned y
+    # a prefill product whose split-k partial tiles exceed the 32 MiB array
+    big = slq.SlqPacked(4, 128, 1024, 8192, B, C, D)
+    assert L.slq_gemm_workspace_bytes(4096, ctypes.byref(big)) > 32 * 2 ** 20
+    assert N(A, ctypes.byref(big), 4096, E, None) == slq.SLQ_ESCRATCH
+    assert b"scratch" in L.slq_strerror(slq.SLQ_ESCRATCH)
 
 
 def test_stream_read_validation():

@@ -15,7 +15,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libslq.so")
 
-SLQ_OK, SLQ_EINVAL, SLQ_ENOTSUP, SLQ_EHIP = 0, 1, 2, 3
+SLQ_OK, SLQ_EINVAL, SLQ_ENOTSUP, SLQ_EHIP, SLQ_ESCRATCH = 0, 1, 2, 3, 4
 SLQ_ASYM, SLQ_SYM = 0, 1
 SLQ_META_F32, SLQ_META_COMPACT = 0, 1
 GROUP = 128
@@ -58,6 +58,9 @@ def lib():
         L.slq_gemm_workspace_bytes.argtypes = [_i64, _pp]
         L.slq_gemm_workspace_bytes.restype = _sz
         L.slq_dequant_gemm.argtypes = [_vp, _pp, _i64, _vp, _vp, _vp]
+        L.slq_dequant_gemm_noalloc.argtypes = [_vp, _pp, _i64, _vp, _vp]
+        L.slq_noalloc_scratch_bytes.argtypes = []
+        L.slq_noalloc_scratch_bytes.restype = _sz
         L.slq_ear_kl_workspace_bytes.argtypes = [_i64, _i64]
         L.slq_ear_kl_workspace_bytes.restype = _sz
         L.slq_row_lse.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
@@ -191,6 +194,18 @@ def workspace(nbytes: int, device, tag: str = "gemm") -> torch.Tensor | None:
 def gemm_workspace_bytes(m: int, pw: PackedWeight) -> int:
     desc = pw.c()
     return lib().slq_gemm_workspace_bytes(m, ctypes.byref(desc))
+
+
+def slq_dequant_gemm_noalloc(x: torch.Tensor, pw: PackedWeight, y: torch.Tensor) -> torch.Tensor:
+    """slq_dequant_gemm without a workspace: the split-k scratch is the
+    library's static per-GPU array (calls overlapping on one GPU race)."""
+    assert x.dtype in (torch.bfloat16, torch.int16, torch.uint16) and x.is_cuda
+    assert x.is_contiguous() and x.shape[-1] == pw.k and y.is_contiguous()
+    m = x.numel() // pw.k if pw.k else x.shape[0]
+    desc = pw.c()
+    _check(lib().slq_dequant_gemm_noalloc(_ptr(x), ctypes.byref(desc), m, _ptr(y), _stream(x)),
+           "slq_dequant_gemm_noalloc")
+    return y
 
 
 def kernel_name(m: int, pw: PackedWeight) -> str:

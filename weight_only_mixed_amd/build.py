@@ -23,6 +23,7 @@ EXTRA = {"quantize.hip": ["-ffp-contract=off"],
          # MFMA results in VGPRs: the decode epilogue reads them with plain VALU ops
          "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 SOURCES = ["quantize.hip", "gemv.hip", "gemm.hip", "fidelity.hip", "mckp.hip", "gptq.hip", "probe.hip",
+           "noalloc.hip",
            "slq_abi.cpp"]
 
 

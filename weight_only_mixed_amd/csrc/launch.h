@@ -80,6 +80,11 @@ hipError_t launch_ear_kl_topk(const float *a, const float *b, int64_t rows, int6
                               double invT, float *ear, float *kl, double *means, void *ws,
                               hipStream_t s);
 
+// noalloc.hip: the split-k scratch of the allocation-free matmul, a static
+// device array per GPU; its device address for the current device
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void **out, hipStream_t s);
+
 // probe.hip: one plain read of `bytes` (a multiple of 16) of `buf`; one XOR
 // fold per 16 KiB read into folds[stream_read_words(bytes)]
 size_t stream_read_words(size_t bytes);

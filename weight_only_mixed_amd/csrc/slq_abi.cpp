@@ -72,11 +72,14 @@ slq_status check_packed(const slq_packed *w, PackedSizes *sz) {
 
 namespace {
 
+constexpr size_t kScratchBytes = slq::kNoallocScratchBytes;
+
 size_t gemm_ws_bytes(int64_t m, const slq_packed *w);
 
-// Validation and launch of slq_dequant_gemm.
+// Validation and launch shared by slq_dequant_gemm and its allocation-free
+// variant (noalloc: the workspace is the device's scratch array).
 slq_status dequant_gemm_checked(const uint16_t *x_bf16, const slq_packed *w, int64_t m, float *y,
-                                void *workspace, slq_stream stream) {
+                                void *workspace, bool noalloc, slq_stream stream) {
   PackedSizes sz;
   slq_status st = check_packed(w, &sz);
   if (st != SLQ_OK) return st;
@@ -86,7 +89,11 @@ slq_status dequant_gemm_checked(const uint16_t *x_bf16, const slq_packed *w, int
   if (!y || !aligned(y, 16)) return SLQ_EINVAL;
   if (xb > 0 && (!x_bf16 || !aligned(x_bf16, 16))) return SLQ_EINVAL;
   const size_t wsb = gemm_ws_bytes(m, w);
-  if (wsb > 0 && (!workspace || !aligned(workspace, 256))) return SLQ_EINVAL;
+  if (noalloc) {
+    if (wsb > kScratchBytes) return SLQ_ESCRATCH;
+  } else if (wsb > 0 && (!workspace || !aligned(workspace, 256))) {
+    return SLQ_EINVAL;
+  }
   if (overlap(y, yb, x_bf16, xb) || overlap(y, yb, w->codes, sz.codes) ||
       overlap(y, yb, w->scales, sz.scales) || overlap(y, yb, w->zeros, sz.zeros) ||
       overlap(y, yb, workspace, wsb) || overlap(workspace, wsb, x_bf16, xb) ||
@@ -98,6 +105,10 @@ slq_status dequant_gemm_checked(const uint16_t *x_bf16, const slq_packed *w, int
   if (m <= kDecodeMaxM) {
     plan = slq::gemv_plan(m, w->n, w->k, w->bits);
     if (plan.ksplits == 0) return SLQ_ENOTSUP;
+  }
+  if (noalloc && wsb > 0) {
+    const hipError_t e = slq::noalloc_scratch(&workspace, s);
+    if (e != hipSuccess) return SLQ_EHIP;
   }
   if (m <= kDecodeMaxM)
     return from_hip(slq::launch_gemv(x_bf16, w->codes, w->scales, w->zeros,
@@ -195,8 +206,15 @@ extern "C" {
 
 slq_status slq_dequant_gemm(const uint16_t *x_bf16, const slq_packed *w, int64_t m, float *y,
                             void *workspace, slq_stream stream) {
-  return dequant_gemm_checked(x_bf16, w, m, y, workspace, stream);
+  return dequant_gemm_checked(x_bf16, w, m, y, workspace, false, stream);
 }
+
+slq_status slq_dequant_gemm_noalloc(const uint16_t *x_bf16, const slq_packed *w, int64_t m,
+                                    float *y, slq_stream stream) {
+  return dequant_gemm_checked(x_bf16, w, m, y, nullptr, true, stream);
+}
+
+size_t slq_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
   static thread_local char buf[96];
@@ -480,6 +498,8 @@ const char *slq_strerror(slq_status s) {
     case SLQ_EINVAL: return "invalid argument (size, bit-width, pointer, alignment or aliasing)";
     case SLQ_ENOTSUP: return "unsupported request (group size other than 128)";
     case SLQ_EHIP: return "HIP runtime error at launch";
+    case SLQ_ESCRATCH:
+      return "the request needs more split-k scratch than the allocation-free entry point holds";
   }
   return "unknown status";
 }
