@@ -42,11 +42,14 @@
 //    cache of another chiplet can hold a stale copy.  The formal form, an
 //    acquire-release ticket, adds an L2 writeback and invalidate per workgroup
 //    and measured 0.3-7 us slower per launch.
-//  * Three kernels: `gemv_kernel` (any m, the general form above),
-//    `gemv_rows_kernel` (33..64 rows on wide or deep layers: the waves split
-//    rows and share each group's activations) and `gemv_mk_kernel` (33..64
-//    rows on mid-width layers: the same sharing with the offset chain formed
-//    once per workgroup); the planner at the end of this file picks one.
+//  * Four kernels: `gemv_kernel` (any m, the general form above),
+//    `gemv_tile_kernel` (17..64 rows on large layers: 64 weight rows x 32
+//    activation rows per wavefront, every load reading whole cache-line
+//    segments), `gemv_rows_kernel` (33..64 rows on other wide or deep layers:
+//    the waves split rows and share each group's activations) and
+//    `gemv_mk_kernel` (33..64 rows on mid-width layers: the same sharing with
+//    the offset chain formed once per workgroup); the planner at the end of
+//    this file picks one.
 
 #include <algorithm>
 #include <limits>
@@ -931,6 +934,292 @@ __global__ __launch_bounds__(kThreads) void gemv_mk_kernel(
     __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 17..64 activation rows: `gemv_tile_kernel`.
+// A wavefront owns kTileNT tiles of 16 weight rows and MTW m-tiles of 16
+// activation rows over a contiguous share of the workgroup's k-block, so each
+// activation fragment feeds kTileNT code chains and each unpacked code operand
+// feeds MTW chains.  The four wavefronts of a workgroup split the activation
+// rows MS ways and the k-block 4/MS ways; the k shares meet in LDS at the end.
+// What bounds these kernels is the L1's rate of about one cache-line lookup per
+// cycle, not bytes: a load whose 64 lanes each touch another 64-byte segment
+// costs 64 lookups.  So every load here reads whole segments:
+//  * activations are loaded row-contiguous (16 lanes per 256-byte group row)
+//    and transposed to fragment order through a wavefront-private LDS stage;
+//  * a lane's 32-code chunk comes in one or two vector loads (three-word and
+//    unaligned four-word loads for the odd widths), so the four lanes of a row
+//    read its 16*b bytes in the same instructions;
+//  * scales and zero points of the wavefront's groups are staged in LDS once,
+//    16 consecutive groups of a row per 4 lanes.
+// Codes and activations of the next group are loaded while the current group
+// is used (two register slots, unconditional clamped loads in whole slot
+// pairs, scheduling fences keeping each slot's loads after the body that
+// frees it).  The offset chain S = x . 128 (x . 1 for 8 bits) is formed per
+// wave and group with the same MFMA sequence as a code chain of all-zero
+// codes, so an all-zero group adds exactly 0 and one-hot activations give
+// w_hat exactly: t = C - (1 + z/128) S (C - z S for 8 bits) with one fma.
+#ifndef SLQ_GEMV_TILE_NT
+#define SLQ_GEMV_TILE_NT 4
+#endif
+constexpr int kTileNT = SLQ_GEMV_TILE_NT;
+constexpr int kTileMTW = 2;          // m-tiles per wavefront
+constexpr int kTileMaxGroups = 16;   // groups per wavefront (its metadata stage)
+constexpr int kTileXPitch = 68;      // words per staged activation row (64 + 4 against bank conflicts)
+#ifndef SLQ_GEMV_TILE_WV
+#define SLQ_GEMV_TILE_WV 4
+#endif
+constexpr int kTileWV = SLQ_GEMV_TILE_WV;   // wavefronts per workgroup
+// LDS of a workgroup: per wavefront an activation stage and a metadata stage
+// (fp32 scales and byte zero points of kTileMaxGroups groups x 16*kTileNT rows)
+constexpr size_t tile_lds_bytes(int wv, int mtw) {
+  return (size_t)wv * (16 * mtw * kTileXPitch * 4 + kTileMaxGroups * 16 * kTileNT * 5) + 16;
+}
+
+typedef uint32_t u32x4a_t __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3a_t __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x2a_t __attribute__((ext_vector_type(2), aligned(4)));
+
+// One 32-code chunk (BITS words, 4-byte aligned) in as few vector loads as
+// the width allows: 4-word parts, then a 3-, 2- or 1-word rest.
+template <int BITS>
+__device__ __forceinline__ Chunk<BITS> load_chunk_wide(const uint32_t *__restrict__ p) {
+  Chunk<BITS> c;
+#pragma unroll
+  for (int i = 0; i + 4 <= BITS; i += 4) {
+    const u32x4a_t v = *reinterpret_cast<const u32x4a_t *>(p + i);
+    c.w[i] = v[0];
+    c.w[i + 1] = v[1];
+    c.w[i + 2] = v[2];
+    c.w[i + 3] = v[3];
+  }
+  constexpr int i0 = BITS / 4 * 4;
+  if constexpr (BITS % 4 == 3) {
+    const u32x3a_t v = *reinterpret_cast<const u32x3a_t *>(p + i0);
+    c.w[i0] = v[0];
+    c.w[i0 + 1] = v[1];
+    c.w[i0 + 2] = v[2];
+  } else if constexpr (BITS % 4 == 2) {
+    const u32x2a_t v = *reinterpret_cast<const u32x2a_t *>(p + i0);
+    c.w[i0] = v[0];
+    c.w[i0 + 1] = v[1];
+  } else if constexpr (BITS % 4 == 1) {
+    c.w[i0] = p[i0];
+  }
+  return c;
+}
+
+template <int BITS, int MTW>
+struct TileSlot {
+  Chunk<BITS> c[kTileNT];
+  u32x4_t xv[4 * MTW];   // 16 * MTW activation rows x 256 bytes, 16 bytes per lane and load
+};
+
+template <int BITS, int MTW, int MS, int WV, bool CM>
+__global__ __launch_bounds__(WV * kWave) void gemv_tile_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ codes,
+    const void *__restrict__ scales, const uint8_t *__restrict__ zeros, int M, int N, int K,
+    int GW, int ksplits, float *__restrict__ y, float *__restrict__ partial,
+    unsigned *__restrict__ tickets) {
+  static_assert(MS == 1 || MS == 2, "WV wavefronts: MS along m, WV / MS along k");
+  constexpr int KW = WV / MS;                // wavefronts along k
+  constexpr int RB = 16 * kTileNT;           // weight rows per workgroup
+  constexpr int NO = kTileNT * MTW * 4;      // outputs per lane
+  constexpr int XI = 4 * MTW;                // activation loads per lane and group
+  constexpr int XW = 16 * MTW * kTileXPitch; // words of a wavefront's activation stage
+  static_assert(RB == kWave, "one staged metadata row per lane");
+  static_assert(NO * kWave <= XW, "the k-share partials fit the wavefront's activation stage");
+  const MetaRd<BITS, CM> md{scales, zeros};
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  uint32_t *xs_all = lds;                                                   // [WV][XW]
+  float *ms_all = reinterpret_cast<float *>(lds + WV * XW);                 // [WV][groups][RB]
+  uint8_t *mzz_all = reinterpret_cast<uint8_t *>(ms_all + WV * kTileMaxGroups * RB);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int ms = wave / KW, kw = wave % KW;
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = K / kGroup;
+  const int kb = blockIdx.y;
+  const int gbase = kb * GW;
+  const int gcount = min(GW, G - gbase);
+  const int ga = (gcount * kw) / KW, gz = (gcount * (kw + 1)) / KW;   // relative to gbase
+  const int ng = gz - ga;                                              // <= kTileMaxGroups
+  const int n0 = blockIdx.x * RB;
+  const int64_t wpr = (int64_t)K * BITS / 32;
+  uint32_t *xs = xs_all + wave * XW;
+  float *mzs = ms_all + wave * kTileMaxGroups * RB;
+  uint8_t *mzz = mzz_all + wave * kTileMaxGroups * RB;
+
+  const uint32_t *crow[kTileNT];
+#pragma unroll
+  for (int t = 0; t < kTileNT; ++t) {
+    const int64_t r = min(n0 + 16 * t + col, N - 1);
+    crow[t] = codes + r * wpr + (int64_t)gbase * 4 * BITS + kq * BITS;
+  }
+  // activation load j covers staged rows 4j .. 4j+3, 16 bytes per lane
+  const int prow = lane >> 4, ppc = lane & 15;
+  uint32_t xoff[XI];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int m = min(16 * MTW * ms + 4 * j + prow, M - 1);
+    xoff[j] = (uint32_t)m * (uint32_t)(K / 8) + (uint32_t)ppc;
+  }
+  const u32x4_t *xg = reinterpret_cast<const u32x4_t *>(x) + (int64_t)gbase * (kGroup / 8);
+  auto load = [&](int g, TileSlot<BITS, MTW> &o) {
+#pragma unroll
+    for (int t = 0; t < kTileNT; ++t) o.c[t] = load_chunk_wide<BITS>(crow[t] + (int64_t)g * 4 * BITS);
+    const u32x4_t *xp = xg + (int64_t)g * (kGroup / 8);
+#pragma unroll
+    for (int j = 0; j < XI; ++j) o.xv[j] = xp[xoff[j]];
+  };
+
+  const uint32_t magic = in_vgpr(kMagic2);
+  const uint32_t unit1 = (BITS == 8) ? kOne2 : kMagic2;
+  const u32x4_t unit = u32x4_t{unit1, unit1, unit1, unit1};
+  f32x4_t acc[kTileNT][MTW];
+#pragma unroll
+  for (int t = 0; t < kTileNT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto body = [&](const TileSlot<BITS, MTW> &sl, int gl) {
+    // transpose the activations to fragment order through the wave's stage
+#pragma unroll
+    for (int j = 0; j < XI; ++j)
+      *reinterpret_cast<u32x4_t *>(xs + (4 * j + prow) * kTileXPitch + 4 * ppc) = sl.xv[j];
+    u32x4_t A[MTW][4];
+    f32x4_t S[MTW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+      uint32_t X[16], F[16];
+      const u32x4_t *src = reinterpret_cast<const u32x4_t *>(xs + (16 * mt + col) * kTileXPitch + 16 * kq);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4_t v = src[q];
+        X[4 * q + 0] = v[0];
+        X[4 * q + 1] = v[1];
+        X[4 * q + 2] = v[2];
+        X[4 * q + 3] = v[3];
+      }
+      x_fragments<BITS>(X, F);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) A[mt][r] = u32x4_t{F[4 * r], F[4 * r + 1], F[4 * r + 2], F[4 * r + 3]};
+      S[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[mt] = mfma16(A[mt][r], unit, S[mt]);
+    }
+#pragma unroll
+    for (int t = 0; t < kTileNT; ++t) {
+      uint32_t p[16];
+      unpack_pairs<BITS>(sl.c[t], p, magic);
+      const float s = mzs[gl * RB + 16 * t + col];
+      const float zf = (float)mzz[gl * RB + 16 * t + col];
+      const float nz = (BITS == 8) ? -zf : -(1.0f + zf * 0.0078125f);
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        f32x4_t C = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          C = mfma16(A[mt][r], u32x4_t{p[4 * r], p[4 * r + 1], p[4 * r + 2], p[4 * r + 3]}, C);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][mt][v] = fmaf(s, fmaf(nz, S[mt][v], C[v]), acc[t][mt][v]);
+      }
+    }
+  };
+
+  if (ng > 0) {
+    // metadata of the wave's groups: entry (row r, group gl) at [gl * RB + r];
+    // lanes 16u .. 16u+15 of load u take 16 consecutive groups of row 4u + lane / 16
+    constexpr int MU = kTileMaxGroups * RB / kWave;
+    float sv[MU];
+    uint32_t zv[MU];
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int i = u * kWave + lane;
+      const int r = i / kTileMaxGroups, gl = min(i % kTileMaxGroups, ng - 1);
+      const int64_t o = (int64_t)min(n0 + r, N - 1) * G + gbase + ga + gl;
+      sv[u] = md.scale(o);
+      zv[u] = md.zero(o);
+    }
+    TileSlot<BITS, MTW> sa, sb;
+    __builtin_amdgcn_sched_barrier(0);
+    load(ga, sa);
+    __builtin_amdgcn_sched_barrier(0);
+    load(min(ga + 1, gz - 1), sb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int i = u * kWave + lane;
+      const int e = (i % kTileMaxGroups) * RB + i / kTileMaxGroups;
+      mzs[e] = sv[u];
+      mzz[e] = (uint8_t)zv[u];
+    }
+    int g = ga;
+    for (; g + 2 < gz; g += 2) {
+      body(sa, g - ga);
+      __builtin_amdgcn_sched_barrier(0);
+      load(g + 2, sa);
+      __builtin_amdgcn_sched_barrier(0);
+      body(sb, g + 1 - ga);
+      __builtin_amdgcn_sched_barrier(0);
+      load(min(g + 3, gz - 1), sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    body(sa, g - ga);
+    if (g + 1 < gz) body(sb, g + 1 - ga);
+  }
+
+  // the k shares meet in LDS (each wavefront's own activation stage); wavefront
+  // kw = 0 adds them in kw order
+  if (kw > 0) {
+    float *dst = reinterpret_cast<float *>(xs) + lane;
+#pragma unroll
+    for (int t = 0; t < kTileNT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dst[((t * MTW + mt) * 4 + v) * kWave] = acc[t][mt][v];
+  }
+  __syncthreads();
+  if (kw == 0) {
+#pragma unroll
+    for (int j = 1; j < KW; ++j) {
+      const float *src = reinterpret_cast<const float *>(xs_all + (wave + j) * XW) + lane;
+#pragma unroll
+      for (int t = 0; t < kTileNT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[t][mt][v] += src[((t * MTW + mt) * 4 + v) * kWave];
+    }
+#pragma unroll
+    for (int t = 0; t < kTileNT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 16 * (MTW * ms + mt) + 4 * kq + v, n = n0 + 16 * t + col;
+          if (m >= M || n >= N) continue;
+          if (ksplits == 1) y[(int64_t)m * N + n] = acc[t][mt][v];
+          else
+            __hip_atomic_store(&partial[((int64_t)kb * M + m) * N + n], acc[t][mt][v],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+  }
+  if (ksplits == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ unsigned last;
+  if (threadIdx.x == 0) {
+    const unsigned ticket = __hip_atomic_fetch_add(&tickets[blockIdx.x], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    last = (ticket == (unsigned)ksplits - 1u);
+  }
+  __syncthreads();
+  if (!last) return;
+  reduce_partials(partial, y, M, N, n0, RB, ksplits, WV * kWave);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&tickets[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Split-K tickets live in a fixed area at the start of the workspace, so no
 // call's partial sums ever overlap another call's tickets; every completed
 // call leaves all tickets at zero.
@@ -1012,6 +1301,16 @@ constexpr int64_t kMkMinGroups = SLQ_GEMV_MK_MIN_GROUPS;
 #define SLQ_GEMV_MK_NT2_MIN_N (1LL << 40)
 #endif
 constexpr int64_t kMkNt2MinN = SLQ_GEMV_MK_NT2_MIN_N;
+// 17..64 rows: the tile kernel from kTileMinM rows on layers of at least
+// kTileMinSize parameters (smaller layers have too few 64-row tiles to fill
+// the chip, and the older kernels measured faster there).
+#ifndef SLQ_GEMV_TILE_MIN_M
+#define SLQ_GEMV_TILE_MIN_M 17
+#endif
+#ifndef SLQ_GEMV_TILE_MIN_SIZE
+#define SLQ_GEMV_TILE_MIN_SIZE (1LL << 25)
+#endif
+constexpr int64_t kTileMinM = SLQ_GEMV_TILE_MIN_M, kTileMinSize = SLQ_GEMV_TILE_MIN_SIZE;
 // Groups per load batch for 1, 2 and 4 row tiles (two batches in flight).
 #ifndef SLQ_GEMV_B_NT1
 #define SLQ_GEMV_B_NT1 4
@@ -1170,10 +1469,40 @@ hipError_t gemv_mk_nt(const uint16_t *x, const uint32_t *codes, const void *scal
   return gemv_mk_launch<BITS, MT, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
 }
 
+template <int BITS, int MS, bool CM>
+hipError_t gemv_tile_launch(const uint16_t *x, const uint32_t *codes, const void *scales,
+                            const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
+                            void *ws, const GemvPlan &plan, hipStream_t st) {
+  // every wavefront's share of a k-block must fit its metadata stage
+  if ((plan.gw + kTileWV / MS - 1) / (kTileWV / MS) > kTileMaxGroups) return hipErrorInvalidValue;
+  constexpr size_t lds = tile_lds_bytes(kTileWV, kTileMTW);
+  static_assert(lds <= kMaxDynLds, "tile kernel LDS");
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&gemv_tile_kernel<BITS, kTileMTW, MS, kTileWV, CM>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) {
+    (void)hipGetLastError();
+    return attr;
+  }
+  float *partial = nullptr;
+  unsigned *tickets = nullptr;
+  if (plan.ksplits > 1) {
+    tickets = static_cast<unsigned *>(ws);
+    partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
+  }
+  hipLaunchKernelGGL((gemv_tile_kernel<BITS, kTileMTW, MS, kTileWV, CM>), dim3(plan.nblocks, plan.ksplits),
+                     dim3(kTileWV * kWave), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
+                     plan.gw, plan.ksplits, y, partial, tickets);
+  return hipGetLastError();
+}
+
 template <int BITS, bool CM>
 hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      const GemvPlan &plan, hipStream_t st) {
+  if (plan.tile)
+    return plan.ms == 2 ? gemv_tile_launch<BITS, 2, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
+                        : gemv_tile_launch<BITS, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
   if (plan.mk) {
     // only the m-tile counts and row tiles the planner can choose are built
     switch (plan.mt) {
@@ -1219,6 +1548,30 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   // activation loads, whose L2 traffic grows with n * k * m / 16; narrower
   // layers and 17..32 rows measured faster with per-lane loads.
   p.wv = kWaves;
+  if (m >= kTileMinM && n * k >= kTileMinSize) {
+    // 17..64 rows on a large layer: gemv_tile_kernel, 16 * kTileNT rows per
+    // workgroup, the activation rows split kTileWV / kw ways and the k-block
+    // kw ways.
+    p.tile = true;
+    p.wv = kTileWV;
+    p.ms = m > 16 * kTileMTW ? 2 : 1;
+    p.nt = kTileNT;
+    p.b = 2;
+    const int64_t kw = kTileWV / p.ms;
+    const int64_t nb = (n + 16 * kTileNT - 1) / (16 * kTileNT);
+    // k is split across workgroups only as far as a wavefront's metadata
+    // stage (kTileMaxGroups groups) requires: splits for occupancy measured
+    // slower, their tails (partial sums, ticket, reduction) cost more than
+    // the second wavefront per SIMD gains
+    const int64_t ks = std::max<int64_t>(1, (G + kTileMaxGroups * kw - 1) / (kTileMaxGroups * kw));
+    const int64_t gw = std::max<int64_t>(1, (G + ks - 1) / ks);
+    p.gw = (int)std::min<int64_t>(gw, std::numeric_limits<int>::max());
+    p.ksplits = (int)((G + gw - 1) / gw);
+    p.nblocks = (int)nb;
+    if ((p.nblocks > kMaxTicketBlocks && p.ksplits > 1) || (G + gw - 1) / gw > 65535) p.ksplits = 0;
+    p.ws_bytes = p.ksplits > 1 ? kTicketBytes + (size_t)p.ksplits * m * n * sizeof(float) : 0;
+    return p;
+  }
   const bool mk_rows = p.mt >= 4 || (p.mt == 3 && (m >= kMkMinM || k >= kMkDeepK));
   if (p.mt >= kMkMinMt && mk_rows && n >= kMkMinN && n <= kMkMaxN) {
     // 33..64 rows on a mid-width layer: gemv_mk_kernel, one LDS copy of each

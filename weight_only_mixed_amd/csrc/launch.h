@@ -33,6 +33,8 @@ struct GemvPlan {
   bool xd;         // activations loaded by each lane with the weight batches (mt == 1)
   bool rows;       // 17..64 activation rows: row-split kernel, 64 rows per workgroup
   bool mk;         // 33..64 activation rows, mid-width layer: gemv_mk_kernel, 64 * nt rows per workgroup
+  bool tile;       // 17..64 activation rows: gemv_tile_kernel, 16 * nt rows per workgroup
+  int ms;          // tile kernel: wavefronts along the activation rows (the rest split k)
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);
