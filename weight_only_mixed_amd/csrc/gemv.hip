@@ -89,28 +89,38 @@ struct Chunk {
   uint32_t w[BITS];
 };
 
+typedef uint32_t u32x4a_t __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3a_t __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x2a_t __attribute__((ext_vector_type(2), aligned(4)));
+
+// One 32-code chunk (BITS words, 4-byte aligned) in as few vector loads as the
+// width allows: 4-word parts, then a 3-, 2- or 1-word rest.  The four lanes of
+// a row then read its 16*BITS bytes of a group in the same instructions, so
+// each load touches one or two 64-byte segments per row: what bounds these
+// kernels is the L1's rate of about one segment lookup per cycle.
 template <int BITS>
 __device__ __forceinline__ Chunk<BITS> load_chunk(const uint32_t *__restrict__ p) {
   Chunk<BITS> c;
-  if constexpr (BITS % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < BITS / 4; ++i) {
-      const u32x4_t v = reinterpret_cast<const u32x4_t *>(p)[i];
-      c.w[4 * i + 0] = v[0];
-      c.w[4 * i + 1] = v[1];
-      c.w[4 * i + 2] = v[2];
-      c.w[4 * i + 3] = v[3];
-    }
-  } else if constexpr (BITS % 2 == 0) {
-#pragma unroll
-    for (int i = 0; i < BITS / 2; ++i) {
-      const u32x2_t v = reinterpret_cast<const u32x2_t *>(p)[i];
-      c.w[2 * i + 0] = v[0];
-      c.w[2 * i + 1] = v[1];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < BITS; ++i) c.w[i] = p[i];
+  for (int i = 0; i + 4 <= BITS; i += 4) {
+    const u32x4a_t v = *reinterpret_cast<const u32x4a_t *>(p + i);
+    c.w[i] = v[0];
+    c.w[i + 1] = v[1];
+    c.w[i + 2] = v[2];
+    c.w[i + 3] = v[3];
+  }
+  constexpr int i0 = BITS / 4 * 4;
+  if constexpr (BITS % 4 == 3) {
+    const u32x3a_t v = *reinterpret_cast<const u32x3a_t *>(p + i0);
+    c.w[i0] = v[0];
+    c.w[i0 + 1] = v[1];
+    c.w[i0 + 2] = v[2];
+  } else if constexpr (BITS % 4 == 2) {
+    const u32x2a_t v = *reinterpret_cast<const u32x2a_t *>(p + i0);
+    c.w[i0] = v[0];
+    c.w[i0 + 1] = v[1];
+  } else if constexpr (BITS % 4 == 1) {
+    c.w[i0] = p[i0];
   }
   return c;
 }
@@ -945,9 +955,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mk_kernel(
 // costs 64 lookups.  So every load here reads whole segments:
 //  * activations are loaded row-contiguous (16 lanes per 256-byte group row)
 //    and transposed to fragment order through a wavefront-private LDS stage;
-//  * a lane's 32-code chunk comes in one or two vector loads (three-word and
-//    unaligned four-word loads for the odd widths), so the four lanes of a row
-//    read its 16*b bytes in the same instructions;
+//  * a lane's 32-code chunk comes in one or two vector loads (load_chunk), so
+//    the four lanes of a row read its 16*b bytes in the same instructions;
 //  * scales and zero points of the wavefront's groups are staged in LDS once,
 //    16 consecutive groups of a row per 4 lanes.
 // Codes and activations of the next group are loaded while the current group
@@ -972,39 +981,6 @@ constexpr int kTileWV = SLQ_GEMV_TILE_WV;   // wavefronts per workgroup
 // (fp32 scales and byte zero points of kTileMaxGroups groups x 16*kTileNT rows)
 constexpr size_t tile_lds_bytes(int wv, int mtw) {
   return (size_t)wv * (16 * mtw * kTileXPitch * 4 + kTileMaxGroups * 16 * kTileNT * 5) + 16;
-}
-
-typedef uint32_t u32x4a_t __attribute__((ext_vector_type(4), aligned(4)));
-typedef uint32_t u32x3a_t __attribute__((ext_vector_type(3), aligned(4)));
-typedef uint32_t u32x2a_t __attribute__((ext_vector_type(2), aligned(4)));
-
-// One 32-code chunk (BITS words, 4-byte aligned) in as few vector loads as
-// the width allows: 4-word parts, then a 3-, 2- or 1-word rest.
-template <int BITS>
-__device__ __forceinline__ Chunk<BITS> load_chunk_wide(const uint32_t *__restrict__ p) {
-  Chunk<BITS> c;
-#pragma unroll
-  for (int i = 0; i + 4 <= BITS; i += 4) {
-    const u32x4a_t v = *reinterpret_cast<const u32x4a_t *>(p + i);
-    c.w[i] = v[0];
-    c.w[i + 1] = v[1];
-    c.w[i + 2] = v[2];
-    c.w[i + 3] = v[3];
-  }
-  constexpr int i0 = BITS / 4 * 4;
-  if constexpr (BITS % 4 == 3) {
-    const u32x3a_t v = *reinterpret_cast<const u32x3a_t *>(p + i0);
-    c.w[i0] = v[0];
-    c.w[i0 + 1] = v[1];
-    c.w[i0 + 2] = v[2];
-  } else if constexpr (BITS % 4 == 2) {
-    const u32x2a_t v = *reinterpret_cast<const u32x2a_t *>(p + i0);
-    c.w[i0] = v[0];
-    c.w[i0 + 1] = v[1];
-  } else if constexpr (BITS % 4 == 1) {
-    c.w[i0] = p[i0];
-  }
-  return c;
 }
 
 template <int BITS, int MTW>
@@ -1065,7 +1041,7 @@ __global__ __launch_bounds__(WV * kWave) void gemv_tile_kernel(
   const u32x4_t *xg = reinterpret_cast<const u32x4_t *>(x) + (int64_t)gbase * (kGroup / 8);
   auto load = [&](int g, TileSlot<BITS, MTW> &o) {
 #pragma unroll
-    for (int t = 0; t < kTileNT; ++t) o.c[t] = load_chunk_wide<BITS>(crow[t] + (int64_t)g * 4 * BITS);
+    for (int t = 0; t < kTileNT; ++t) o.c[t] = load_chunk<BITS>(crow[t] + (int64_t)g * 4 * BITS);
     const u32x4_t *xp = xg + (int64_t)g * (kGroup / 8);
 #pragma unroll
     for (int j = 0; j < XI; ++j) o.xv[j] = xp[xoff[j]];
