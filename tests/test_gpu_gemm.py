@@ -346,3 +346,76 @@ def test_decode_split_tails_and_mid_width_kernel(bits):
         assert_gemm_close(y.cpu().numpy(), yr, br, what=f"tails b{bits} m{m} {n}x{k}")
         del y, y2, pw
         torch.cuda.empty_cache()
+
+
+def test_stack_parallel_branches_match_one_stream():
+    """Calls that overlap on different streams, each with its own split-k
+    workspace, give bit-identical outputs to the same calls in sequence on one
+    stream: a layer's independent projections as parallel graph branches
+    (q || k || v, then o, then gate || up, then down), eagerly and on every
+    replay of the captured graph, with the tickets back at zero."""
+    m = 64
+    bmap = S.mixed_bit_map()
+    Ws = {p: gpu(S.skewed_weights(*S.LLAMA3_8B_PROJ[p], S.seed_for(3, 0, j), row_offset_std=0.005))
+          for j, p in enumerate(S.PROJ_ORDER)}
+    layers = [{p: slq.slq_quantize_pack(Ws[p], bmap[layer][p]) for p in S.PROJ_ORDER}
+              for layer in (0, 31)]
+    del Ws
+    xk = {k: x_gpu(S.activations_bf16(m, k, 40 + k % 97)) for k in (4096, 14336)}
+    wsb = max(slq.gemm_workspace_bytes(m, pw) for lay in layers for pw in lay.values())
+    wss = [torch.zeros(max(wsb, 256), dtype=torch.uint8, device=DEV) for _ in range(3)]
+    ys = [{p: torch.empty((m, pw.n), dtype=torch.float32, device=DEV) for p, pw in lay.items()}
+          for lay in layers]
+
+    def gemm(li, p, w):
+        pw = layers[li][p]
+        slq.slq_dequant_gemm(xk[pw.k], pw, y=ys[li][p], ws=wss[w])
+
+    side = [torch.cuda.Stream(device=DEV) for _ in range(2)]
+
+    def branches():
+        main = torch.cuda.current_stream()
+        for li in range(len(layers)):
+            for sd in side:
+                sd.wait_stream(main)
+            with torch.cuda.stream(side[0]):
+                gemm(li, "k", 1)
+            with torch.cuda.stream(side[1]):
+                gemm(li, "v", 2)
+            gemm(li, "q", 0)
+            for sd in side:
+                main.wait_stream(sd)
+            gemm(li, "o", 0)
+            side[0].wait_stream(main)
+            with torch.cuda.stream(side[0]):
+                gemm(li, "up", 1)
+            gemm(li, "gate", 0)
+            main.wait_stream(side[0])
+            gemm(li, "down", 0)
+
+    for li in range(len(layers)):
+        for p in S.PROJ_ORDER:
+            gemm(li, p, 0)
+    torch.cuda.synchronize()
+    ref = [{p: y.clone() for p, y in d.items()} for d in ys]
+    branches()
+    torch.cuda.synchronize()
+    for li in range(len(layers)):
+        for p in S.PROJ_ORDER:
+            assert torch.equal(ys[li][p], ref[li][p]), ("eager branches", li, p)
+    cap = torch.cuda.Stream(device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        branches()
+    for rep in range(3):
+        for d in ys:
+            for y in d.values():
+                y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li in range(len(layers)):
+            for p in S.PROJ_ORDER:
+                assert torch.equal(ys[li][p], ref[li][p]), ("graph replay", rep, li, p)
+    for w in wss:
+        assert int(w[:65536].sum()) == 0
