@@ -71,15 +71,15 @@ def test_tile_kernel_sampled_and_pins(bits):
 
 @pytest.mark.parametrize("bits", [3, 5, 6, 8])
 def test_tile_kernel_split_k(bits):
-    """2100 x 16384 (128 groups): more groups than a workgroup's metadata
-    stages hold, so k is split across workgroups (2 splits at 17..32 rows, 4
-    at 33..64) and the last workgroup of each row tile adds the partials; a
-    ragged row edge; sampled outputs plus the whole last row and column;
-    bit-identical repeats; the tickets are back at zero."""
-    n, k = 2100, 16384
-    W = S.skewed_weights(n, k, 70 + bits, row_offset_std=0.005)
-    pw = slq.slq_quantize_pack(gpu(W), bits)
-    for m, ks in ((20, 2), (64, 4)):
+    """k split across workgroups, the last workgroup of each row tile adding
+    the partials: 2100 x 16384 (128 groups: more than a workgroup's metadata
+    stages hold; 5 k-blocks at 20 rows, where the split also fills the chip,
+    4 at 64 rows) and 5500 x 6144 at 24 rows (2 k-blocks, only to fill the
+    chip); ragged row edges; sampled outputs plus the whole last row and
+    column; bit-identical repeats; the tickets are back at zero."""
+    for (n, k), m, ks in (((2100, 16384), 20, 5), ((2100, 16384), 64, 4), ((5500, 6144), 24, 2)):
+        W = S.skewed_weights(n, k, 70 + bits + n, row_offset_std=0.005)
+        pw = slq.slq_quantize_pack(gpu(W), bits)
         name = slq.kernel_name(m, pw)
         say(f"tile split bits={bits} m={m} {n}x{k}: {name}")
         assert name.startswith(TILE) and _splits(m, pw) == ks
@@ -95,7 +95,9 @@ def test_tile_kernel_split_k(bits):
         mi = np.concatenate([g.integers(0, m, 2000), np.full(n, m - 1), np.arange(m)]).astype(np.int64)
         ni = np.concatenate([g.integers(0, n, 2000), np.arange(n), np.full(m, n - 1)]).astype(np.int64)
         yr, br = oracle_sampled(W, bits, x, mi, ni)
-        assert_gemm_close(yh[mi, ni], yr, br, what=f"tile split b{bits} m{m}")
+        assert_gemm_close(yh[mi, ni], yr, br, what=f"tile split b{bits} m{m} {n}x{k}")
+        del pw, y, y2, ws
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("bits", [3, 4, 7])

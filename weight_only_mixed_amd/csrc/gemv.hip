@@ -1306,6 +1306,10 @@ constexpr int64_t kMkNt2MinN = SLQ_GEMV_MK_NT2_MIN_N;
 #define SLQ_GEMV_TILE_MIN_SIZE (1LL << 25)
 #endif
 constexpr int64_t kTileMinM = SLQ_GEMV_TILE_MIN_M, kTileMinSize = SLQ_GEMV_TILE_MIN_SIZE;
+#ifndef SLQ_GEMV_TILE_MIN_BLOCKS
+#define SLQ_GEMV_TILE_MIN_BLOCKS 192
+#endif
+constexpr int64_t kTileMinBlocks = SLQ_GEMV_TILE_MIN_BLOCKS, kTileFillBlocks = 256;
 // Groups per load batch for 1, 2 and 4 row tiles (two batches in flight).
 #ifndef SLQ_GEMV_B_NT1
 #define SLQ_GEMV_B_NT1 4
@@ -1558,7 +1562,14 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
     // stage (kTileMaxGroups groups) requires: splits for occupancy measured
     // slower, their tails (partial sums, ticket, reduction) cost more than
     // the second wavefront per SIMD gains
-    const int64_t ks = std::max<int64_t>(1, (G + kTileMaxGroups * kw - 1) / (kTileMaxGroups * kw));
+    int64_t ks = std::max<int64_t>(1, (G + kTileMaxGroups * kw - 1) / (kTileMaxGroups * kw));
+    // ... except, at 17..32 rows, on grids that would leave a quarter of the
+    // CUs idle (the down projection: 64 row tiles x 2 k-blocks), which split k
+    // for about 256 workgroups while each wavefront keeps 6 groups or more.
+    // (At 33..64 rows and with fewer groups per wavefront such splits measured
+    // slower.)
+    if (p.ms == 1 && nb * ks < kTileMinBlocks)
+      ks = std::max<int64_t>(ks, std::min<int64_t>((kTileFillBlocks + nb - 1) / nb, G / (6 * kw)));
     const int64_t gw = std::max<int64_t>(1, (G + ks - 1) / ks);
     p.gw = (int)std::min<int64_t>(gw, std::numeric_limits<int>::max());
     p.ksplits = (int)((G + gw - 1) / gw);
