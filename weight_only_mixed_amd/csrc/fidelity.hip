@@ -67,7 +67,14 @@ size_t ws_doubles(int64_t rows, const Fid &f) {
          (size_t)rows * f.C * kTopKMax + (size_t)rows * f.C * kTopKMax / 2 + 2;
 }
 
-__device__ __forceinline__ float fast_exp(float v) { return exp2f(v * kLog2e); }
+// The hardware base-2 exponential (v_exp_f32).  Arguments here are
+// (logit - running max) * log2(e) / T <= 0, so only terms below 2^-126 of the
+// running maximum flush to zero: negligible next to a sum that is >= 1 and
+// the 1e-5 tolerance of EAR and KL.  exp2f adds a denormal-range fix-up of
+// about five instructions per call around the same instruction, which made
+// the first pass VALU-bound.
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float fast_exp(float v) { return exp2_hw(v * kLog2e); }
 
 // (m, z, u) combine: z, u are sums of exp(. - m).
 struct MZ {
@@ -106,13 +113,13 @@ __device__ __forceinline__ void online4(float4 a, float4 b, float &m, double &z,
                                         float c) {
   const float mx = fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w));
   if (mx > m) {
-    const float f = exp2f((m - mx) * c);   // m = -inf gives 0
+    const float f = exp2_hw((m - mx) * c);   // m = -inf gives 0
     z *= (double)f;
     if (WITH_U) u *= (double)f;
     m = mx;
   }
-  const float e0 = exp2f((a.x - m) * c), e1 = exp2f((a.y - m) * c), e2 = exp2f((a.z - m) * c),
-              e3 = exp2f((a.w - m) * c);
+  const float e0 = exp2_hw((a.x - m) * c), e1 = exp2_hw((a.y - m) * c), e2 = exp2_hw((a.z - m) * c),
+              e3 = exp2_hw((a.w - m) * c);
   if (!WITH_U) {
     z += (double)((e0 + e1) + (e2 + e3));
   } else {
@@ -134,12 +141,12 @@ template <bool WITH_U>
 __device__ __forceinline__ void online1(float a, float b, float &m, double &z, double &u,
                                         float c) {
   if (a > m) {
-    const float f = exp2f((m - a) * c);
+    const float f = exp2_hw((m - a) * c);
     z *= (double)f;
     if (WITH_U) u *= (double)f;
     m = a;
   }
-  const float e = exp2f((a - m) * c);
+  const float e = exp2_hw((a - m) * c);
   z += (double)e;
   if (WITH_U) u = fma((double)e, (double)a - (double)b, u);
 }
