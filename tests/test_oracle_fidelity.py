@@ -89,7 +89,22 @@ def test_small_noise_asymptotics(orc, sigma):
     assert abs(kl.mean() / want_kl.mean() - 1) < 0.1
 
 
-def test_ear_interpretation_from_pages():
-    """EAR 0.99 is 99% agreement: for a point-mass-free case, EAR = 1 - TV."""
+def test_ear_interpretation_from_pages(orc):
+    """The pages read EAR 0.99 as 99% agreement: EAR is the probability that
+    the two models emit the same token under the best coupling, i.e. 1 - TV.
+    Two distributions that agree on 99% of their mass (q moves 1% of p's mass
+    from token 0 to token 1; and a 4-token case) give EAR = 0.99 to rounding,
+    and the same agreement computed by coupling (the mass both put on each
+    token) matches, within the fp32 rounding of the logits."""
     v = GOLDEN["ear_interpretation"]
-    assert v["ear"] == v["agreement"]
+    cases = [(np.array([0.5, 0.5]), np.array([0.49, 0.51])),
+             (np.array([0.4, 0.3, 0.2, 0.1]), np.array([0.39, 0.3, 0.2, 0.11]))]
+    for p, q in cases:
+        a = np.log(p)[None, :]
+        b = np.log(q)[None, :]
+        ear, kl, _ = orc.ear_kl(a, b)
+        agreement = np.minimum(p, q).sum()          # coupled mass on equal tokens
+        assert abs(agreement - v["agreement"]) < 1e-12
+        # the logits are fp32: log p rounds at ~6e-8 relative
+        assert abs(ear[0] - v["ear"]) < 1e-7, (ear[0], v["ear"])
+        assert abs(ear[0] - (1 - 0.5 * np.abs(p - q).sum())) < 1e-7
