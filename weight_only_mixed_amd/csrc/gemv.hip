@@ -296,6 +296,13 @@ __device__ __forceinline__ float meta_zero(uint32_t z) {
 // (4 consecutive groups of a row) per lane and round; a wave stages its own
 // 16*NT rows x [ga, gz) groups.
 constexpr int kMetaRounds = 2;
+// Without MV, on row blocks of 32 or 64 rows: per-group entries, the first
+// kMetaPre rounds per lane loaded ahead of the first weight batches (any
+// further rounds after them, one at a time).
+#ifndef SLQ_GEMV_META_PRE
+#define SLQ_GEMV_META_PRE 4
+#endif
+constexpr int kMetaPre = SLQ_GEMV_META_PRE;
 
 template <int BITS, int MT, int NT, int B, bool MV, bool XD, int WV, bool CM>
 __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
@@ -367,15 +374,27 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
         md.load4(o, msv[r], mzv[r]);
       }
     }
-  } else {
-    const int cnt = gz - ga;
-    for (int i = lane; i < mrows * cnt; i += kWave) {
+  }
+  // Without MV, entry i is (row i / cnt, group ga + i % cnt).  Wide row
+  // blocks (PRE): the first kMetaPre rounds are loaded with the first weight
+  // batches, ahead of them, and stored after them; returns come back in issue
+  // order, so the stores wait for these loads alone.  (A loop that stored each
+  // entry as it arrived made one memory round trip per round before the first
+  // weight load; on 16-row blocks, whose waves stage one round or two, that
+  // loop measured faster.)
+  constexpr bool PRE = !MV && NT > 1 && WV <= 8;   // (16-wave instances have no registers to spare)
+  const int cnt = gz - ga;
+  const int mtot = MV ? 0 : mrows * cnt;
+  if constexpr (!MV && !PRE) {
+    for (int i = lane; i < mtot; i += kWave) {
       const int n = min(n0 + i / cnt, N - 1);
       const int gl = ga + i % cnt;
       const int64_t o = (int64_t)n * G + gbase + gl;
       meta[gl * mrows + i / cnt] = make_float2(md.scale(o), meta_zero<BITS, ZS>(md.zero(o)));
     }
   }
+  float psv[PRE ? kMetaPre : 1];
+  uint32_t pzv[PRE ? kMetaPre : 1];
 
   const uint32_t *crow[NT];
 #pragma unroll
@@ -499,10 +518,37 @@ __global__ __launch_bounds__(WV * kWave) void gemv_kernel(
 
   // Ring of two batch buffers: both are filled before the staging barrier, and
   // each is refilled (two batches ahead) as soon as it has been consumed.
+  // PRE: the metadata loads share the weight batches' branch (on a path
+  // without the batches, the compiler's in-order wait counts would have to
+  // assume nothing in flight behind them, and the stores would wait for
+  // every load).
   Batch<BITS, MT, NT, B, XD> b0, b1;
   if (ga < gz) {
+    if constexpr (PRE) {
+#pragma unroll
+      for (int u = 0; u < kMetaPre; ++u) {
+        const int i = min(lane + u * kWave, mtot - 1);   // clamped: no load is skipped
+        const int n = min(n0 + i / cnt, N - 1);
+        const int64_t o = (int64_t)n * G + gbase + ga + i % cnt;
+        psv[u] = md.scale(o);
+        pzv[u] = md.zero(o);
+      }
+    }
     load(b0, ga);
     load(b1, ga + B);
+  }
+  if constexpr (PRE) {
+#pragma unroll
+    for (int u = 0; u < kMetaPre; ++u) {
+      const int i = lane + u * kWave;
+      if (i < mtot) meta[(ga + i % cnt) * mrows + i / cnt] = make_float2(psv[u], meta_zero<BITS, ZS>(pzv[u]));
+    }
+    for (int i = lane + kMetaPre * kWave; i < mtot; i += kWave) {
+      const int n = min(n0 + i / cnt, N - 1);
+      const int gl = ga + i % cnt;
+      const int64_t o = (int64_t)n * G + gbase + gl;
+      meta[gl * mrows + i / cnt] = make_float2(md.scale(o), meta_zero<BITS, ZS>(md.zero(o)));
+    }
   }
   if constexpr (MV) {
 #pragma unroll
