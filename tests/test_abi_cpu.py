@@ -244,7 +244,8 @@ def test_sizes_and_strings():
     assert L.slq_dequant_gemm_kernel_name(40, ctypes.byref(mid)).startswith(b"slq::gemv_kernel<4, 3,")
     # layers of 2^25 parameters or more take the tile kernel from 17 rows
     deep = packed(n=4096, k=14336)
-    assert L.slq_dequant_gemm_kernel_name(40, ctypes.byref(deep)) == b"slq::gemv_tile_kernel<4, 2, 2, 4, false>"
+    assert L.slq_dequant_gemm_kernel_name(40, ctypes.byref(deep)) == b"slq::gemv_tile_kernel<4, 3, 1, 4, false>"
+    assert L.slq_dequant_gemm_kernel_name(49, ctypes.byref(deep)) == b"slq::gemv_tile_kernel<4, 2, 2, 4, false>"
     assert L.slq_dequant_gemm_kernel_name(32, ctypes.byref(deep)) == b"slq::gemv_tile_kernel<4, 2, 1, 4, false>"
     assert L.slq_dequant_gemm_kernel_name(17, ctypes.byref(wide)) == b"slq::gemv_tile_kernel<4, 2, 1, 4, false>"
     assert L.slq_dequant_gemm_kernel_name(64, ctypes.byref(wide)) == b"slq::gemv_tile_kernel<4, 2, 2, 4, false>"

@@ -73,11 +73,12 @@ def test_tile_kernel_sampled_and_pins(bits):
 def test_tile_kernel_split_k(bits):
     """k split across workgroups, the last workgroup of each row tile adding
     the partials: 2100 x 16384 (128 groups: more than a workgroup's metadata
-    stages hold; 5 k-blocks at 20 rows, where the split also fills the chip,
-    4 at 64 rows) and 5500 x 6144 at 24 rows (2 k-blocks, only to fill the
-    chip); ragged row edges; sampled outputs plus the whole last row and
+    stages hold; 5 k-blocks at 20 and 40 rows, where the split also fills
+    the chip, 4 at 64 rows) and 5500 x 6144 at 24 rows (2 k-blocks, only to
+    fill the chip); ragged row edges; sampled outputs plus the whole last row and
     column; bit-identical repeats; the tickets are back at zero."""
-    for (n, k), m, ks in (((2100, 16384), 20, 5), ((2100, 16384), 64, 4), ((5500, 6144), 24, 2)):
+    for (n, k), m, ks in (((2100, 16384), 20, 5), ((2100, 16384), 40, 5), ((2100, 16384), 64, 4),
+                          ((5500, 6144), 24, 2)):
         W = S.skewed_weights(n, k, 70 + bits + n, row_offset_std=0.005)
         pw = slq.slq_quantize_pack(gpu(W), bits)
         name = slq.kernel_name(m, pw)

@@ -43,7 +43,7 @@
 //    acquire-release ticket, adds an L2 writeback and invalidate per workgroup
 //    and measured 0.3-7 us slower per launch.
 //  * Four kernels: `gemv_kernel` (any m, the general form above),
-//    `gemv_tile_kernel` (17..64 rows on large layers: 64 weight rows x 32
+//    `gemv_tile_kernel` (17..64 rows on large layers: 64 weight rows x 32 or 48
 //    activation rows per wavefront, every load reading whole cache-line
 //    segments), `gemv_rows_kernel` (33..64 rows on other wide or deep layers:
 //    the waves split rows and share each group's activations) and
@@ -1011,10 +1011,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mk_kernel(
 
 // 17..64 activation rows: `gemv_tile_kernel`.
 // A wavefront owns kTileNT tiles of 16 weight rows and MTW m-tiles of 16
-// activation rows over a contiguous share of the workgroup's k-block, so each
-// activation fragment feeds kTileNT code chains and each unpacked code operand
-// feeds MTW chains.  The four wavefronts of a workgroup split the activation
-// rows MS ways and the k-block 4/MS ways; the k shares meet in LDS at the end.
+// activation rows (2 or 3) over a contiguous share of the workgroup's k-block,
+// so each activation fragment feeds kTileNT code chains and each unpacked code
+// operand feeds MTW chains.  The four wavefronts of a workgroup split the
+// activation rows MS ways and the k-block 4/MS ways; the k shares meet in LDS
+// at the end.
 // What bounds these kernels is the L1's rate of about one cache-line lookup per
 // cycle, not bytes: a load whose 64 lanes each touch another 64-byte segment
 // costs 64 lookups.  So every load here reads whole segments:
@@ -1035,7 +1036,15 @@ __global__ __launch_bounds__(kThreads) void gemv_mk_kernel(
 #define SLQ_GEMV_TILE_NT 4
 #endif
 constexpr int kTileNT = SLQ_GEMV_TILE_NT;
-constexpr int kTileMTW = 2;          // m-tiles per wavefront
+// m-tiles per wavefront: 2 at 17..32 rows and at 49..64 rows (there the
+// activation rows are split over two wavefront pairs, so each code is
+// unpacked twice); 3 at 33..48 rows, every wavefront on all activation rows
+// and its own quarter of the k-block, so each code is unpacked once per
+// workgroup.  Measured on the 8B gate/up and down shapes at b = 3, 4, 6, 8:
+// 3 m-tiles beat the split pairs by 5-10% at 40 and 48 rows; 4 m-tiles at 64
+// rows were 3-10% slower than the split pairs.
+constexpr int kTileMTW = 2;
+constexpr int kTileMTW3MaxM = 48;
 constexpr int kTileMaxGroups = 16;   // groups per wavefront (its metadata stage)
 constexpr int kTileXPitch = 68;      // words per staged activation row (64 + 4 against bank conflicts)
 #ifndef SLQ_GEMV_TILE_WV
@@ -1514,16 +1523,16 @@ hipError_t gemv_mk_nt(const uint16_t *x, const uint32_t *codes, const void *scal
   return gemv_mk_launch<BITS, MT, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
 }
 
-template <int BITS, int MS, bool CM>
+template <int BITS, int MTW, int MS, bool CM>
 hipError_t gemv_tile_launch(const uint16_t *x, const uint32_t *codes, const void *scales,
                             const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y,
                             void *ws, const GemvPlan &plan, hipStream_t st) {
   // every wavefront's share of a k-block must fit its metadata stage
   if ((plan.gw + kTileWV / MS - 1) / (kTileWV / MS) > kTileMaxGroups) return hipErrorInvalidValue;
-  constexpr size_t lds = tile_lds_bytes(kTileWV, kTileMTW);
+  constexpr size_t lds = tile_lds_bytes(kTileWV, MTW);
   static_assert(lds <= kMaxDynLds, "tile kernel LDS");
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&gemv_tile_kernel<BITS, kTileMTW, MS, kTileWV, CM>),
+      reinterpret_cast<const void *>(&gemv_tile_kernel<BITS, MTW, MS, kTileWV, CM>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) {
     (void)hipGetLastError();
@@ -1535,7 +1544,7 @@ hipError_t gemv_tile_launch(const uint16_t *x, const uint32_t *codes, const void
     tickets = static_cast<unsigned *>(ws);
     partial = reinterpret_cast<float *>(static_cast<char *>(ws) + kTicketBytes);
   }
-  hipLaunchKernelGGL((gemv_tile_kernel<BITS, kTileMTW, MS, kTileWV, CM>), dim3(plan.nblocks, plan.ksplits),
+  hipLaunchKernelGGL((gemv_tile_kernel<BITS, MTW, MS, kTileWV, CM>), dim3(plan.nblocks, plan.ksplits),
                      dim3(kTileWV * kWave), lds, st, x, codes, scales, zeros, (int)m, (int)n, (int)k,
                      plan.gw, plan.ksplits, y, partial, tickets);
   return hipGetLastError();
@@ -1545,9 +1554,14 @@ template <int BITS, bool CM>
 hipError_t gemv_bits(const uint16_t *x, const uint32_t *codes, const void *scales,
                      const uint8_t *zeros, int64_t m, int64_t n, int64_t k, float *y, void *ws,
                      const GemvPlan &plan, hipStream_t st) {
-  if (plan.tile)
-    return plan.ms == 2 ? gemv_tile_launch<BITS, 2, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
-                        : gemv_tile_launch<BITS, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+  if (plan.tile) {
+    if (plan.mtw == 2)
+      return plan.ms == 2 ? gemv_tile_launch<BITS, 2, 2, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st)
+                          : gemv_tile_launch<BITS, 2, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    if (plan.mtw == 3)
+      return gemv_tile_launch<BITS, 3, 1, CM>(x, codes, scales, zeros, m, n, k, y, ws, plan, st);
+    return hipErrorInvalidValue;
+  }
   if (plan.mk) {
     // only the m-tile counts and row tiles the planner can choose are built
     switch (plan.mt) {
@@ -1595,11 +1609,12 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
   p.wv = kWaves;
   if (m >= kTileMinM && n * k >= kTileMinSize) {
     // 17..64 rows on a large layer: gemv_tile_kernel, 16 * kTileNT rows per
-    // workgroup, the activation rows split kTileWV / kw ways and the k-block
-    // kw ways.
+    // workgroup, mtw m-tiles per wavefront, the activation rows split
+    // kTileWV / kw ways and the k-block kw ways.
     p.tile = true;
     p.wv = kTileWV;
-    p.ms = m > 16 * kTileMTW ? 2 : 1;
+    p.mtw = (m > 16 * kTileMTW && m <= kTileMTW3MaxM) ? 3 : kTileMTW;
+    p.ms = (m > 16 * p.mtw) ? 2 : 1;
     p.nt = kTileNT;
     p.b = 2;
     const int64_t kw = kTileWV / p.ms;
@@ -1609,11 +1624,12 @@ GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits) {
     // slower, their tails (partial sums, ticket, reduction) cost more than
     // the second wavefront per SIMD gains
     int64_t ks = std::max<int64_t>(1, (G + kTileMaxGroups * kw - 1) / (kTileMaxGroups * kw));
-    // ... except, at 17..32 rows, on grids that would leave a quarter of the
-    // CUs idle (the down projection: 64 row tiles x 2 k-blocks), which split k
-    // for about 256 workgroups while each wavefront keeps 6 groups or more.
-    // (At 33..64 rows and with fewer groups per wavefront such splits measured
-    // slower.)
+    // ... except, when every wavefront covers all activation rows (17..48
+    // rows), on grids that would leave a quarter of the CUs idle (the down
+    // projection: 64 row tiles x 2 k-blocks), which split k for about 256
+    // workgroups while each wavefront keeps 6 groups or more.  (With the
+    // activation rows split over wavefront pairs, and so fewer groups per
+    // wavefront, such splits measured slower.)
     if (p.ms == 1 && nb * ks < kTileMinBlocks)
       ks = std::max<int64_t>(ks, std::min<int64_t>((kTileFillBlocks + nb - 1) / nb, G / (6 * kw)));
     const int64_t gw = std::max<int64_t>(1, (G + ks - 1) / ks);

@@ -35,6 +35,7 @@ struct GemvPlan {
   bool mk;         // 33..64 activation rows, mid-width layer: gemv_mk_kernel, 64 * nt rows per workgroup
   bool tile;       // 17..64 activation rows: gemv_tile_kernel, 16 * nt rows per workgroup
   int ms;          // tile kernel: wavefronts along the activation rows (the rest split k)
+  int mtw;         // tile kernel: 16-row activation tiles per wavefront
   size_t ws_bytes; // tickets + partial sums
 };
 GemvPlan gemv_plan(int64_t m, int64_t n, int64_t k, int bits);

@@ -225,7 +225,7 @@ const char *slq_dequant_gemm_kernel_name(int64_t m, const slq_packed *w) {
     const slq::GemvPlan p = slq::gemv_plan(m, w->n, w->k, w->bits);
     const char *cm = w->meta == SLQ_META_COMPACT ? "true" : "false";
     if (p.tile)
-      snprintf(buf, sizeof buf, "slq::gemv_tile_kernel<%d, 2, %d, %d, %s>", w->bits, p.ms, p.wv, cm);
+      snprintf(buf, sizeof buf, "slq::gemv_tile_kernel<%d, %d, %d, %d, %s>", w->bits, p.mtw, p.ms, p.wv, cm);
     else if (p.mk)
       snprintf(buf, sizeof buf, "slq::gemv_mk_kernel<%d, %d, %d, %s>", w->bits, p.mt, p.nt, cm);
     else if (p.rows)
